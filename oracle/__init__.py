@@ -1,0 +1,147 @@
+"""Loader for the plain fp64 CPU oracle (``parallax_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may use this module; the product path (the HIP library and
+its binding) never imports it, and it is no fallback for the GPU.
+
+The oracle computes the Parallax forward from its definition (review page
+"Parallax: Parameterized Local Linear Attention for Language Modeling",
+sec. 1 and sec. 3): softmax weights over the visible keys, the weighted key
+mean, the probe correction rho.(k_j - kbar) and the corrected weighted sum of
+values, all in fp64.  Everything here converts arrays to contiguous float64
+and calls the C code; no arithmetic of the method lives in this file.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "parallax_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+_D = ctypes.POINTER(ctypes.c_double)
+_L = ctypes.POINTER(ctypes.c_long)
+_I = ctypes.POINTER(ctypes.c_int)
+
+
+def build(out: str = LIBRARY, mutant: int = 0) -> str:
+    """Compile the oracle with gcc (OpenMP, IEEE fp64; no fast-math).
+
+    ``mutant`` > 0 plants one deliberate mistake (see the C file); such
+    builds exist only for the tests that prove the pins catch mistakes.
+    """
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-DORACLE_MUTANT=%d" % int(mutant), "-o", tmp, SOURCE, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes handle on one build of the oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            build(path)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.parallax_oracle_rows.restype = ctypes.c_int
+        lib.parallax_oracle_rows.argtypes = [
+            _D, _D, _L, ctypes.c_long, _D, _D, ctypes.c_long, ctypes.c_int,
+            ctypes.c_double, ctypes.c_long, ctypes.c_long, _D, _D, ctypes.c_int]
+        lib.parallax_oracle_fwd.restype = ctypes.c_int
+        lib.parallax_oracle_fwd.argtypes = [
+            _D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            ctypes.c_int, ctypes.c_double, ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        lib.parallax_oracle_decode.restype = ctypes.c_int
+        lib.parallax_oracle_decode.argtypes = [
+            _D, _D, _D, _D, _I, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            ctypes.c_int, ctypes.c_double, ctypes.c_int]
+        self.lib = lib
+
+    @staticmethod
+    def _f64(a) -> np.ndarray:
+        return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+    @staticmethod
+    def _ptr(a: np.ndarray):
+        return a.ctypes.data_as(_D)
+
+    def fwd(self, q, k, v, r, scale=None, window=0, n_sink=0, nthreads=None):
+        """Prefill forward on [B,H,L,d] arrays; returns (o [B,H,L,d], lse [B,H,L])."""
+        q, k, v, r = (self._f64(x) for x in (q, k, v, r))
+        B, H, L, d = q.shape
+        for x in (k, v, r):
+            if x.shape != q.shape:
+                raise ValueError("q, k, v, r must share one [B,H,L,d] shape")
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        o = np.zeros_like(q)
+        lse = np.zeros((B, H, L), dtype=np.float64)
+        rc = self.lib.parallax_oracle_fwd(
+            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(r), self._ptr(o),
+            self._ptr(lse), B, H, L, d, float(scale), int(window), int(n_sink),
+            int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return o, lse
+
+    def rows(self, q_rows, r_rows, pos, k, v, scale, window=0, n_sink=0, nthreads=None):
+        """Selected rows of one (batch, head) slice.
+
+        q_rows, r_rows: [n, d]; pos: [n] positions; k, v: [n_ctx, d].
+        Returns (o [n, d], lse [n]).
+        """
+        q_rows, r_rows, k, v = (self._f64(x) for x in (q_rows, r_rows, k, v))
+        pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+        n, d = q_rows.shape
+        n_ctx = k.shape[0]
+        o = np.zeros((n, d), dtype=np.float64)
+        lse = np.zeros(n, dtype=np.float64)
+        rc = self.lib.parallax_oracle_rows(
+            self._ptr(q_rows), self._ptr(r_rows), pos.ctypes.data_as(_L), n,
+            self._ptr(k), self._ptr(v), n_ctx, d, float(scale), int(window), int(n_sink),
+            self._ptr(o), self._ptr(lse), int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return o, lse
+
+    def decode(self, q, r, k_cache, v_cache, seqlens=None, scale=None, nthreads=None):
+        """Decode: q, r [B,H,d]; caches [B,H,Lmax,d]; seqlens [B] or None."""
+        q, r, k_cache, v_cache = (self._f64(x) for x in (q, r, k_cache, v_cache))
+        B, H, Lmax, d = k_cache.shape
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        sl = None
+        if seqlens is not None:
+            sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+        o = np.zeros((B, H, d), dtype=np.float64)
+        lse = np.zeros((B, H), dtype=np.float64)
+        rc = self.lib.parallax_oracle_decode(
+            self._ptr(q), self._ptr(r), self._ptr(k_cache), self._ptr(v_cache),
+            sl.ctypes.data_as(_I) if sl is not None else None, self._ptr(o), self._ptr(lse),
+            B, H, Lmax, d, float(scale), int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return o, lse
+
+
+_default = None
+
+
+def default_threads() -> int:
+    """Host threads for the oracle: all cores, at most 16 (a GPU machine's CPU share)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def default() -> Oracle:
+    """The oracle built from the unmodified source (built on first use)."""
+    global _default
+    if _default is None:
+        _default = Oracle(LIBRARY)
+    return _default

@@ -1,0 +1,300 @@
+/*
+ * Plain fp64 CPU oracle for the Parallax attention forward (prefill rows and
+ * decode rows).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
+ * GPU kernels are compared against.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no code, header, table
+ * or helper with the HIP library, and it must never be used as a fallback for
+ * the GPU path.
+ *
+ * What it computes (method: "Parallax: Parameterized Local Linear Attention
+ * for Language Modeling", review page, sec. 1 "Key Terms & Definitions" and
+ * sec. 3 "Method & Key Results"; tilnote note on Parallax, section on the
+ * starting point, Local Linear Attention):
+ *
+ *   Softmax attention reads the values as a locally constant estimate; Local
+ *   Linear Attention (LLA) fits a local linear estimate and needs a per-token
+ *   linear solve.  Parallax drops the solve and lets a learned projection
+ *   give the probe rho_i = x_i W_R, which reads the key/value covariance as a
+ *   correction on top of softmax attention.  Written out, with p_ij the
+ *   softmax weights over the visible keys of query i:
+ *
+ *     kbar_i = sum_j p_ij k_j
+ *     c_ij   = rho_i . (k_j - kbar_i)          (no 1/sqrt(d) on this term)
+ *     o_i    = sum_j p_ij (1 + c_ij) v_j
+ *     lse_i  = log sum_j exp(scale * q_i . k_j)
+ *
+ *   The rho = (Sigma_kk)^-1 (q - kbar) choice of the probe turns o_i into the
+ *   intercept of the p-weighted least-squares fit v ~ a + B (k - q), i.e. the
+ *   LLA estimate; Parallax keeps this form with a learned rho.
+ *
+ * Visible set of query position i (causal; optional sliding window and
+ * attention sinks, per the "Sliding-window beats linear attention" review,
+ * sec. 1, on windows over preceding tokens and on sink tokens):
+ *
+ *     j in V(i)  iff  0 <= j <= i  and  (window <= 0 or i - j < window
+ *                                         or j < n_sink)
+ *
+ * Readings taken where the pages are silent: the window counts the query's
+ * own key (a window of W keys is i-W < j <= i); sinks stay causal; an empty
+ * visible set (only possible for a decode row of length 0, position -1)
+ * gives o = 0 and lse = -inf.
+ *
+ * Algorithm, per row, in the order of the definition: (1) scores and their
+ * max, (2) exponentials, their sum and the weights, (3) the weighted key
+ * mean, (4) the correction coefficient for each key, (5) the weighted sum of
+ * values.  Two plain passes over the visible keys; no tiling, no online
+ * rescaling.
+ *
+ * Build with -DORACLE_MUTANT=n (n >= 1) to plant one deliberate mistake; the
+ * CPU tests use such builds to show that the pins catch each of them.  The
+ * default build (ORACLE_MUTANT = 0) contains no planted mistake.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+/* Is key j visible from query position i? */
+static int visible(long i, long j, long window, long n_sink)
+{
+#if ORACLE_MUTANT == 4
+    /* planted mistake: sink keys visible even ahead of the query */
+    if (j >= 0 && j < n_sink)
+        return 1;
+#endif
+    if (j < 0 || j > i)
+        return 0;
+#if ORACLE_MUTANT == 5
+    /* planted mistake: window boundary off by one (W+1 keys) */
+    if (window <= 0 || i - j <= window || j < n_sink)
+        return 1;
+#else
+    if (window <= 0 || i - j < window || j < n_sink)
+        return 1;
+#endif
+    return 0;
+}
+
+static double dot(const double *a, const double *b, int d)
+{
+    double s = 0.0;
+    for (int t = 0; t < d; ++t)
+        s += a[t] * b[t];
+    return s;
+}
+
+/* One output row.  k, v: [n_ctx][d]; q_i, r_i: [d]; work: scratch [2*n_ctx + d]. */
+static void one_row(const double *q_i, const double *r_i, long i,
+                    const double *k, const double *v, long n_ctx, int d,
+                    double scale, long window, long n_sink,
+                    double *o_i, double *lse_i, double *work)
+{
+    double *z = work;            /* scores, then weights p_j       */
+    double *c = work + n_ctx;    /* correction coefficients c_j    */
+    double *kbar = work + 2 * n_ctx;
+    long last = n_ctx - 1;      /* visible() alone decides which keys count */
+
+    /* (1) scores over the visible set and their maximum */
+    double m = -INFINITY;
+    long n_vis = 0;
+    for (long j = 0; j <= last; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+        z[j] = scale * dot(q_i, k + j * (long)d, d);
+        if (z[j] > m)
+            m = z[j];
+        ++n_vis;
+    }
+    for (int t = 0; t < d; ++t)
+        o_i[t] = 0.0;
+    if (n_vis == 0) {
+        *lse_i = -INFINITY;
+        return;
+    }
+
+    /* (2) exponentials, their sum, normalised weights */
+    double ell = 0.0;
+    for (long j = 0; j <= last; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+        z[j] = exp(z[j] - m);
+        ell += z[j];
+    }
+#if ORACLE_MUTANT == 6
+    /* planted mistake: log-sum-exp without the max */
+    *lse_i = log(ell);
+#else
+    *lse_i = m + log(ell);
+#endif
+    for (long j = 0; j <= last; ++j)
+        if (visible(i, j, window, n_sink))
+            z[j] /= ell;
+
+    /* (3) weighted key mean kbar = sum_j p_j k_j */
+    for (int t = 0; t < d; ++t)
+        kbar[t] = 0.0;
+    for (long j = 0; j <= last; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+#if ORACLE_MUTANT == 7
+        /* planted mistake: key mean with unnormalised weights */
+        double w = z[j] * ell;
+#else
+        double w = z[j];
+#endif
+        for (int t = 0; t < d; ++t)
+            kbar[t] += w * k[j * (long)d + t];
+    }
+
+    /* (4) correction coefficient c_j = rho . (k_j - kbar) */
+    for (long j = 0; j <= last; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+        const double *kj = k + j * (long)d;
+        double s = 0.0;
+        for (int t = 0; t < d; ++t) {
+#if ORACLE_MUTANT == 2
+            /* planted mistake: correction not centred on kbar */
+            s += r_i[t] * kj[t];
+#elif ORACLE_MUTANT == 8
+            /* planted mistake: probe read against the values, not the keys */
+            s += r_i[t] * (v[j * (long)d + t] - kbar[t]);
+#else
+            s += r_i[t] * (kj[t] - kbar[t]);
+#endif
+        }
+#if ORACLE_MUTANT == 3
+        /* planted mistake: softmax scale also applied to the correction */
+        s *= scale;
+#endif
+        c[j] = s;
+    }
+
+    /* (5) o = sum_j p_j (1 + c_j) v_j */
+    for (long j = 0; j <= last; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+#if ORACLE_MUTANT == 1
+        /* planted mistake: correction with the wrong sign */
+        double w = z[j] * (1.0 - c[j]);
+#elif ORACLE_MUTANT == 9
+        /* planted mistake: plain softmax term dropped */
+        double w = z[j] * c[j];
+#elif ORACLE_MUTANT == 10
+        /* planted mistake: weights taken from the previous key */
+        double w = (j > 0 ? z[j - 1] : z[j]) * (1.0 + c[j]);
+#else
+        double w = z[j] * (1.0 + c[j]);
+#endif
+        const double *vj = v + j * (long)d;
+        for (int t = 0; t < d; ++t)
+            o_i[t] += w * vj[t];
+    }
+}
+
+/*
+ * Rows of one (batch, head) slice.
+ *   q_rows, r_rows : [n_rows][d]  query and probe of each requested row
+ *   pos            : [n_rows]     position i of each row, -1 <= i < n_ctx
+ *                                 (-1 = empty visible set, a length-0 decode)
+ *   k, v           : [n_ctx][d]   keys and values of the slice
+ *   o_rows         : [n_rows][d]  output;  lse_rows: [n_rows]
+ * Returns 0, or -1 on an invalid argument (nothing written then).
+ */
+int parallax_oracle_rows(const double *q_rows, const double *r_rows,
+                         const long *pos, long n_rows,
+                         const double *k, const double *v, long n_ctx, int d,
+                         double scale, long window, long n_sink,
+                         double *o_rows, double *lse_rows, int nthreads)
+{
+    if (n_rows < 0 || n_ctx < 0 || d <= 0 || n_sink < 0)
+        return -1;
+    for (long n = 0; n < n_rows; ++n)
+        if (pos[n] < -1 || pos[n] >= n_ctx)
+            return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *work = (double *)malloc(sizeof(double) * (size_t)(2 * n_ctx + d + 1));
+        if (!work) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long n = 0; n < n_rows; ++n)
+                one_row(q_rows + n * (long)d, r_rows + n * (long)d, pos[n],
+                        k, v, n_ctx, d, scale, window, n_sink,
+                        o_rows + n * (long)d, lse_rows + n, work);
+            free(work);
+        }
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Whole prefill forward over contiguous [B][H][L][d] tensors:
+ * o [B][H][L][d], lse [B][H][L].  Returns 0 or -1.
+ */
+int parallax_oracle_fwd(const double *q, const double *k, const double *v,
+                        const double *r, double *o, double *lse,
+                        long B, long H, long L, int d,
+                        double scale, long window, long n_sink, int nthreads)
+{
+    if (B < 0 || H < 0 || L < 0 || d <= 0 || n_sink < 0)
+        return -1;
+    long *pos = (long *)malloc(sizeof(long) * (size_t)(L > 0 ? L : 1));
+    if (!pos)
+        return -2;
+    for (long i = 0; i < L; ++i)
+        pos[i] = i;
+    int rc = 0;
+    for (long bh = 0; bh < B * H && rc == 0; ++bh) {
+        long off = bh * L * (long)d;
+        rc = parallax_oracle_rows(q + off, r + off, pos, L, k + off, v + off, L, d,
+                                  scale, window, n_sink, o + off, lse + bh * L, nthreads);
+    }
+    free(pos);
+    return rc;
+}
+
+/*
+ * Decode: one query per sequence against a contiguous cache.
+ *   q, r   : [B][H][d];  k_cache, v_cache: [B][H][Lmax][d]
+ *   seqlens: [B] host array or NULL (all Lmax); each clamped to [0, Lmax].
+ * The query sits at position seqlen-1 and sees keys 0..seqlen-1.
+ * o: [B][H][d], lse: [B][H].  Returns 0 or -1.
+ */
+int parallax_oracle_decode(const double *q, const double *r,
+                           const double *k_cache, const double *v_cache,
+                           const int *seqlens, double *o, double *lse,
+                           long B, long H, long Lmax, int d, double scale, int nthreads)
+{
+    if (B < 0 || H < 0 || Lmax < 0 || d <= 0)
+        return -1;
+    int rc = 0;
+    for (long b = 0; b < B && rc == 0; ++b) {
+        long n = seqlens ? seqlens[b] : Lmax;
+        if (n < 0)
+            n = 0;
+        if (n > Lmax)
+            n = Lmax;
+        for (long h = 0; h < H && rc == 0; ++h) {
+            long bh = b * H + h;
+            long p = n - 1;
+            rc = parallax_oracle_rows(q + bh * d, r + bh * d, &p, 1,
+                                      k_cache + bh * Lmax * d, v_cache + bh * Lmax * d,
+                                      Lmax, d, scale, 0, 0, o + bh * d, lse + bh, nthreads);
+        }
+    }
+    return rc;
+}

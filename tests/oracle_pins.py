@@ -1,0 +1,226 @@
+"""Pins of the fp64 CPU oracle against facts outside the oracle itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` handle and raises AssertionError
+when the oracle disagrees with the fact it is pinned to.  The same functions
+run on the unmodified oracle (all must pass) and on builds with a planted
+mistake (at least one must fail), so a plausible slip anywhere in the oracle
+-- a dropped term, a wrong sign, an index or mask off by one, a transposed
+operand -- is caught.
+
+Facts used (none of them re-types the oracle's own two-pass algorithm):
+  * the matrix closed form with brute-force mask enumeration (bruteforce.py);
+  * rho = 0 reduces to softmax attention: torch's scaled_dot_product_attention
+    and torch.logsumexp in fp64 on the CPU (library routines);
+  * rho = Sigma_kk^-1 (q - kbar) reproduces the intercept of the weighted
+    least-squares local linear fit (the LLA estimator that Parallax
+    parameterises), solved by numpy.linalg.lstsq;
+  * closed forms: a single visible key gives o = v, lse = scale q.k;
+  * invariants: key translation, value affinity, linearity in rho;
+  * a hand-worked example with exact rational results (tests/golden).
+Sources: review page "Parallax: Parameterized Local Linear Attention for
+Language Modeling", sec. 1-3; tilnote note on Parallax, section on Local
+Linear Attention as the starting point; "Sliding-window beats linear
+attention" review, sec. 1 (windows and sinks).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+from bruteforce import closed_form, visible_mask
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+TOL = 1e-11
+
+
+def _rand(shape, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(shape) * scale
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    err = np.max(np.abs(a - b) / (1.0 + np.abs(b))) if a.size else 0.0
+    assert np.all(np.isfinite(a) == np.isfinite(b)), what + ": finiteness differs"
+    fin = np.isfinite(b)
+    if fin.any():
+        err = np.max(np.abs(a[fin] - b[fin]) / (1.0 + np.abs(b[fin])))
+        assert err <= tol, "%s: max rel err %.3e > %.1e" % (what, err, tol)
+
+
+MASKS = [(0, 0), (1, 0), (3, 0), (5, 2), (2, 4), (0, 3), (64, 0)]
+
+
+def pin_closed_form(orc):
+    """Oracle == matrix closed form (brute-force masks), several masks and d."""
+    for d, L in ((3, 9), (8, 17)):
+        for seed, (window, n_sink) in enumerate(MASKS):
+            q, k, v, r = (_rand((2, 2, L, d), 100 * seed + t + d) for t in range(4))
+            o, lse = orc.fwd(q, k, v, r, window=window, n_sink=n_sink)
+            o2, lse2 = closed_form(q, k, v, r, window=window, n_sink=n_sink)
+            _close(o, o2, what="O closed form W=%d S=%d" % (window, n_sink))
+            _close(lse, lse2, what="LSE closed form W=%d S=%d" % (window, n_sink))
+
+
+def pin_softmax_special_case(orc):
+    """rho = 0 gives exactly softmax attention (torch SDPA, fp64, CPU)."""
+    import torch
+    import torch.nn.functional as F
+    for seed, (window, n_sink) in enumerate(MASKS):
+        B, H, L, d = 1, 2, 13, 8
+        q, k, v = (_rand((B, H, L, d), 7 + 3 * seed + t) for t in range(3))
+        r = np.zeros_like(q)
+        scale = 1.0 / np.sqrt(d)
+        o, lse = orc.fwd(q, k, v, r, scale=scale, window=window, n_sink=n_sink)
+        mask = torch.from_numpy(visible_mask(L, window, n_sink))
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+        scores = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+        scores = scores.masked_fill(~mask, float("-inf"))
+        ref_lse = torch.logsumexp(scores, dim=-1)
+        _close(o, ref.numpy(), what="O vs SDPA W=%d S=%d" % (window, n_sink))
+        _close(lse, ref_lse.numpy(), what="LSE vs logsumexp W=%d S=%d" % (window, n_sink))
+
+
+def _softmax_weights(q, K, scale, vis):
+    z = scale * (K[vis] @ q)
+    z = z - z.max()
+    e = np.exp(z)
+    return e / e.sum()
+
+
+def pin_local_linear_fit(orc):
+    """With rho = Sigma_kk^-1 (q - kbar) the output is the weighted LLS intercept.
+
+    The local linear estimate at the query point fits v ~ a + B (k - q) with
+    the softmax weights and reports a; the probe form sum p (1 + rho.(k-kbar)) v
+    equals it for this rho.  Checked on rows with more visible keys than d.
+    """
+    for (window, n_sink) in ((0, 0), (9, 2)):
+        B, H, L, d = 1, 1, 16, 3
+        q, k, v = (_rand((B, H, L, d), 31 + t + window) for t in range(3))
+        scale = 1.0 / np.sqrt(d)
+        mask = visible_mask(L, window, n_sink)
+        r = np.zeros_like(q)
+        rows = [i for i in range(L) if mask[i].sum() >= d + 2]
+        for i in rows:
+            vis = mask[i]
+            K = k[0, 0]
+            p = _softmax_weights(q[0, 0, i], K, scale, vis)
+            Kv = K[vis]
+            kbar = p @ Kv
+            cov = (Kv - kbar).T @ ((Kv - kbar) * p[:, None])
+            r[0, 0, i] = np.linalg.solve(cov, q[0, 0, i] - kbar)
+        o, _ = orc.fwd(q, k, v, r, scale=scale, window=window, n_sink=n_sink)
+        for i in rows:
+            vis = mask[i]
+            K = k[0, 0]
+            p = _softmax_weights(q[0, 0, i], K, scale, vis)
+            X = np.concatenate([np.ones((vis.sum(), 1)), K[vis] - q[0, 0, i]], axis=1)
+            w = np.sqrt(p)[:, None]
+            coef, *_ = np.linalg.lstsq(X * w, v[0, 0][vis] * w, rcond=None)
+            _close(o[0, 0, i], coef[0], tol=1e-9, what="LLS intercept row %d" % i)
+
+
+def pin_single_key(orc):
+    """One visible key: o = v_j and lse = scale * q.k_j (row 0; window 1)."""
+    B, H, L, d = 2, 1, 6, 5
+    q, k, v, r = (_rand((B, H, L, d), 50 + t) for t in range(4))
+    scale = 0.37
+    o, lse = orc.fwd(q, k, v, r, scale=scale)
+    _close(o[:, :, 0], v[:, :, 0], what="row 0 output")
+    _close(lse[:, :, 0], scale * np.sum(q[:, :, 0] * k[:, :, 0], axis=-1), what="row 0 lse")
+    o, lse = orc.fwd(q, k, v, r, scale=scale, window=1)
+    _close(o, v, what="window 1 output")
+    _close(lse, scale * np.sum(q * k, axis=-1), what="window 1 lse")
+
+
+def pin_key_translation(orc):
+    """k_j -> k_j + u: o unchanged, lse shifted by scale * q.u."""
+    B, H, L, d = 1, 2, 11, 4
+    q, k, v, r = (_rand((B, H, L, d), 60 + t) for t in range(4))
+    u = _rand((d,), 99) * 3.0
+    scale = 0.5
+    for (window, n_sink) in ((0, 0), (3, 2)):
+        o, lse = orc.fwd(q, k, v, r, scale=scale, window=window, n_sink=n_sink)
+        o2, lse2 = orc.fwd(q, k + u, v, r, scale=scale, window=window, n_sink=n_sink)
+        _close(o2, o, tol=1e-10, what="translated keys output")
+        _close(lse2, lse + scale * (q @ u), tol=1e-10, what="translated keys lse")
+
+
+def pin_value_affine(orc):
+    """v_j -> v_j + w gives o + w; constant values give constant outputs."""
+    B, H, L, d = 1, 1, 10, 6
+    q, k, v, r = (_rand((B, H, L, d), 70 + t) for t in range(4))
+    w = _rand((d,), 77)
+    o, _ = orc.fwd(q, k, v, r)
+    o2, _ = orc.fwd(q, k, v + w, r)
+    _close(o2, o + w, tol=1e-10, what="value shift")
+    o3, _ = orc.fwd(q, k, np.ones_like(v), r, window=4, n_sink=1)
+    _close(o3, np.ones_like(v), tol=1e-10, what="constant values")
+
+
+def pin_rho_linearity(orc):
+    """o is affine in rho: o(a rho) = o(0) + a (o(rho) - o(0))."""
+    B, H, L, d = 1, 1, 9, 4
+    q, k, v, r = (_rand((B, H, L, d), 80 + t) for t in range(4))
+    o0, _ = orc.fwd(q, k, v, np.zeros_like(r))
+    o1, _ = orc.fwd(q, k, v, r)
+    oa, _ = orc.fwd(q, k, v, -2.5 * r)
+    _close(oa, o0 - 2.5 * (o1 - o0), tol=1e-10, what="rho linearity")
+
+
+def pin_masks(orc):
+    """Window >= L equals causal; sinks without a window change nothing."""
+    B, H, L, d = 1, 1, 12, 4
+    q, k, v, r = (_rand((B, H, L, d), 90 + t) for t in range(4))
+    base = orc.fwd(q, k, v, r)
+    for window, n_sink in ((L, 0), (L + 5, 3), (0, 4)):
+        o, lse = orc.fwd(q, k, v, r, window=window, n_sink=n_sink)
+        _close(o, base[0], what="mask W=%d S=%d vs causal" % (window, n_sink))
+        _close(lse, base[1], what="mask lse W=%d S=%d vs causal" % (window, n_sink))
+
+
+def pin_golden(orc):
+    """Hand-worked uniform-weight example (tests/golden/uniform_weights.json)."""
+    with open(os.path.join(GOLDEN, "uniform_weights.json")) as f:
+        g = json.load(f)
+    shape = (1, 1, g["L"], g["d"])
+    q, k, v, r = (np.array(g[n], dtype=np.float64).reshape(shape) for n in "qkvr")
+    for case in g["cases"]:
+        o, lse = orc.fwd(q, k, v, r, scale=g["scale"], window=case["window"],
+                         n_sink=case["n_sink"])
+        _close(o[0, 0], np.array(case["o"], dtype=np.float64), tol=1e-14,
+               what="golden O W=%d S=%d" % (case["window"], case["n_sink"]))
+        _close(lse[0, 0], np.log(np.array(case["lse_n_visible"], dtype=np.float64)),
+               tol=1e-14, what="golden LSE W=%d S=%d" % (case["window"], case["n_sink"]))
+
+
+def pin_decode(orc):
+    """A decode row equals the prefill row at position seqlen-1; seqlen 0 is empty."""
+    B, H, Lmax, d = 3, 2, 9, 4
+    k, v = (_rand((B, H, Lmax, d), 110 + t) for t in range(2))
+    q, r = (_rand((B, H, d), 120 + t) for t in range(2))
+    seqlens = [9, 4, 0]
+    o, lse = orc.decode(q, r, k, v, seqlens=seqlens, scale=0.4)
+    for b, n in enumerate(seqlens):
+        if n == 0:
+            assert np.all(o[b] == 0.0) and np.all(np.isneginf(lse[b])), "empty decode row"
+            continue
+        qq = np.zeros((1, H, n, d))
+        rr = np.zeros((1, H, n, d))
+        qq[0, :, n - 1] = q[b]
+        rr[0, :, n - 1] = r[b]
+        o2, lse2 = closed_form(qq, k[b:b + 1, :, :n], v[b:b + 1, :, :n], rr, scale=0.4)
+        _close(o[b], o2[0, :, n - 1], what="decode row b=%d" % b)
+        _close(lse[b], lse2[0, :, n - 1], what="decode lse b=%d" % b)
+
+
+ALL_PINS = [pin_closed_form, pin_softmax_special_case, pin_local_linear_fit,
+            pin_single_key, pin_key_translation, pin_value_affine, pin_rho_linearity,
+            pin_masks, pin_golden, pin_decode]
