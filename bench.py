@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the Parallax forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * the causal prefill on the 1.7B-like long workload
+    (B=2, H=16, L=8192, d=128, bf16, N(0,1) inputs), then
+  * one decode step on the decode workload
+    (B=64, H=16, 4096-token bf16 KV cache, d=128, 16 splits),
+both launched on one dedicated stream with inputs already resident in HBM.
+
+Printed: ONE JSON line.  `value` is the prefill throughput in TFLOP/s
+(algorithmic FLOP: 8d per visible (query, key) pair -- the two score and two
+value products -- divided by the prefill kernel time measured with HIP events
+on its own stream); the decode throughput in GB/s is reported beside it.
+`roofline` describes the dominant kernel (the prefill); `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Parallax attn fwd TFLOP/s & % bf16 MFMA peak (L=8192,d=128); decode HBM GB/s"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16/f16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_fwd.hip"),
+    "decode": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle (profiling runs)")
+    p.add_argument("--cpu-sample-heads", type=int, default=8,
+                   help="(b,h) slices of the prefill workload the CPU oracle computes")
+    p.add_argument("--extra", action="store_true",
+                   help="also time the other prefill workloads (printed to stderr)")
+    return p.parse_args()
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when they were taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, n_heads: int):
+    """Time the fp64 oracle on all rows of the first n_heads (b, h) slices."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from parallax_local_linear_amd import accounting, workloads
+
+    q, k, v, r = workloads.prefill_inputs(cfg, device="cpu")
+    orc = oracle.default()
+    nthreads = oracle.default_threads()
+    scale = 1.0 / np.sqrt(cfg.d)
+    pos = np.arange(cfg.L)
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    slices = [(b, h) for b in range(cfg.B) for h in range(cfg.H)][:n_heads]
+    data = [(f64(q[b, h]), f64(r[b, h]), f64(k[b, h]), f64(v[b, h])) for b, h in slices]
+    t0 = time.perf_counter()
+    for Q, R, K, V in data:
+        orc.rows(Q, R, pos, K, V, scale, cfg.window, cfg.n_sink, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    flops = 8 * cfg.d * len(slices) * accounting.visible_pairs(cfg.L, cfg.window, cfg.n_sink)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": "all %d rows of %d of the %d (b,h) slices of %s (%.3g GFLOP, %.1f s)"
+                      % (cfg.L, len(slices), cfg.B * cfg.H, cfg.name, flops / 1e9, dt)}
+
+
+def time_prefill_only(cfg, steps, warmup, stream):
+    """Median-free mean kernel time (ms) of one prefill workload (for --extra)."""
+    import torch
+
+    from parallax_local_linear_amd import accounting, parallax_attn_fwd, workloads
+    q, k, v, r = workloads.prefill_inputs(cfg, device="cuda:0")
+    o = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda:0")
+    for _ in range(warmup):
+        parallax_attn_fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,
+                          stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        parallax_attn_fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,
+                          stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": cfg.name, "ms": ms,
+            "tflops": accounting.prefill_flops(cfg) / (ms * 1e-3) / 1e12,
+            "gbs": accounting.prefill_bytes(cfg) / (ms * 1e-3) / 1e9}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X and has no "
+              "multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from parallax_local_linear_amd import (accounting, parallax_attn_decode, parallax_attn_fwd,
+                                           workloads)
+    from parallax_local_linear_amd.binding import LIBRARY
+
+    if not os.path.exists(LIBRARY):
+        from parallax_local_linear_amd import build as lib_build
+        lib_build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    dev = torch.device("cuda:0")
+    pcfg = workloads.PREFILL_17B
+    dcfg = workloads.DECODE
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    q, k, v, r = workloads.prefill_inputs(pcfg, device=dev)
+    o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv, dr = workloads.decode_inputs(dcfg, device=dev)
+    do = torch.empty(dq.shape, dtype=torch.float32, device=dev)
+    dlse = torch.empty(dq.shape[:2], dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        parallax_attn_fwd(q, k, v, r, window=pcfg.window, n_sink=pcfg.n_sink, out=o, lse=lse,
+                          stream=stream)
+        if events is not None:
+            events[1].record(stream)
+        parallax_attn_decode(dq, dr, dk, dv, None, num_splits=dcfg.num_splits, out=do,
+                             lse=dlse, stream=stream)
+        if events is not None:
+            events[2].record(stream)
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
+
+    total_ms = t_start.elapsed_time(t_end)
+    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    p_flops = accounting.prefill_flops(pcfg)
+    p_tflops = p_flops / (pre_avg * 1e-3) / 1e12
+    d_bytes = accounting.decode_bytes(dcfg)
+    d_gbs = d_bytes / (dec_avg * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(p_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s + %s" % (pcfg.name, dcfg.name),
+            "prefill": {"B": pcfg.B, "H": pcfg.H, "L": pcfg.L, "d": pcfg.d, "mask": "causal",
+                        "inputs": "N(0,1) bf16, seed %d" % pcfg.seed},
+            "decode": {"B": dcfg.B, "H": dcfg.H, "Lmax": dcfg.Lmax, "d": dcfg.d,
+                       "num_splits": dcfg.num_splits, "inputs": "N(0,1) bf16, seed %d" % dcfg.seed},
+            "precision": "bf16 inputs; bf16 score MFMA, f16 value MFMA, fp32 accumulate; fp32 O",
+        },
+        "prefill_ms": round(pre_avg, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(p_tflops, 2),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4),
+            "traffic": measured_traffic("prefill"),
+            "algorithmic_flop_per_launch": p_flops,
+            "kernel": "parallax_fwd_kernel<128>",
+        },
+        "decode": {
+            "value": round(d_gbs, 1),
+            "unit": "GB/s",
+            "ms": round(dec_avg, 4),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(d_gbs, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(d_gbs / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("decode"),
+                "algorithmic_bytes_per_launch": d_bytes,
+                "kernel": "parallax_decode_kernel<128,16>",
+            },
+        },
+    }
+    if args.extra:
+        for cfg in (workloads.PREFILL_06B, workloads.LOCAL, workloads.TINY):
+            print(json.dumps(time_prefill_only(cfg, 20, 3, stream)), file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(pcfg, args.cpu_sample_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

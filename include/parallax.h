@@ -1,0 +1,137 @@
+/*
+ * parallax.h -- C ABI of the MI355X (gfx950) Parallax attention library.
+ *
+ * Parallax (parameterized Local Linear Attention) keeps softmax attention's
+ * weights and adds a correction read from the key/value covariance by a
+ * learned probe rho_i = x_i W_R, in place of Local Linear Attention's
+ * per-token linear solve (review page "Parallax: Parameterized Local Linear
+ * Attention for Language Modeling", sec. 1 "Key Terms & Definitions" and
+ * sec. 3 "Method & Key Results"; tilnote note on Parallax, section on its
+ * starting point, Local Linear Attention).  For query position i with visible
+ * key set V(i):
+ *
+ *     p_ij   = softmax_j (scale * q_i . k_j)           over j in V(i)
+ *     kbar_i = sum_j p_ij k_j
+ *     o_i    = sum_j p_ij (1 + rho_i . (k_j - kbar_i)) v_j
+ *     lse_i  = log sum_{j in V(i)} exp(scale * q_i . k_j)    (natural log)
+ *
+ * The probe term carries no softmax scale.  Visible set (causal, optional
+ * sliding window and attention sinks; "Sliding-window beats linear
+ * attention" review, sec. 1):
+ *
+ *     j in V(i)  iff  j <= i  and  (window == 0 or i - j < window or j < n_sink)
+ *
+ * so a window of W keys includes the query's own key, and sink keys are
+ * still causal.
+ *
+ * Conventions shared by every entry point:
+ *   - Inputs q, k, v, r are bfloat16 (raw 16-bit storage, passed as void*);
+ *     outputs o and lse are float32.  The feature dimension d is 64 or 128.
+ *   - All pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; it needs no workspace.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously.  Calls are stateless and thread-safe.
+ *   - Every argument is checked on the host before anything is enqueued; a
+ *     non-OK status means nothing was launched and no output was touched.
+ *     PARALLAX_ERR_LAUNCH reports a failed kernel launch.
+ *   - Outputs must not alias inputs.  Non-finite inputs give undefined
+ *     results.
+ *   - Numerical range: the kernels feed the softmax weights, the products
+ *     p * (rho . k) and the values to float16 matrix-core operands, so
+ *     |v| and |rho_i . k_j| must stay below 4096 (values beyond float16's
+ *     range become infinite).
+ */
+#ifndef PARALLAX_H
+#define PARALLAX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PARALLAX_OK = 0,
+    PARALLAX_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, bad stride,
+                                     negative window or n_sink, scale not > 0 and finite */
+    PARALLAX_ERR_UNSUPPORTED = 2, /* d not in {64,128}, num_splits not in {1,2,4,8,16},
+                                     problem too large for the launch grid */
+    PARALLAX_ERR_LAUNCH = 3       /* the HIP runtime rejected the kernel launch */
+} parallax_status;
+
+/* Element strides (not bytes) of a [B, H, L, d] tensor along B, H and L.
+ * The d dimension must be contiguous (stride 1). */
+typedef struct {
+    int64_t b, h, l;
+} parallax_strides;
+
+/*
+ * Causal prefill forward.
+ *
+ *   q, k, v, r : bf16 tensors of logical shape [B, H, L, d] with strides
+ *                sq, sk, sv, sr (r is the probe rho = x W_R, one row per
+ *                query position).  Base pointers 16-byte aligned; every
+ *                stride a multiple of 8 elements.
+ *   o          : fp32 [B, H, L, d] with strides so (16-byte aligned; strides
+ *                multiples of 4 elements).
+ *   lse        : fp32 [B, H, L], contiguous (4-byte aligned).
+ *   B, H, L    : >= 0; if any is 0 the call returns PARALLAX_OK and does
+ *                nothing.
+ *   d          : 64 or 128.
+ *   softmax_scale : multiplies q.k only (usually 1/sqrt(d)); must be > 0
+ *                and finite.
+ *   window     : 0 = plain causal; W > 0 = key j visible iff i - j < W
+ *                (or j is a sink).  Must be >= 0.
+ *   n_sink     : number of leading sink keys (always visible once causal);
+ *                >= 0; only matters when window > 0.
+ */
+parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, const void *r,
+                                  float *o, float *lse,
+                                  int B, int H, int L, int d,
+                                  parallax_strides sq, parallax_strides sk,
+                                  parallax_strides sv, parallax_strides sr,
+                                  parallax_strides so,
+                                  float softmax_scale, int window, int n_sink,
+                                  void *stream);
+
+/*
+ * Decode step: one query (and probe) per sequence against a contiguous KV
+ * cache.  A decoding Parallax model reads a KV cache like softmax attention
+ * does (tilnote note on Parallax, section explaining that it is a different
+ * estimator and not a linear-time attention).
+ *
+ *   q, r       : bf16 [B, H, d], contiguous, 16-byte aligned.
+ *   k_cache,
+ *   v_cache    : bf16 [B, H, Lmax, d] with strides sk, sv (16-byte aligned
+ *                base, strides multiples of 8 elements).
+ *   seqlens    : DEVICE int32 [B] or NULL (= Lmax for every sequence).  The
+ *                cache already holds the current token: the query sits at
+ *                position seqlen-1 and sees keys 0 .. seqlen-1.  Values are
+ *                clamped to [0, Lmax]; a length of 0 gives o = 0 and
+ *                lse = -inf.
+ *   o          : fp32 [B, H, d] contiguous (16-byte aligned).
+ *   lse        : fp32 [B, H] contiguous.
+ *   B, H       : >= 0 (0 -> OK, nothing done); Lmax >= 0; d 64 or 128.
+ *   softmax_scale : as for the prefill (> 0, finite).
+ *   num_splits : 1, 2, 4, 8 or 16 -- the cache of each (b, h) is cut into
+ *                this many contiguous chunks, processed by separate
+ *                wavefronts and merged on chip.  The result does not depend
+ *                on it beyond rounding.
+ */
+parallax_status parallax_attn_decode(const void *q, const void *r,
+                                     const void *k_cache, const void *v_cache,
+                                     const int32_t *seqlens,
+                                     float *o, float *lse,
+                                     int B, int H, int Lmax, int d,
+                                     parallax_strides sk, parallax_strides sv,
+                                     float softmax_scale, int num_splits,
+                                     void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *parallax_status_string(parallax_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARALLAX_H */

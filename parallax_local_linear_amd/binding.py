@@ -1,0 +1,169 @@
+"""Thin ctypes binding over ``libparallax.so`` (the C ABI in include/parallax.h).
+
+Argument marshalling only: tensors are checked for dtype, device and layout,
+their data pointers and element strides are passed through, outputs are
+allocated with torch when the caller gives none, and every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+torch is imported first on purpose: the library then binds to the HIP
+runtime torch already loaded, so torch's streams and device pointers are
+valid in it.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libparallax.so")
+
+PARALLAX_OK = 0
+STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
+                2: "PARALLAX_ERR_UNSUPPORTED", 3: "PARALLAX_ERR_LAUNCH"}
+
+# Every symbol include/parallax.h declares.
+EXPORTED = ("parallax_attn_fwd", "parallax_attn_decode", "parallax_status_string")
+
+
+class parallax_strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("l", ctypes.c_int64)]
+
+
+class ParallaxError(RuntimeError):
+    def __init__(self, status: int, name: str):
+        super().__init__("%s (status %d)" % (name, status))
+        self.status = status
+        self.name = name
+
+
+_lib = None
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the built library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libparallax.so is not built (%s); run `python -m parallax_local_linear_amd.build`"
+            % path)
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    S = parallax_strides
+    lib.parallax_attn_fwd.restype = ctypes.c_int
+    lib.parallax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, S, S, S, S, S,
+                                      f, i, i, vp]
+    lib.parallax_attn_decode.restype = ctypes.c_int
+    lib.parallax_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, S, S,
+                                         f, i, vp]
+    lib.parallax_status_string.restype = ctypes.c_char_p
+    lib.parallax_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def parallax_status_string(status: int) -> str:
+    return load_library().parallax_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != PARALLAX_OK:
+        raise ParallaxError(status, parallax_status_string(status))
+
+
+def _strides(t: torch.Tensor) -> parallax_strides:
+    if t.stride(-1) != 1:
+        raise ValueError("the feature dimension must be contiguous (stride 1)")
+    s = t.stride()
+    return parallax_strides(s[0], s[1], s[2])
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions" % (name, ndim))
+
+
+def parallax_attn_fwd(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
+                      out=None, lse=None, stream=None):
+    """Causal Parallax prefill. q, k, v, r: bf16 [B,H,L,d] -> (o fp32 [B,H,L,d], lse fp32 [B,H,L])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (r, "r")):
+        _need(t, n, torch.bfloat16, 4)
+        if t.shape != q.shape:
+            raise ValueError("q, k, v and r must share one [B,H,L,d] shape")
+    B, H, L, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 4)
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(out.shape) != (B, H, L, d) or tuple(lse.shape) != (B, H, L):
+        raise ValueError("out / lse have the wrong shape")
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    lib = load_library()
+    st = lib.parallax_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, H, L, d, _strides(q), _strides(k), _strides(v), _strides(r), _strides(out),
+        float(softmax_scale), int(window), int(n_sink), _stream_handle(q.device, stream))
+    _check(st)
+    return out, lse
+
+
+def parallax_attn_decode(q, r, k_cache, v_cache, seqlens=None, *, softmax_scale=None,
+                         num_splits=16, out=None, lse=None, stream=None):
+    """Decode step. q, r: bf16 [B,H,d]; caches bf16 [B,H,Lmax,d]; seqlens int32 [B] or None.
+
+    Returns (o fp32 [B,H,d], lse fp32 [B,H]).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(r, "r", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, H, Lmax, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or tuple(q.shape) != (B, H, d) or r.shape != q.shape:
+        raise ValueError("decode shapes disagree")
+    if not (q.is_contiguous() and r.is_contiguous()):
+        raise ValueError("q and r must be contiguous")
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, 1)
+        if seqlens.shape[0] != B or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be a contiguous int32 [B] tensor")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if not (out.is_contiguous() and lse.is_contiguous()):
+        raise ValueError("out and lse must be contiguous")
+    if tuple(out.shape) != (B, H, d) or tuple(lse.shape) != (B, H):
+        raise ValueError("out / lse have the wrong shape")
+    lib = load_library()
+    st = lib.parallax_attn_decode(
+        q.data_ptr(), r.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        seqlens.data_ptr() if seqlens is not None else None, out.data_ptr(), lse.data_ptr(),
+        B, H, Lmax, d, _strides(k_cache), _strides(v_cache), float(softmax_scale),
+        int(num_splits), _stream_handle(q.device, stream))
+    _check(st)
+    return out, lse

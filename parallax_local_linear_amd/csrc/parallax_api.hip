@@ -1,0 +1,137 @@
+// C-ABI entry points of the Parallax library: host-side argument checks,
+// then one kernel launch on the caller's stream.  No allocation, no
+// synchronisation, no global state.
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+#include "parallax.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Strides of a bf16 tensor used with 16-byte vector loads: non-negative
+// multiples of 8 elements.
+bool bf16_strides_ok(const parallax_strides &s) {
+    return s.b >= 0 && s.h >= 0 && s.l >= 0 && s.b % 8 == 0 && s.h % 8 == 0 && s.l % 8 == 0;
+}
+
+// Strides of the fp32 output written with 16-byte stores.
+bool f32_strides_ok(const parallax_strides &s) {
+    return s.b >= 0 && s.h >= 0 && s.l >= 0 && s.b % 4 == 0 && s.h % 4 == 0 && s.l % 4 == 0;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+const char *parallax_status_string(parallax_status s) {
+    switch (s) {
+    case PARALLAX_OK: return "PARALLAX_OK";
+    case PARALLAX_ERR_INVALID_ARG: return "PARALLAX_ERR_INVALID_ARG";
+    case PARALLAX_ERR_UNSUPPORTED: return "PARALLAX_ERR_UNSUPPORTED";
+    case PARALLAX_ERR_LAUNCH: return "PARALLAX_ERR_LAUNCH";
+    }
+    return "PARALLAX_ERR_UNKNOWN";
+}
+
+parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, const void *r,
+                                  float *o, float *lse, int B, int H, int L, int d,
+                                  parallax_strides sq, parallax_strides sk, parallax_strides sv,
+                                  parallax_strides sr, parallax_strides so, float softmax_scale,
+                                  int window, int n_sink, void *stream) {
+    if (B < 0 || H < 0 || L < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!scale_ok(softmax_scale) || window < 0 || n_sink < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * H * L == 0)
+        return PARALLAX_OK;
+    if (!q || !k || !v || !r || !o || !lse)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(r, 16) ||
+        !aligned(o, 16) || !aligned(lse, 4))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!bf16_strides_ok(sq) || !bf16_strides_ok(sk) || !bf16_strides_ok(sv) ||
+        !bf16_strides_ok(sr) || !f32_strides_ok(so))
+        return PARALLAX_ERR_INVALID_ARG;
+
+    const int64_t n_qtiles = ((int64_t)L + plx::kFwdBlockM - 1) / plx::kFwdBlockM;
+    if ((int64_t)B * H * n_qtiles > INT_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+
+    plx::FwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.r = static_cast<const uint16_t *>(r);
+    a.o = o;
+    a.lse = lse;
+    a.q_b = sq.b; a.q_h = sq.h; a.q_l = sq.l;
+    a.k_b = sk.b; a.k_h = sk.h; a.k_l = sk.l;
+    a.v_b = sv.b; a.v_h = sv.h; a.v_l = sv.l;
+    a.r_b = sr.b; a.r_h = sr.h; a.r_l = sr.l;
+    a.o_b = so.b; a.o_h = so.h; a.o_l = so.l;
+    a.B = B;
+    a.H = H;
+    a.L = L;
+    a.n_qtiles = (int)n_qtiles;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.window = window;
+    a.n_sink = n_sink;
+    hipError_t e = plx::launch_fwd(a, d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
+parallax_status parallax_attn_decode(const void *q, const void *r, const void *k_cache,
+                                     const void *v_cache, const int32_t *seqlens, float *o,
+                                     float *lse, int B, int H, int Lmax, int d,
+                                     parallax_strides sk, parallax_strides sv,
+                                     float softmax_scale, int num_splits, void *stream) {
+    if (B < 0 || H < 0 || Lmax < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (num_splits != 1 && num_splits != 2 && num_splits != 4 && num_splits != 8 &&
+        num_splits != 16)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!scale_ok(softmax_scale))
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * H == 0)
+        return PARALLAX_OK;
+    if (!q || !r || !o || !lse || (Lmax > 0 && (!k_cache || !v_cache)))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(r, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(o, 4) || !aligned(lse, 4) || !aligned(seqlens, 4))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!bf16_strides_ok(sk) || !bf16_strides_ok(sv))
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * H > INT_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+
+    plx::DecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.r = static_cast<const uint16_t *>(r);
+    a.k = static_cast<const uint16_t *>(k_cache);
+    a.v = static_cast<const uint16_t *>(v_cache);
+    a.seqlens = seqlens;
+    a.o = o;
+    a.lse = lse;
+    a.k_b = sk.b; a.k_h = sk.h; a.k_l = sk.l;
+    a.v_b = sv.b; a.v_h = sv.h; a.v_l = sv.l;
+    a.B = B;
+    a.H = H;
+    a.Lmax = Lmax;
+    a.scale_log2 = softmax_scale * kLog2e;
+    hipError_t e = plx::launch_decode(a, d, num_splits, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
+}  // extern "C"

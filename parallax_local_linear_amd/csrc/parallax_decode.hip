@@ -1,0 +1,231 @@
+// Parallax decode step for gfx950: one query and probe per (sequence, head)
+// against a contiguous bf16 KV cache.
+//
+// A decoding Parallax model keeps a KV cache like softmax attention (tilnote
+// note on Parallax, section on it being a different estimator rather than a
+// linear-time attention), and reading that cache is the cost: the KV cache
+// is the memory bottleneck of inference ("Simple linear attention language
+// models balance the recall-throughput tradeoff" review, abstract and
+// motivation; "Sliding-window beats linear attention" review, sec. 1).  The
+// kernel is therefore built to stream K and V from HBM once, with many
+// 16-byte loads in flight, and to keep all arithmetic in fp32.
+//
+// Work split: one workgroup per (b, h) with NS wavefronts; wavefront s owns
+// one contiguous chunk of the cache.  Inside a wavefront, D/8 lanes share a
+// key (16 bytes = 8 features each), so a wave step covers 512/D keys and
+// every global load is fully coalesced.  Each lane group keeps running
+//     m, ell = sum p~, S = sum p~ s, A = sum p~ v, C = sum p~ s v
+// (s = rho . k, p~ = 2^(x - m)) for its 8 features.  The partial states are
+// merged first across lane groups with shuffles, then across wavefronts
+// through LDS, by rescaling each (ell, S, A, C) with 2^(m_s - M).  The
+// normalised pair (o, lse) would NOT merge correctly for Parallax because
+// the correction's key mean depends on the whole visible set; the
+// un-normalised sums do.
+#include "device_common.h"
+#include "launch.h"
+
+namespace plx {
+namespace {
+
+template <int D, int NS>
+__global__ __launch_bounds__(64 * NS) void parallax_decode_kernel(DecodeArgs a) {
+    constexpr int LPK = D / 8;     // lanes per key
+    constexpr int KPS = 64 / LPK;  // keys per wave step
+    constexpr int U = 4;           // wave steps per iteration (loads in flight)
+
+    __shared__ float s_m[NS], s_l[NS], s_s[NS];
+    __shared__ float s_A[NS][D], s_C[NS][D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = lane / LPK;
+    const int sub = lane % LPK;
+    const int bh = blockIdx.x;
+    const int b = bh / a.H;
+    const int h = bh - b * a.H;
+    const float c = a.scale_log2;
+
+    int n = a.seqlens ? a.seqlens[b] : a.Lmax;
+    n = n < 0 ? 0 : (n > a.Lmax ? a.Lmax : n);
+    const int chunk = (n + NS - 1) / NS;
+    const int start = min(wave * chunk, n);
+    const int end = min(start + chunk, n);
+
+    float qv[8], rv[8];
+    {
+        const u32x4 qw = ldg16(a.q + (int64_t)bh * D + 8 * sub);
+        const u32x4 rw = ldg16(a.r + (int64_t)bh * D + 8 * sub);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            qv[2 * w] = bf16_lo(qw[w]);
+            qv[2 * w + 1] = bf16_hi(qw[w]);
+            rv[2 * w] = bf16_lo(rw[w]);
+            rv[2 * w + 1] = bf16_hi(rw[w]);
+        }
+    }
+    const uint16_t *kb = a.k + (int64_t)b * a.k_b + (int64_t)h * a.k_h + 8 * sub;
+    const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h + 8 * sub;
+
+    float m = kNegInf, ell = 0.f, ssum = 0.f;
+    float A[8], C[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        A[e] = 0.f;
+        C[e] = 0.f;
+    }
+
+    for (int j = start; j < end; j += KPS * U) {
+        u32x4 kw[U], vw[U];
+        bool valid[U];
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int key = j + u * KPS + grp;
+            valid[u] = key < end;
+            kw[u] = valid[u] ? ldg16(kb + (int64_t)key * a.k_l) : zero;
+            vw[u] = valid[u] ? ldg16(vb + (int64_t)key * a.v_l) : zero;
+        }
+        float x[U], sr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float dq = 0.f, dr = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float k0 = bf16_lo(kw[u][w]);
+                const float k1 = bf16_hi(kw[u][w]);
+                dq = fmaf(qv[2 * w], k0, dq);
+                dq = fmaf(qv[2 * w + 1], k1, dq);
+                dr = fmaf(rv[2 * w], k0, dr);
+                dr = fmaf(rv[2 * w + 1], k1, dr);
+            }
+#pragma unroll
+            for (int off = 1; off < LPK; off <<= 1) {
+                dq += __shfl_xor(dq, off, 64);
+                dr += __shfl_xor(dr, off, 64);
+            }
+            x[u] = valid[u] ? dq * c : kNegInf;
+            sr[u] = dr;
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u)
+            mt = fmaxf(mt, x[u]);
+        const float m_new = fmaxf(m, mt);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m - m_new);
+        m = m_new;
+        const float msub = (m == kNegInf) ? 0.f : m;
+        ell *= alpha;
+        ssum *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            A[e] *= alpha;
+            C[e] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float p = exp2_fast(x[u] - msub);
+            const float w = p * sr[u];
+            ell += p;
+            ssum += w;
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                const float v0 = bf16_lo(vw[u][q2]);
+                const float v1 = bf16_hi(vw[u][q2]);
+                A[2 * q2] = fmaf(p, v0, A[2 * q2]);
+                A[2 * q2 + 1] = fmaf(p, v1, A[2 * q2 + 1]);
+                C[2 * q2] = fmaf(w, v0, C[2 * q2]);
+                C[2 * q2 + 1] = fmaf(w, v1, C[2 * q2 + 1]);
+            }
+        }
+    }
+
+    // Merge the lane groups of this wavefront (same features, disjoint keys).
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) {
+        const float mo = __shfl_xor(m, off, 64);
+        const float lo = __shfl_xor(ell, off, 64);
+        const float so = __shfl_xor(ssum, off, 64);
+        const float M = fmaxf(m, mo);
+        const float f = (M == kNegInf) ? 0.f : exp2_fast(m - M);
+        const float fo = (M == kNegInf) ? 0.f : exp2_fast(mo - M);
+        ell = ell * f + lo * fo;
+        ssum = ssum * f + so * fo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            A[e] = A[e] * f + __shfl_xor(A[e], off, 64) * fo;
+            C[e] = C[e] * f + __shfl_xor(C[e], off, 64) * fo;
+        }
+        m = M;
+    }
+    if (lane < LPK) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s_A[wave][8 * sub + e] = A[e];
+            s_C[wave][8 * sub + e] = C[e];
+        }
+        if (lane == 0) {
+            s_m[wave] = m;
+            s_l[wave] = ell;
+            s_s[wave] = ssum;
+        }
+    }
+    __syncthreads();
+
+    // Merge the wavefronts' chunks and write the row.
+    float M = kNegInf;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        M = fmaxf(M, s_m[s]);
+    float lt = 0.f, st = 0.f;
+    float f[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        f[s] = (M == kNegInf) ? 0.f : exp2_fast(s_m[s] - M);
+        lt += f[s] * s_l[s];
+        st += f[s] * s_s[s];
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float keep = 1.f - st * inv;
+    for (int nidx = tid; nidx < D; nidx += 64 * NS) {
+        float at = 0.f, ct = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            at += f[s] * s_A[s][nidx];
+            ct += f[s] * s_C[s][nidx];
+        }
+        a.o[(int64_t)bh * D + nidx] = (at * keep + ct) * inv;
+    }
+    if (tid == 0)
+        a.lse[bh] = lt > 0.f ? (M + log2f(lt)) * kLn2 : kNegInf;
+}
+
+template <int D, int NS>
+hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.B * a.H));
+    const dim3 block(64 * NS);
+    DecodeArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&parallax_decode_kernel<D, NS>), grid,
+                           block, params, 0, stream);
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs &a, int num_splits, hipStream_t stream) {
+    switch (num_splits) {
+    case 1: return launch_decode_t<D, 1>(a, stream);
+    case 2: return launch_decode_t<D, 2>(a, stream);
+    case 4: return launch_decode_t<D, 4>(a, stream);
+    case 8: return launch_decode_t<D, 8>(a, stream);
+    default: return launch_decode_t<D, 16>(a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, int d, int num_splits, hipStream_t stream) {
+    return d == 64 ? launch_decode_d<64>(a, num_splits, stream)
+                   : launch_decode_d<128>(a, num_splits, stream);
+}
+
+}  // namespace plx

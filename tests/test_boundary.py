@@ -1,0 +1,149 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+No call here reaches a kernel launch: every call either fails validation or
+describes an empty problem, both of which return before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from parallax_local_linear_amd import binding
+from parallax_local_linear_amd.binding import parallax_strides as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "parallax.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+A16 = 0x10000          # fake, 16-byte aligned device address (never dereferenced)
+CONTIG = S(8 * 128 * 64, 128 * 64, 64)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(parallax_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIBRARY):
+        pytest.fail("libparallax.so is not built; run `python -m parallax_local_linear_amd.build`")
+    return binding.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(binding.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for code, name in binding.STATUS_NAMES.items():
+        assert binding.parallax_status_string(code) == name
+    assert binding.parallax_status_string(99) == "PARALLAX_ERR_UNKNOWN"
+
+
+def fwd(lib, q=A16, k=A16, v=A16, r=A16, o=A16, lse=A16, B=1, H=2, L=64, d=64,
+        sq=CONTIG, sk=CONTIG, sv=CONTIG, sr=CONTIG, so=CONTIG, scale=0.125, window=0,
+        n_sink=0):
+    return lib.parallax_attn_fwd(q, k, v, r, o, lse, B, H, L, d, sq, sk, sv, sr, so, scale,
+                                 window, n_sink, None)
+
+
+def dec(lib, q=A16, r=A16, k=A16, v=A16, seqlens=None, o=A16, lse=A16, B=2, H=2, Lmax=64,
+        d=128, sk=CONTIG, sv=CONTIG, scale=0.1, splits=16):
+    return lib.parallax_attn_decode(q, r, k, v, seqlens, o, lse, B, H, Lmax, d, sk, sv, scale,
+                                    splits, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED),
+    (dict(d=256), UNSUPPORTED),
+    (dict(B=-1), INVALID),
+    (dict(H=-2), INVALID),
+    (dict(L=-5), INVALID),
+    (dict(q=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(v=None), INVALID),
+    (dict(r=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(lse=None), INVALID),
+    (dict(q=A16 + 8), INVALID),
+    (dict(v=A16 + 2), INVALID),
+    (dict(o=A16 + 4), INVALID),
+    (dict(lse=A16 + 2), INVALID),
+    (dict(window=-1), INVALID),
+    (dict(n_sink=-3), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-0.5), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(sq=S(8 * 128 * 64, 128 * 64, 60)), INVALID),
+    (dict(sk=S(8 * 128 * 64, 4, 64)), INVALID),
+    (dict(sv=S(-64, 128 * 64, 64)), INVALID),
+    (dict(so=S(8 * 128 * 64, 128 * 64, 66)), INVALID),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(L=0),
+                                dict(B=0, q=None, k=None, v=None, r=None, o=None, lse=None)])
+def test_fwd_empty_problem_is_a_no_op(lib, kw):
+    assert fwd(lib, **kw) == OK
+
+
+def test_fwd_empty_still_checks_d(lib):
+    assert fwd(lib, L=0, d=80) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED),
+    (dict(splits=3), UNSUPPORTED),
+    (dict(splits=32), UNSUPPORTED),
+    (dict(splits=0), UNSUPPORTED),
+    (dict(B=-1), INVALID),
+    (dict(Lmax=-1), INVALID),
+    (dict(q=None), INVALID),
+    (dict(r=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(lse=None), INVALID),
+    (dict(q=A16 + 4), INVALID),
+    (dict(k=A16 + 8), INVALID),
+    (dict(seqlens=A16 + 2), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(sk=S(8, 8, 4)), INVALID),
+])
+def test_decode_rejects(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    assert dec(lib, B=0, q=None, r=None, k=None, v=None, o=None, lse=None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.parallax_attn_fwd(x, x, x, x)
+    with pytest.raises(TypeError):
+        binding.parallax_attn_fwd(x.float(), x, x, x)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = binding._lib
+    binding._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            binding.load_library(str(tmp_path / "nope.so"))
+    finally:
+        binding._lib = saved

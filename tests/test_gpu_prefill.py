@@ -1,0 +1,176 @@
+"""GPU parity of the prefill kernel against the fp64 oracle (MI355X only).
+
+Every case compares the HIP path element by element with the oracle run on
+the same bf16 inputs: whole outputs at sizes the oracle finishes in seconds
+(several tiles plus ragged tails), sampled rows at the full workload sizes
+in the same launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import compare, default_scale, f64, oracle_rows, sample_rows, say
+from parallax_local_linear_amd import parallax_attn_fwd, workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+
+
+def rand(shape, seed, scale=1.0):
+    return workloads.random_tensor(shape, seed, device="cpu", scale=scale)
+
+
+def full_check(orc, q, k, v, r, window=0, n_sink=0, scale=None, what=""):
+    d = q.shape[-1]
+    scale = default_scale(d) if scale is None else scale
+    say("[case] %s shape=%s window=%d n_sink=%d" % (what, tuple(q.shape), window, n_sink))
+    qd, kd, vd, rd = (x.to(DEV) for x in (q, k, v, r))
+    o, lse = parallax_attn_fwd(qd, kd, vd, rd, softmax_scale=scale, window=window, n_sink=n_sink)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.fwd(f64(q), f64(k), f64(v), f64(r), scale=scale, window=window,
+                             n_sink=n_sink)
+    return compare(f64(o), f64(lse), o_ref, lse_ref, what), o, lse
+
+
+def test_tiny_workload(orc):
+    """B=1 H=2 L=256 d=64, fp32 draws rounded to bf16; plus the unrounded error (reported)."""
+    cfg = workloads.TINY
+    q32, k32, v32, r32 = workloads.prefill_inputs(cfg, dtype=torch.float32)
+    q, k, v, r = (x.to(torch.bfloat16) for x in (q32, k32, v32, r32))
+    _, o, _ = full_check(orc, q, k, v, r, what="tiny")
+    o_fp32_ref, _ = orc.fwd(f64(q32), f64(k32), f64(v32), f64(r32))
+    say("[report] tiny vs oracle on the unrounded fp32 inputs: max|dO|=%.3e"
+        % float(np.max(np.abs(f64(o) - o_fp32_ref))))
+
+
+def test_tiny_probe_zero_is_softmax(orc):
+    """rho = 0: the kernel must reduce to softmax attention (oracle pinned to SDPA)."""
+    cfg = workloads.TINY
+    q, k, v, _ = workloads.prefill_inputs(cfg)
+    full_check(orc, q, k, v, torch.zeros_like(q), what="tiny rho=0")
+
+
+SMALL = [
+    # (B, H, L, d, window, n_sink)
+    (1, 2, 1000, 64, 0, 0),
+    (1, 2, 1000, 128, 0, 0),
+    (2, 1, 129, 64, 0, 0),
+    (1, 1, 1, 64, 0, 0),
+    (1, 1, 1, 128, 0, 0),
+    (1, 1, 63, 128, 0, 0),
+    (1, 1, 65, 64, 0, 0),
+    (3, 1, 200, 128, 0, 0),
+    (1, 2, 300, 64, 1, 0),
+    (1, 2, 300, 128, 128, 4),
+    (1, 1, 700, 64, 37, 70),
+    (1, 1, 700, 128, 200, 130),
+    (1, 1, 500, 64, 600, 0),
+    (1, 1, 500, 64, 0, 5),
+    (1, 1, 257, 128, 64, 4),
+    (1, 1, 1000, 64, 1, 64),
+    (1, 2, 1500, 64, 128, 4),
+]
+
+
+@pytest.mark.parametrize("B,H,L,d,window,n_sink", SMALL)
+def test_small_shapes(orc, B, H, L, d, window, n_sink):
+    seed = B * 1000003 + H * 10007 + L * 101 + d + window * 7 + n_sink
+    q, k, v, r = (rand((B, H, L, d), seed + t) for t in range(4))
+    full_check(orc, q, k, v, r, window=window, n_sink=n_sink,
+               what="small B%d H%d L%d d%d" % (B, H, L, d))
+
+
+def test_window_one_returns_values(orc):
+    """Window 1 and no sinks: each row sees only itself, so o = v (up to f16 rounding of v)."""
+    q, k, v, r = (rand((1, 2, 333, 128), 900 + t) for t in range(4))
+    o, lse = parallax_attn_fwd(*(x.to(DEV) for x in (q, k, v, r)), window=1)
+    np.testing.assert_allclose(f64(o), f64(v), atol=1e-6, rtol=2 ** -10)
+
+
+def test_scaled_inputs_and_custom_scale(orc):
+    q, k, v, r = (rand((1, 2, 400, 64), 950 + t, scale=0.5) for t in range(4))
+    full_check(orc, q, k, v, r, scale=0.3, what="custom scale 0.3")
+
+
+@pytest.mark.parametrize("cfg", [workloads.PREFILL_06B, workloads.PREFILL_17B, workloads.LOCAL],
+                         ids=lambda c: c.name)
+def test_full_size_sampled_rows(orc, cfg):
+    """The benchmark workloads at full size; sampled rows of several (b, h) against the oracle."""
+    say("[case] full size %s" % cfg.name)
+    q, k, v, r = workloads.prefill_inputs(cfg, device=DEV)
+    scale = default_scale(cfg.d)
+    o, lse = parallax_attn_fwd(q, k, v, r, softmax_scale=scale, window=cfg.window,
+                               n_sink=cfg.n_sink)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    rng = np.random.default_rng(cfg.seed)
+    BH = cfg.B * cfg.H
+    pairs = sorted({(0, 0), (cfg.B - 1, cfg.H - 1)} |
+                   {(int(x) // cfg.H, int(x) % cfg.H) for x in rng.integers(0, BH, size=2)})
+    for b, h in pairs:
+        rows = sample_rows(cfg.L, rng)
+        o_ref, lse_ref = oracle_rows(orc, q, k, v, r, b, h, rows, scale, cfg.window, cfg.n_sink)
+        idx = torch.as_tensor(rows, device=DEV)
+        compare(f64(o[b, h].index_select(0, idx)), f64(lse[b, h].index_select(0, idx)),
+                o_ref, lse_ref, "%s b=%d h=%d (%d rows)" % (cfg.name, b, h, len(rows)))
+
+
+def test_constant_values_give_constant_output():
+    """Weights 1 + rho.(k - kbar) sum to one under p, so v = 1 everywhere gives o = 1."""
+    q, k, r = (rand((2, 2, 777, 128), 1000 + t) for t in range(3))
+    v = torch.ones_like(q)
+    o, _ = parallax_attn_fwd(*(x.to(DEV) for x in (q, k, v, r)), window=100, n_sink=3)
+    err = float((o - 1).abs().max())
+    say("[invariant] constant values: max|o-1|=%.3e" % err)
+    assert err <= 2e-2
+
+
+def test_deterministic():
+    q, k, v, r = (rand((2, 4, 1100, 128), 1100 + t).to(DEV) for t in range(4))
+    o1, l1 = parallax_attn_fwd(q, k, v, r)
+    o2, l2 = parallax_attn_fwd(q, k, v, r)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_strided_layouts_match_contiguous():
+    """[B, L, H, d] storage (viewed as [B, H, L, d]) and a strided output give identical bits."""
+    B, H, L, d = 2, 3, 517, 64
+    base = [rand((B, L, H, d), 1200 + t).to(DEV) for t in range(4)]
+    views = [x.permute(0, 2, 1, 3) for x in base]
+    conts = [x.contiguous() for x in views]
+    o1, l1 = parallax_attn_fwd(*conts, window=64, n_sink=2)
+    big = torch.full((B, H, L, 2 * d), float("nan"), device=DEV)
+    out = big[..., :d]
+    o2, l2 = parallax_attn_fwd(*views, window=64, n_sink=2, out=out)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.isnan(big[..., d:]).all()
+
+
+def test_64bit_offsets(orc):
+    """More than 2^31 elements per tensor (windowed so it stays fast): rows at the far end."""
+    B, H, L, d = 1, 2, (1 << 23) + 1000, 128
+    window, n_sink = 128, 4
+    say("[case] 64-bit offsets B=%d H=%d L=%d d=%d" % (B, H, L, d))
+    q, k, v, r = (workloads.random_tensor((B, H, L, d), 1300 + t, device=DEV) for t in range(4))
+    o, lse = parallax_attn_fwd(q, k, v, r, window=window, n_sink=n_sink)
+    torch.cuda.synchronize()
+    scale = default_scale(d)
+    for i in (L - 1, L - 200, L // 2, 5):
+        # The visible set of row i is the sinks plus the last `window` keys; give the
+        # oracle exactly that context, re-indexed so that it keeps the same visible set.
+        lo = max(n_sink, i - window + 1)
+        keys = list(range(min(n_sink, i + 1))) + list(range(lo, i + 1))
+        keys = sorted(set(keys))
+        idx = torch.as_tensor(keys, device=DEV)
+        K = f64(k[0, 1].index_select(0, idx))
+        V = f64(v[0, 1].index_select(0, idx))
+        pos = len(keys) - 1
+        o_ref, lse_ref = orc.rows(f64(q[0, 1, i:i + 1]), f64(r[0, 1, i:i + 1]), [pos], K, V,
+                                  scale, 0, 0)
+        compare(f64(o[0, 1, i:i + 1]), f64(lse[0, 1, i:i + 1]), o_ref, lse_ref,
+                "64-bit offsets row %d" % i)
