@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "Parallax attn fwd TFLOP/s & % bf16 MFMA peak (L=8192,d=128); decode HBM GB/s"
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16/f16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+COPY_BYTES = 1 << 30        # plain copy used to calibrate the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_fwd.hip"),
@@ -49,6 +50,9 @@ def parse():
                    help="(b,h) slices of the prefill workload the CPU oracle computes")
     p.add_argument("--extra", action="store_true",
                    help="also time the other prefill workloads (printed to stderr)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run a plain 1 GiB device-to-device copy kernel three times, "
+                        "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
@@ -154,6 +158,15 @@ def main():
     dlse = torch.empty(dq.shape[:2], dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 3 x %d bytes read and written" % COPY_BYTES,
+              file=sys.stderr, flush=True)
+        del src, dst
 
     def step(events=None):
         if events is not None:
