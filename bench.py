@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (profiling runs)")
-    p.add_argument("--cpu-sample-heads", type=int, default=8,
+    p.add_argument("--cpu-sample-heads", type=int, default=16,
                    help="(b,h) slices of the prefill workload the CPU oracle computes")
     p.add_argument("--extra", action="store_true",
                    help="also time the other prefill workloads (printed to stderr)")

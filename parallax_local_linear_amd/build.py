@@ -18,6 +18,14 @@ LIBRARY = os.path.join(PKG, "libparallax.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["parallax_api.hip", "parallax_fwd.hip", "parallax_decode.hip"]
+# Kernel sources: no NaN ever reaches a max or compare (masking uses -inf and
+# non-finite inputs are outside the contract), so max chains need no NaN
+# canonicalisation.  The host API keeps IEEE NaN semantics for its argument
+# checks.
+KERNEL_FLAGS = {
+    "parallax_fwd.hip": ["-fno-honor-nans"],
+    "parallax_decode.hip": ["-fno-honor-nans"],
+}
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code.
@@ -39,7 +47,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     objects = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *extra_flags, "-c",
+        cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *KERNEL_FLAGS.get(src, []), *extra_flags, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

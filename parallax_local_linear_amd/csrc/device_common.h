@@ -25,6 +25,26 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Buffer resource over [base, base + nbytes): loads at or past nbytes return
+// zeros, so no lane ever reads outside that range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes,
+                                             0x00020000);
+}
+
+// 16-byte buffer load at a per-lane byte offset.
+__device__ __forceinline__ u32x4 bufld16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
+// Bytes from the start of row j0 through the last element of row L-1 of a
+// [rows, d] slice with row stride `ld` elements (2-byte elements), clamped
+// to the 32-bit range of a buffer resource.
+__device__ __forceinline__ uint32_t rows_bytes(int j0, int L, int64_t ld, int d) {
+    const int64_t n = (int64_t)(L - 1 - j0) * ld * 2 + (int64_t)d * 2;
+    return n <= 0 ? 0u : (n > 0xffffffffll ? 0xffffffffu : (uint32_t)n);
+}
+
 // bf16 bits -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -36,7 +36,7 @@ struct DecodeArgs {
 };
 
 // Query rows per prefill workgroup.
-constexpr int kFwdBlockM = 128;
+constexpr int kFwdBlockM = 64;
 
 hipError_t launch_fwd(const FwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int d, int num_splits, hipStream_t stream);

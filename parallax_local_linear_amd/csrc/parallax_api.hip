@@ -25,6 +25,10 @@ bool f32_strides_ok(const parallax_strides &s) {
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
+// Row strides are used in 32-bit byte offsets inside a tile of rows.
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;
+bool row_stride_ok(const parallax_strides &s) { return s.l < kMaxRowStride; }
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace
@@ -62,6 +66,8 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
     if (!bf16_strides_ok(sq) || !bf16_strides_ok(sk) || !bf16_strides_ok(sv) ||
         !bf16_strides_ok(sr) || !f32_strides_ok(so))
         return PARALLAX_ERR_INVALID_ARG;
+    if (!row_stride_ok(sq) || !row_stride_ok(sk) || !row_stride_ok(sv) || !row_stride_ok(sr))
+        return PARALLAX_ERR_UNSUPPORTED;
 
     const int64_t n_qtiles = ((int64_t)L + plx::kFwdBlockM - 1) / plx::kFwdBlockM;
     if ((int64_t)B * H * n_qtiles > INT_MAX)
