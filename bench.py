@@ -105,19 +105,22 @@ def time_prefill_only(cfg, steps, warmup, stream):
     import torch
 
     from parallax_local_linear_amd import accounting, parallax_attn_fwd, workloads
+    from parallax_local_linear_amd import parallax_attn_fwd_workspace_size
     q, k, v, r = workloads.prefill_inputs(cfg, device="cuda:0")
     o = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(parallax_attn_fwd_workspace_size(cfg.B, cfg.H, cfg.L, cfg.d),
+                     dtype=torch.uint8, device="cuda:0")
     for _ in range(warmup):
         parallax_attn_fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,
-                          stream=stream)
+                          workspace=ws, stream=stream)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
         parallax_attn_fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,
-                          stream=stream)
+                          workspace=ws, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -136,7 +139,7 @@ def main():
     import torch
 
     from parallax_local_linear_amd import (accounting, parallax_attn_decode, parallax_attn_fwd,
-                                           workloads)
+                                           parallax_attn_fwd_workspace_size, workloads)
     from parallax_local_linear_amd.binding import LIBRARY
 
     if not os.path.exists(LIBRARY):
@@ -153,6 +156,8 @@ def main():
     q, k, v, r = workloads.prefill_inputs(pcfg, device=dev)
     o = torch.empty(q.shape, dtype=torch.float32, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(parallax_attn_fwd_workspace_size(pcfg.B, pcfg.H, pcfg.L, pcfg.d),
+                     dtype=torch.uint8, device=dev)
     dq, dk, dv, dr = workloads.decode_inputs(dcfg, device=dev)
     do = torch.empty(dq.shape, dtype=torch.float32, device=dev)
     dlse = torch.empty(dq.shape[:2], dtype=torch.float32, device=dev)
@@ -172,7 +177,7 @@ def main():
         if events is not None:
             events[0].record(stream)
         parallax_attn_fwd(q, k, v, r, window=pcfg.window, n_sink=pcfg.n_sink, out=o, lse=lse,
-                          stream=stream)
+                          workspace=ws, stream=stream)
         if events is not None:
             events[1].record(stream)
         parallax_attn_decode(dq, dr, dk, dv, None, num_splits=dcfg.num_splits, out=do,

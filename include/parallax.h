@@ -28,7 +28,10 @@
  *   - Inputs q, k, v, r are bfloat16 (raw 16-bit storage, passed as void*);
  *     outputs o and lse are float32.  The feature dimension d is 64 or 128.
  *   - All pointers are DEVICE pointers owned by the caller.  The library
- *     never allocates, frees or synchronises; it needs no workspace.
+ *     never allocates, frees or synchronises.  The prefill takes a device
+ *     workspace from the caller (parallax_attn_fwd_workspace_size); its
+ *     contents need no initialisation and are scratch once the call's
+ *     work on `stream` has finished.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously.  Calls are stateless and thread-safe.
  *   - Every argument is checked on the host before anything is enqueued; a
@@ -36,14 +39,16 @@
  *     PARALLAX_ERR_LAUNCH reports a failed kernel launch.
  *   - Outputs must not alias inputs.  Non-finite inputs give undefined
  *     results.
- *   - Numerical range: the kernels feed the softmax weights, the products
- *     p * (rho . k) and the values to float16 matrix-core operands, so
- *     |v| and |rho_i . k_j| must stay below 4096 (values beyond float16's
- *     range become infinite).
+ *   - Numerical range: the kernels feed the un-normalised softmax weights
+ *     (at most 2^5 each), their products with rho_i . k_j and the values
+ *     to float16 matrix-core operands, so |rho_i . k_j| must stay below
+ *     2047 and |v| at or below 65504 (float16's largest finite value);
+ *     beyond that results become infinite or NaN.
  */
 #ifndef PARALLAX_H
 #define PARALLAX_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -66,6 +71,15 @@ typedef struct {
 } parallax_strides;
 
 /*
+ * Bytes of device workspace parallax_attn_fwd needs for these sizes: the
+ * values converted to float16 and laid out per 32-key stage, i.e.
+ * B * H * ceil(L / 32) * 32 * d * 2 bytes (0 when B, H or L is 0).  Returns
+ * 0 for sizes parallax_attn_fwd would reject (negative sizes, d not in
+ * {64, 128}).
+ */
+size_t parallax_attn_fwd_workspace_size(int B, int H, int L, int d);
+
+/*
  * Causal prefill forward.
  *
  *   q, k, v, r : bf16 tensors of logical shape [B, H, L, d] with strides
@@ -84,6 +98,14 @@ typedef struct {
  *                (or j is a sink).  Must be >= 0.
  *   n_sink     : number of leading sink keys (always visible once causal);
  *                >= 0; only matters when window > 0.
+ *   workspace  : device memory of at least workspace_bytes >=
+ *                parallax_attn_fwd_workspace_size(B, H, L, d) bytes, 16-byte
+ *                aligned, not aliasing any input or output; NULL is allowed
+ *                only when that size is 0.  Two calls in flight at once need
+ *                two workspaces.
+ *
+ * Two kernels run on `stream`: the first converts v into the workspace,
+ * the second computes o and lse.
  */
 parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, const void *r,
                                   float *o, float *lse,
@@ -92,6 +114,7 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
                                   parallax_strides sv, parallax_strides sr,
                                   parallax_strides so,
                                   float softmax_scale, int window, int n_sink,
+                                  void *workspace, size_t workspace_bytes,
                                   void *stream);
 
 /*

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
                 2: "PARALLAX_ERR_UNSUPPORTED", 3: "PARALLAX_ERR_LAUNCH"}
 
 # Every symbol include/parallax.h declares.
-EXPORTED = ("parallax_attn_fwd", "parallax_attn_decode", "parallax_status_string")
+EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_decode",
+            "parallax_status_string")
 
 
 class parallax_strides(ctypes.Structure):
@@ -54,9 +55,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     S = parallax_strides
+    lib.parallax_attn_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.parallax_attn_fwd_workspace_size.argtypes = [i, i, i, i]
     lib.parallax_attn_fwd.restype = ctypes.c_int
     lib.parallax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, S, S, S, S, S,
-                                      f, i, i, vp]
+                                      f, i, i, vp, ctypes.c_size_t, vp]
     lib.parallax_attn_decode.restype = ctypes.c_int
     lib.parallax_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, S, S,
                                          f, i, vp]
@@ -99,9 +102,19 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int):
         raise ValueError("%s must have %d dimensions" % (name, ndim))
 
 
+def parallax_attn_fwd_workspace_size(B: int, H: int, L: int, d: int) -> int:
+    """Bytes of device workspace the prefill needs for these sizes."""
+    return int(load_library().parallax_attn_fwd_workspace_size(int(B), int(H), int(L), int(d)))
+
+
 def parallax_attn_fwd(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
-                      out=None, lse=None, stream=None):
-    """Causal Parallax prefill. q, k, v, r: bf16 [B,H,L,d] -> (o fp32 [B,H,L,d], lse fp32 [B,H,L])."""
+                      out=None, lse=None, workspace=None, stream=None):
+    """Causal Parallax prefill. q, k, v, r: bf16 [B,H,L,d] -> (o fp32 [B,H,L,d], lse fp32 [B,H,L]).
+
+    ``workspace`` (a device tensor of at least
+    ``parallax_attn_fwd_workspace_size(B, H, L, d)`` bytes) is allocated with
+    torch when not given.
+    """
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (r, "r")):
         _need(t, n, torch.bfloat16, 4)
         if t.shape != q.shape:
@@ -120,10 +133,17 @@ def parallax_attn_fwd(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
     if not lse.is_contiguous():
         raise ValueError("lse must be contiguous")
     lib = load_library()
+    ws_bytes = parallax_attn_fwd_workspace_size(B, H, L, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a device tensor")
+    have = workspace.numel() * workspace.element_size()
     st = lib.parallax_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, H, L, d, _strides(q), _strides(k), _strides(v), _strides(r), _strides(out),
-        float(softmax_scale), int(window), int(n_sink), _stream_handle(q.device, stream))
+        float(softmax_scale), int(window), int(n_sink), workspace.data_ptr(), have,
+        _stream_handle(q.device, stream))
     _check(st)
     return out, lse
 

@@ -39,10 +39,12 @@ __device__ __forceinline__ u32x4 bufld16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 // Bytes from the start of row j0 through the last element of row L-1 of a
 // [rows, d] slice with row stride `ld` elements (2-byte elements), clamped
-// to the 32-bit range of a buffer resource.
+// to the 32-bit range of a buffer resource (0 when j0 is past the end).
 __device__ __forceinline__ uint32_t rows_bytes(int j0, int L, int64_t ld, int d) {
-    const int64_t n = (int64_t)(L - 1 - j0) * ld * 2 + (int64_t)d * 2;
-    return n <= 0 ? 0u : (n > 0xffffffffll ? 0xffffffffu : (uint32_t)n);
+    const int64_t rows = (int64_t)L - 1 - j0;
+    const uint64_t n = (uint64_t)(rows < 0 ? 0 : rows) * (uint64_t)ld * 2u + (uint64_t)d * 2u;
+    const uint64_t clamped = n < 0xffffffffull ? n : 0xffffffffull;
+    return rows < 0 ? 0u : (uint32_t)clamped;
 }
 
 // bf16 bits -> fp32 (exact).

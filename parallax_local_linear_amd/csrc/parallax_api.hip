@@ -1,5 +1,5 @@
 // C-ABI entry points of the Parallax library: host-side argument checks,
-// then one kernel launch on the caller's stream.  No allocation, no
+// then the kernel launches on the caller's stream.  No allocation, no
 // synchronisation, no global state.
 #include <climits>
 #include <cmath>
@@ -45,11 +45,18 @@ const char *parallax_status_string(parallax_status s) {
     return "PARALLAX_ERR_UNKNOWN";
 }
 
+size_t parallax_attn_fwd_workspace_size(int B, int H, int L, int d) {
+    if (B < 0 || H < 0 || L < 0 || (d != 64 && d != 128))
+        return 0;
+    return plx::fwd_workspace_bytes(B, H, L, d);
+}
+
 parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, const void *r,
                                   float *o, float *lse, int B, int H, int L, int d,
                                   parallax_strides sq, parallax_strides sk, parallax_strides sv,
                                   parallax_strides sr, parallax_strides so, float softmax_scale,
-                                  int window, int n_sink, void *stream) {
+                                  int window, int n_sink, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
     if (B < 0 || H < 0 || L < 0)
         return PARALLAX_ERR_INVALID_ARG;
     if (d != 64 && d != 128)
@@ -68,8 +75,12 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
         return PARALLAX_ERR_INVALID_ARG;
     if (!row_stride_ok(sq) || !row_stride_ok(sk) || !row_stride_ok(sv) || !row_stride_ok(sr))
         return PARALLAX_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, 16) ||
+        workspace_bytes < plx::fwd_workspace_bytes(B, H, L, d))
+        return PARALLAX_ERR_INVALID_ARG;
 
-    const int64_t n_qtiles = ((int64_t)L + plx::kFwdBlockM - 1) / plx::kFwdBlockM;
+    const int bm = plx::fwd_block_rows(d);
+    const int64_t n_qtiles = ((int64_t)L + bm - 1) / bm;
     if ((int64_t)B * H * n_qtiles > INT_MAX)
         return PARALLAX_ERR_UNSUPPORTED;
 
@@ -80,6 +91,7 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
     a.r = static_cast<const uint16_t *>(r);
     a.o = o;
     a.lse = lse;
+    a.vt = static_cast<uint16_t *>(workspace);
     a.q_b = sq.b; a.q_h = sq.h; a.q_l = sq.l;
     a.k_b = sk.b; a.k_h = sk.h; a.k_l = sk.l;
     a.v_b = sv.b; a.v_h = sv.h; a.v_l = sv.l;
@@ -89,6 +101,7 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
     a.H = H;
     a.L = L;
     a.n_qtiles = (int)n_qtiles;
+    a.n_st = (int)(((int64_t)L + plx::kStageKeys - 1) / plx::kStageKeys);
     a.scale_log2 = softmax_scale * kLog2e;
     a.window = window;
     a.n_sink = n_sink;

@@ -17,18 +17,27 @@
 // value products (P~ V and (P~ o S) V) sharing one V operand.
 //
 // Mapping onto CDNA4:
-//   * A workgroup = 4 wavefronts x 16 query rows = 64 rows; two workgroups
-//     share a CU, so every SIMD runs two independent wavefronts and the
-//     hardware overlaps one's exponentials, memory waits and barrier with
-//     the other's matrix-core work.  Each wavefront keeps its Q and R
-//     fragments and its fp32 accumulators in registers (<= 256 per lane).
-//   * Keys stream through LDS in stages of 32 keys with three buffers; the
-//     global loads of a stage are issued two stages ahead through buffer
-//     resources that end at the last valid row, so rows past the sequence
-//     end read as zeros without per-lane branches.  K is stored row-major
-//     (bf16); V is stored transposed and converted to f16, with the keys of
-//     each stage permuted so that one 16-byte LDS read gives each lane the
-//     8 keys the value MFMA needs.
+//   * A workgroup = 8 wavefronts x 16 query rows = 128 rows, one workgroup
+//     per CU, two wavefronts per SIMD.  The wavefronts form two groups of
+//     four (waves 0-3 and 4-7, one of each on every SIMD) that run half a
+//     stage apart ("ping-pong"): while one group issues its matrix-core
+//     work, the other does its exponentials, LDS traffic and global loads,
+//     and a workgroup barrier after every phase swaps the roles.  Each wave
+//     alternates
+//        M phase: score MFMAs of stage t, value MFMAs of stage t-1
+//        V phase: weights of stage t, LDS reads of the K fragments of stage
+//                 t+1 and the V fragments of stage t, its group's half of
+//                 stage t+2 into LDS, global loads of stage t+4.
+//     Every operand of an M phase is in registers when it starts.
+//   * Keys stream through LDS in stages of 32 keys with three buffers; each
+//     group moves half of every stage, two stages ahead of use.  K comes
+//     from the K tensor (bf16, row-major in LDS) through buffer resources
+//     that end at the last valid row, so rows past the sequence end read as
+//     zeros without per-lane branches.  V comes from a workspace image that
+//     a small first kernel writes once per key: float16, transposed, with
+//     the keys of each stage permuted so that one 16-byte LDS read gives
+//     each lane the 8 keys the value MFMA needs.  Moving a stage into LDS
+//     is then 16-byte copies only, with no conversion in the main loop.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_16x16x32_bf16.  In that accumulator layout each lane holds
 //     one query row (4 lanes, l ^ 16 and l ^ 32 apart, share a row), so row
@@ -45,28 +54,32 @@
 //   * Causal, sliding-window and sink masks ("Sliding-window beats linear
 //     attention" review, sec. 1) skip whole stages per workgroup.  Stages
 //     visible to every row of the workgroup run mask-free; the others apply
-//     per-element masks (no branches either way).
+//     per-element masks (selects, a wave-uniform branch around them).
 //   * Workgroups are issued heaviest query tile first; the block index keeps
 //     all tiles of one (batch, head) on one XCD when B*H is a multiple of 8,
 //     so their K/V reuse stays in that XCD's L2.
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace plx {
 namespace {
 
-constexpr int ROWS = 16;              // query rows per wavefront
-constexpr int NWAVES = 4;
-constexpr int BM = ROWS * NWAVES;     // query rows per workgroup
-constexpr int BN = 32;                // keys per stage
-constexpr int NBUF = 3;               // LDS stage buffers
+constexpr int ROWS = 16;                  // query rows per wavefront
+constexpr int NWAVES = 8;                 // two groups of four wavefronts
 constexpr int NTHREADS = 64 * NWAVES;
-static_assert(BM == kFwdBlockM, "host and kernel must agree on the query tile");
+constexpr int GTHREADS = NTHREADS / 2;    // threads per group
+constexpr int BM = ROWS * NWAVES;         // query rows per workgroup
+constexpr int BN = 32;                    // keys per stage
+constexpr int HALF = BN / 2;              // keys of a stage moved by one group
+constexpr int NBUF = 3;                   // LDS stage buffers
 // Softmax offsets, log2 units (see above).
 constexpr float kMargin = 3.0f;
 constexpr float kTauHi = 5.0f;
 
-typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
+static_assert(BM == fwd_block_rows(64) && BM == fwd_block_rows(128),
+              "host and kernel must agree on the query tile");
 
 template <int D>
 struct Cfg {
@@ -79,17 +92,13 @@ struct Cfg {
     static constexpr int V_ELEMS = D * VP;
     static constexpr int KC = D / 32;   // reduction chunks of the score MFMA
     static constexpr int DT = D / 16;   // output tiles of the value MFMA
-    static constexpr int K_LOADS = BN * (D / 8) / NTHREADS;  // 16-byte K loads per thread
-    // Each thread transposes KQ consecutive keys x 8 features of V.
-    static constexpr int KQ = BN * (D / 8) / NTHREADS;
-    static_assert(K_LOADS >= 1 && K_LOADS * NTHREADS == BN * (D / 8), "K stage must split evenly");
-    static_assert(KQ == 1 || KQ == 2, "V transpose handles 1 or 2 keys per thread");
-};
-
-template <int D>
-struct StageRegs {
-    u32x4 k[Cfg<D>::K_LOADS];
-    u32x4 v[Cfg<D>::KQ];
+    // 16-byte chunks in a group's half stage of K (and of V).  At d = 128
+    // every thread of the group moves one K and one V chunk; at d = 64 the
+    // first two waves of the group move K chunks and the other two V chunks.
+    static constexpr int HALF_CHUNKS = HALF * (D / 8);
+    static constexpr bool SPLIT = HALF_CHUNKS < GTHREADS;
+    static_assert(HALF_CHUNKS == GTHREADS || 2 * HALF_CHUNKS == GTHREADS,
+                  "a half stage must split evenly over a group");
 };
 
 // Position of stage key j (0..31) inside the transposed V stage.  The score
@@ -111,117 +120,102 @@ __device__ __forceinline__ float xor32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Exchanges between 16-lane rows done on the VALU (v_permlane16_swap):
+// no LDS instruction, so they never wait behind outstanding LDS reads.
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Reductions over the four lanes that share a query row (l, l^16, l^32, l^48).
-__device__ __forceinline__ float row_max4(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16, 64));
-    return xor32_max(x);
+__device__ __forceinline__ float row_max4(float x) { return xor32_max(xor16_max(x)); }
+
+__device__ __forceinline__ float row_sum4(float x) { return xor32_sum(xor16_sum(x)); }
+
+// Marks x as produced here: code that computes it cannot be moved past this
+// point (neither by IR passes nor by the scheduler), which keeps each
+// ping-pong phase's work inside its phase.
+template <typename T>
+__device__ __forceinline__ void pin(T &x) {
+    asm volatile("" : "+v"(x));
 }
 
-__device__ __forceinline__ float row_sum4(float x) {
-    x = x + __shfl_xor(x, 16, 64);
-    return xor32_sum(x);
+// Workgroup barrier between ping-pong phases; the scheduler may not move
+// any instruction across it.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
-// Per-thread byte offsets of this thread's K and V chunks inside a stage.
+// This thread's share of a half stage: where its 16-byte chunks come from
+// and where they go in LDS.  Group g moves keys 16g .. 16g+15 of K (from the
+// K tensor) and features g*d/2 .. (g+1)*d/2 - 1 of the stage's V^T image
+// (from the workspace, already float16, transposed and permuted).
 template <int D>
-struct StageOffsets {
-    uint32_t k[Cfg<D>::K_LOADS];
-    uint32_t v[Cfg<D>::KQ];
+struct ChunkMap {
+    uint32_t gk;  // K: byte offset from the stage's first row
+    uint32_t gv;  // V^T image: byte offset inside the stage's image
+    int sk;       // element offset of the K chunk in a K stage
+    int sv;       // element offset of the V^T chunk in a V^T stage
 };
 
 template <int D>
-__device__ __forceinline__ StageOffsets<D> stage_offsets(int64_t k_l, int64_t v_l, int tid) {
+__device__ __forceinline__ ChunkMap<D> chunk_map(int64_t k_l, int grp, int gt) {
     using C = Cfg<D>;
-    StageOffsets<D> o;
-#pragma unroll
-    for (int u = 0; u < C::K_LOADS; ++u) {
-        const int c = tid + NTHREADS * u;
-        o.k[u] = (uint32_t)((c / (D / 8)) * k_l * 2 + (c % (D / 8)) * 16);
-    }
-    const int a = tid % (BN / C::KQ);
-    const int cc = tid / (BN / C::KQ);
-#pragma unroll
-    for (int u = 0; u < C::KQ; ++u)
-        o.v[u] = (uint32_t)((C::KQ * a + u) * v_l * 2 + cc * 16);
-    return o;
+    const int c = C::SPLIT ? (gt % C::HALF_CHUNKS) : gt;
+    ChunkMap<D> m;
+    const int kr = HALF * grp + c / (D / 8);   // K: consecutive lanes walk along a row
+    const int col = (c % (D / 8)) * 8;
+    m.gk = (uint32_t)(kr * k_l * 2 + col * 2);
+    m.sk = kr * C::KP + col;
+    const int f = (D / 2) * grp + c / 4;       // V^T: 4 lanes per 32-position row
+    const int q = c % 4;
+    m.gv = (uint32_t)(f * BN * 2 + q * 16);
+    m.sv = f * C::VP + 8 * q;
+    return m;
 }
 
-// Global -> registers for the stage starting at key j0, through buffer
-// resources that end at the last valid row: rows past the sequence end read
-// as zeros and nothing outside the tensors is touched.
+// Chunks of a half stage in flight between global memory and LDS.  At
+// d = 64 only `k` is used (holding a K or a V chunk, by wave).
 template <int D>
-__device__ __forceinline__ void load_stage(StageRegs<D> &t, const uint16_t *kbase,
-                                           const uint16_t *vbase, int64_t k_l, int64_t v_l,
-                                           int j0, int L, const StageOffsets<D> &off) {
-    using C = Cfg<D>;
-    j0 = __builtin_amdgcn_readfirstlane(j0);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)j0 * k_l, rows_bytes(j0, L, k_l, D));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)j0 * v_l, rows_bytes(j0, L, v_l, D));
-#pragma unroll
-    for (int u = 0; u < C::K_LOADS; ++u)
-        t.k[u] = bufld16(rk, off.k[u]);
-#pragma unroll
-    for (int u = 0; u < C::KQ; ++u)
-        t.v[u] = bufld16(rv, off.v[u]);
-}
+struct Chunks {
+    u32x4 k, v;
+};
 
-// Registers -> LDS: K row-major; V converted to f16 and transposed.
-template <int D>
-__device__ __forceinline__ void store_stage(const StageRegs<D> &t, uint16_t *sk, uint16_t *sv,
-                                            int tid) {
-    using C = Cfg<D>;
-#pragma unroll
-    for (int u = 0; u < C::K_LOADS; ++u) {
-        const int c = tid + NTHREADS * u;
-        const int row = c / (D / 8);
-        const int col = (c % (D / 8)) * 8;
-        *reinterpret_cast<u32x4 *>(sk + row * C::KP + col) = t.k[u];
-    }
-    const int a = tid % (BN / C::KQ);
-    const int cc = tid / (BN / C::KQ);
-    const int pos = vt_pos(C::KQ * a);
-    if constexpr (C::KQ == 2) {
-        // keys 2a, 2a+1 sit next to each other in the permuted order
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t w0 = t.v[0][e >> 1], w1 = t.v[1][e >> 1];
-            const float f0 = (e & 1) ? bf16_hi(w0) : bf16_lo(w0);
-            const float f1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
-            *reinterpret_cast<uint32_t *>(sv + (8 * cc + e) * C::VP + pos) =
-                __builtin_bit_cast(uint32_t, cvt_f16x2(f0, f1));
-        }
-    } else {
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const uint32_t w = t.v[0][e2];
-            const f16x2 hh = cvt_f16x2(bf16_lo(w), bf16_hi(w));
-            const uint32_t bits = __builtin_bit_cast(uint32_t, hh);
-            sv[(8 * cc + 2 * e2) * C::VP + pos] = (uint16_t)(bits & 0xffffu);
-            sv[(8 * cc + 2 * e2 + 1) * C::VP + pos] = (uint16_t)(bits >> 16);
-        }
-    }
-}
-
-// Visibility class of the 32-key stage starting at j0 for rows [r0, r1]:
-// 0 = no visible pair, 1 = every pair visible, 2 = needs a per-element mask.
-__device__ __forceinline__ int classify(int j0, int r0, int r1, int L, int window, int n_sink) {
-    const int j1 = j0 + BN - 1;
-    if (r1 < r0 || j0 > r1 || j0 >= L)
-        return 0;
-    if (window > 0 && j1 < r0 - window + 1 && j0 >= n_sink)
-        return 0;
-    if (j1 <= r0 && j1 < L && (window <= 0 || r1 - j0 < window || j1 < n_sink))
-        return 1;
-    return 2;
-}
+// Floor and ceiling of a / BN for any sign of a.
+__device__ __forceinline__ int floor_div_bn(int a) { return a >= 0 ? a / BN : -((-a + BN - 1) / BN); }
+__device__ __forceinline__ int ceil_div_bn(int a) { return -floor_div_bn(-a); }
 
 template <int D>
 struct Ctx {
     bf16x8 qf[Cfg<D>::KC], rf[Cfg<D>::KC];
     f32x4 accA[Cfg<D>::DT], accC[Cfg<D>::DT];
-    float m_ref;  // this row's softmax offset (scaled log2 units)
-    float xmax;   // running max of the row's raw scores
+    float m_ref;  // this row's softmax offset (scaled log2 units), -inf until set
+    float msub;   // m_ref, or 0 while it is unset (all scores so far are -inf)
+    float xlane;  // running max of this lane's raw scores of the row
     float ell, ssum;
+};
+
+// K fragments of one stage (A operand of the score MFMAs): key 16 kt + l16,
+// features 32 kc + 8G .. +7.
+template <int D>
+struct KFrags {
+    bf16x8 f[2][Cfg<D>::KC];
+};
+
+// V^T fragments of one stage (A operand of the value MFMAs): V^T row
+// 16 dt + l16, reduction positions 8G .. 8G+7.
+template <int D>
+struct VFrags {
+    f16x8 f[Cfg<D>::DT];
 };
 
 // Scores of one stage: S^T tiles (16 keys x 16 rows) for keys 0-15 and 16-31.
@@ -229,31 +223,59 @@ struct Scores {
     f32x4 q[2], r[2];
 };
 
-// S^T = K Q^T and R K^T for one stage: 2 key tiles x KC chunks x 2 MFMAs,
-// each K fragment shared by the Q and the R product.
+// f16 weights of one stage in the value MFMA's B-operand order: p~ and p~ s.
+struct Weights {
+    f16x8 p, w;
+};
+
 template <int D>
-__device__ __forceinline__ void score_stage(const Ctx<D> &cx, const uint16_t *sk, int l16, int G,
-                                            Scores &s) {
-    using C = Cfg<D>;
+__device__ __forceinline__ void read_kfrags(KFrags<D> &kf, const uint16_t *sk, int l16, int G) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int kc = 0; kc < Cfg<D>::KC; ++kc)
+            kf.f[kt][kc] = *reinterpret_cast<const bf16x8 *>(sk + (16 * kt + l16) * Cfg<D>::KP +
+                                                             32 * kc + 8 * G);
+}
+
+template <int D>
+__device__ __forceinline__ void read_vfrags(VFrags<D> &vf, const uint16_t *sv, int l16, int G) {
+#pragma unroll
+    for (int dt = 0; dt < Cfg<D>::DT; ++dt)
+        vf.f[dt] = *reinterpret_cast<const f16x8 *>(sv + (16 * dt + l16) * Cfg<D>::VP + 8 * G);
+}
+
+// S^T = K Q^T and R K^T for one stage: 2 key tiles x KC chunks x 2 MFMAs,
+// four independent accumulation chains, each K fragment shared by the Q and
+// the R product.
+template <int D>
+__device__ __forceinline__ void score_mfmas(const Ctx<D> &cx, const KFrags<D> &kf, Scores &s) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-        bf16x8 kf[C::KC];
+        s.q[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[kt][0], cx.qf[0], z, 0, 0, 0);
+        s.r[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[kt][0], cx.rf[0], z, 0, 0, 0);
+    }
 #pragma unroll
-        for (int kc = 0; kc < C::KC; ++kc)
-            kf[kc] = *reinterpret_cast<const bf16x8 *>(sk + (16 * kt + l16) * C::KP + 32 * kc + 8 * G);
-        f32x4 zq = {0.f, 0.f, 0.f, 0.f}, zr = {0.f, 0.f, 0.f, 0.f};
-        s.q[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], cx.qf[0], zq, 0, 0, 0);
-        s.r[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], cx.rf[0], zr, 0, 0, 0);
+    for (int kc = 1; kc < Cfg<D>::KC; ++kc)
 #pragma unroll
-        for (int kc = 1; kc < C::KC; ++kc) {
-            s.q[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc], cx.qf[kc], s.q[kt], 0, 0, 0);
-            s.r[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc], cx.rf[kc], s.r[kt], 0, 0, 0);
+        for (int kt = 0; kt < 2; ++kt) {
+            s.q[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[kt][kc], cx.qf[kc], s.q[kt], 0, 0, 0);
+            s.r[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[kt][kc], cx.rf[kc], s.r[kt], 0, 0, 0);
         }
+}
+
+// O^T += V^T P~^T and V^T (P~ o S)^T for one stage.
+template <int D>
+__device__ __forceinline__ void value_mfmas(Ctx<D> &cx, const VFrags<D> &vf, const Weights &pw) {
+#pragma unroll
+    for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
+        cx.accA[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], pw.p, cx.accA[dt], 0, 0, 0);
+        cx.accC[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], pw.w, cx.accC[dt], 0, 0, 0);
     }
 }
 
-// Per-element mask of a stage: invisible scores become -inf (bitwise logic
-// and a select, no branches).
+// Per-element mask of a stage: invisible scores become -inf.
 __device__ __forceinline__ void mask_scores(Scores &s, int j0, int row, int G, int L, int window,
                                             int n_sink) {
     const int lim = min(row, L - 1);                            // causal and sequence end
@@ -269,64 +291,95 @@ __device__ __forceinline__ void mask_scores(Scores &s, int j0, int row, int G, i
     }
 }
 
-// Weights of one stage: track the row max and fix the row's offset at its
-// first visible stage (per-lane selects; the accumulators are never
-// touched), form the f16 weights in the value MFMA's B-operand order, add
-// them to ell and S, and run the value MFMAs on the stage's V fragments.
+// Sets the softmax offset of rows that have none yet from this stage's row
+// max (+ kMargin); rows whose scores so far are all -inf stay unset.
+// Returns whether every row of the wavefront now has its offset.
 template <int D>
-struct VFrags {
-    f16x8 f[Cfg<D>::DT];
-};
-
-// V^T fragments of one stage (A operand of the value MFMAs): V^T row
-// 16 dt + l16, reduction positions 8G .. 8G+7.
-template <int D>
-__device__ __forceinline__ void read_vfrags(VFrags<D> &vf, const uint16_t *sv, int l16, int G) {
-#pragma unroll
-    for (int dt = 0; dt < Cfg<D>::DT; ++dt)
-        vf.f[dt] = *reinterpret_cast<const f16x8 *>(sv + (16 * dt + l16) * Cfg<D>::VP + 8 * G);
-}
-
-template <int D>
-__device__ __forceinline__ void value_stage(Ctx<D> &cx, const Scores &s, const VFrags<D> &vf,
-                                            float c) {
-    using C = Cfg<D>;
-
+__device__ __forceinline__ bool init_offsets(Ctx<D> &cx, const Scores &s, float c) {
     float mt = fmaxf(fmaxf(fmaxf(s.q[0][0], s.q[0][1]), s.q[0][2]),
                      fmaxf(fmaxf(s.q[0][3], s.q[1][0]), s.q[1][1]));
     mt = fmaxf(fmaxf(mt, s.q[1][2]), s.q[1][3]);
     mt = row_max4(mt);
-    cx.xmax = fmaxf(cx.xmax, mt);
     cx.m_ref = (cx.m_ref == kNegInf) ? fmaf(mt, c, kMargin) : cx.m_ref;
-    const float msub = (cx.m_ref == kNegInf) ? 0.f : cx.m_ref;
+    cx.msub = (cx.m_ref == kNegInf) ? 0.f : cx.m_ref;
+    return __builtin_amdgcn_ballot_w64(cx.m_ref == kNegInf) == 0;
+}
 
+// Weights of one stage: the per-lane running max of the raw scores, the f16
+// weights in the value MFMA's B-operand order, and their sums ell and S.
+template <int D>
+__device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights &pw, float c) {
+    cx.xlane = fmaxf(fmaxf(fmaxf(cx.xlane, s.q[0][0]), s.q[0][1]),
+                     fmaxf(fmaxf(s.q[0][2], s.q[0][3]), s.q[1][0]));
+    cx.xlane = fmaxf(fmaxf(fmaxf(cx.xlane, s.q[1][1]), s.q[1][2]), s.q[1][3]);
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    f16x8 pf, wf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
             const int e = 2 * e2;
-            const float p0 = exp2_fast(fmaf(s.q[kt][e], c, -msub));
-            const float p1 = exp2_fast(fmaf(s.q[kt][e + 1], c, -msub));
+            const float p0 = exp2_fast(fmaf(s.q[kt][e], c, -cx.msub));
+            const float p1 = exp2_fast(fmaf(s.q[kt][e + 1], c, -cx.msub));
             const f16x2 ph = cvt_f16x2(p0, p1);
             const f16x2 wh = cvt_f16x2(p0 * s.r[kt][e], p1 * s.r[kt][e + 1]);
             cx.ell = __builtin_amdgcn_fdot2(ph, ones, cx.ell, false);
             cx.ssum = __builtin_amdgcn_fdot2(wh, ones, cx.ssum, false);
-            pf[4 * kt + e] = ph[0];
-            pf[4 * kt + e + 1] = ph[1];
-            wf[4 * kt + e] = wh[0];
-            wf[4 * kt + e + 1] = wh[1];
+            pw.p[4 * kt + e] = ph[0];
+            pw.p[4 * kt + e + 1] = ph[1];
+            pw.w[4 * kt + e] = wh[0];
+            pw.w[4 * kt + e + 1] = wh[1];
         }
-    }
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-        cx.accA[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], pf, cx.accA[dt], 0, 0, 0);
-        cx.accC[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], wf, cx.accC[dt], 0, 0, 0);
     }
 }
 
+// Workspace image of the values: one workgroup per (32-key stage, batch *
+// head).  Keys 32s .. 32s+31 (zeros past L) are converted to float16 and
+// transposed through LDS into [d features][32 positions], position
+// vt_pos(key), so that the prefill moves each stage into LDS with plain
+// 16-byte copies.  The conversion and transposition happen once per key
+// instead of once per query tile.
 template <int D>
+__global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
+    constexpr int TP = BN + 8;  // LDS row pitch (halves): 16-byte aligned rows
+    __shared__ __attribute__((aligned(16))) uint16_t T[D * TP];
+    const int s = blockIdx.x;
+    const int j0 = s * BN;
+    for (int bh = blockIdx.y; bh < a.B * a.H; bh += gridDim.y) {
+        const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+        const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h;
+        for (int c = threadIdx.x; c < BN * (D / 8); c += blockDim.x) {
+            const int key = c / (D / 8);
+            const int col = (c % (D / 8)) * 8;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (j0 + key < a.L)
+                x = ldg16(vb + (int64_t)(j0 + key) * a.v_l + col);
+            const int pos = vt_pos(key);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const uint32_t w = x[e2];
+                const uint32_t bits =
+                    __builtin_bit_cast(uint32_t, cvt_f16x2(bf16_lo(w), bf16_hi(w)));
+                T[(col + 2 * e2) * TP + pos] = (uint16_t)(bits & 0xffffu);
+                T[(col + 2 * e2 + 1) * TP + pos] = (uint16_t)(bits >> 16);
+            }
+        }
+        __syncthreads();
+        uint16_t *dst = a.vt + ((int64_t)bh * a.n_st + s) * (D * BN);
+        for (int c = threadIdx.x; c < D * (BN / 8); c += blockDim.x) {
+            const int f = c / (BN / 8);
+            const int q = c % (BN / 8);
+            *reinterpret_cast<u32x4 *>(dst + f * BN + 8 * q) =
+                *reinterpret_cast<const u32x4 *>(&T[f * TP + 8 * q]);
+        }
+        __syncthreads();
+    }
+}
+
+// WHOLE: the K slice and the V^T images of one (batch, head) each span
+// fewer than 2^31 bytes, so one buffer resource per tensor covers every
+// stage and a stage needs only an offset; otherwise every stage builds its
+// own resources.
+template <int D, bool WHOLE>
 __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][C::K_ELEMS];
@@ -334,7 +387,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;            // ping-pong group
+    const int gt = tid & (GTHREADS - 1);  // thread index inside the group
     const int l16 = lane & 15;
     const int G = lane >> 4;
 
@@ -354,7 +409,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     const uint16_t *qb = a.q + (int64_t)b * a.q_b + (int64_t)h * a.q_h;
     const uint16_t *rb = a.r + (int64_t)b * a.r_b + (int64_t)h * a.r_h;
     const uint16_t *kb = a.k + (int64_t)b * a.k_b + (int64_t)h * a.k_h;
-    const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h;
+    const uint16_t *vtb = a.vt + (int64_t)bh * a.n_st * (D * BN);  // this slice's V^T images
 
     Ctx<D> cx;
     {
@@ -372,7 +427,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             cx.rf[kc] = __builtin_bit_cast(bf16x8, bufld16(rr, roff + col));
         }
         cx.m_ref = kNegInf;
-        cx.xmax = kNegInf;
+        cx.msub = 0.f;
+        cx.xlane = kNegInf;
     }
 
     // Stages with at least one visible pair for rows [i0, i1]: the sink
@@ -385,51 +441,133 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         n_ss = min((n_sink + BN - 1) / BN, st_lo);
     }
     const int n = n_ss + (st_hi - st_lo + 1);
-    auto stage_j0 = [&](int t) { return (t < n_ss ? t : st_lo + (t - n_ss)) * BN; };
+    // Key offset of stage u of that list.
+    auto list_j0 = [&](int u) { return (u < n_ss ? u : st_lo + (u - n_ss)) * BN; };
 
-    // Stages fully visible to every row of the workgroup: [f_lo, f_hi).
-    // Causal stages before the diagonal (with a window: those well inside
-    // it) are full; sink stages, window edges and the diagonal are not.
+    // Stages of the window/causal run that every row of the workgroup sees
+    // in full: [f_lo, f_hi).  A stage starting at key j0 qualifies when its
+    // last key is causal for the first row and inside the sequence
+    // (j0 <= jmax) and, with a window, its first key is inside the last
+    // row's window (j0 >= jmin).  Sink stages and stages that are full only
+    // through the sinks are left to the masked path, which is exact for
+    // every stage.
     int f_lo = n, f_hi = n;
-    for (int t = 0; t < n; ++t) {
-        if (classify(stage_j0(t), i0, i1, L, window, n_sink) == 1) {
-            f_lo = t;
-            break;
+    {
+        const int jmax = min(i0 - (BN - 1), L - BN);
+        const int jmin = window > 0 ? i1 - window + 1 : 0;
+        const int lo = n_ss + max(0, ceil_div_bn(jmin) - st_lo);
+        const int hi = min(n, n_ss + floor_div_bn(jmax) - st_lo + 1);
+        if (jmax >= 0 && lo < hi) {
+            f_lo = lo;
+            f_hi = hi;
         }
     }
-    if (f_lo < n) {
-        f_hi = f_lo + 1;
-        while (f_hi < n && classify(stage_j0(f_hi), i0, i1, L, window, n_sink) == 1)
-            ++f_hi;
-    }
-
-    // Global prefetches past the last stage reload the last stage into a
-    // buffer nobody reads again, which keeps the loop bodies branch-free.
-    const StageOffsets<D> soff = stage_offsets<D>(a.k_l, a.v_l, tid);
-    auto fetch = [&](StageRegs<D> &p, int t) __attribute__((always_inline)) {
-        load_stage<D>(p, kb, vb, a.k_l, a.v_l, stage_j0(min(t, n - 1)), L, soff);
+    // Processing order: the full stages first (so that the first stage
+    // fixes every row's softmax offset from 32 visible keys and the main
+    // loop needs neither masks nor offset logic), then the masked ones.
+    const int n_full = f_hi - f_lo;
+    auto stage_j0 = [&](int t) {
+        const int m = t - n_full;
+        return list_j0(t < n_full ? f_lo + t : (m < f_lo ? m : f_hi + (m - f_lo)));
     };
 
-    // Stage t: prefetch stage t+3 into p_ld, scores, (mask), weights and
-    // value MFMAs of stage t from LDS buffer t%3, store stage t+2 (p_st) into
-    // buffer (t+2)%3, barrier.  Between stages p0 holds stage t+2.
-    StageRegs<D> p0, p1;
-    Scores sc;
+    // Global <-> LDS movement of this group's half of a stage.  Loads past
+    // the last stage reload the last stage (into a buffer nobody reads
+    // again), which keeps the phases branch-free.
+    const ChunkMap<D> cm = chunk_map<D>(a.k_l, grp, gt);
+    const bool k_role = !C::SPLIT || (wave & 2) == 0;  // d = 64: waves moving K chunks
+    constexpr uint32_t kImage = D * BN * 2;           // bytes of one stage's V^T image
+    const __amdgpu_buffer_rsrc_t rk_all = make_rsrc(kb, WHOLE ? rows_bytes(0, L, a.k_l, D) : 0u);
+    const __amdgpu_buffer_rsrc_t rv_all = make_rsrc(vtb, WHOLE ? (uint32_t)a.n_st * kImage : 0u);
+    auto fetch = [&](Chunks<D> &p, int t) __attribute__((always_inline)) {
+        const int j0 = __builtin_amdgcn_readfirstlane(stage_j0(min(t, n - 1)));
+        const int si = j0 / BN;
+        if constexpr (WHOLE) {
+            // Offsets stay below 2^32: the K slice is < 2^31 bytes and a
+            // stage reaches at most 31 rows (< 2^30 bytes) past its end; the
+            // V^T images of the slice span < 2^31 bytes.
+            const uint32_t ko = (uint32_t)j0 * (uint32_t)a.k_l * 2u;
+            const uint32_t vo = (uint32_t)si * kImage;
+            if constexpr (!C::SPLIT) {
+                p.k = bufld16(rk_all, cm.gk + ko);
+                p.v = bufld16(rv_all, cm.gv + vo);
+            } else {
+                p.k = bufld16(k_role ? rk_all : rv_all, k_role ? cm.gk + ko : cm.gv + vo);
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t rk =
+                make_rsrc(kb + (int64_t)j0 * a.k_l, rows_bytes(j0, L, a.k_l, D));
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vtb + (int64_t)si * (D * BN), kImage);
+            if constexpr (!C::SPLIT) {
+                p.k = bufld16(rk, cm.gk);
+                p.v = bufld16(rv, cm.gv);
+            } else {
+                p.k = bufld16(k_role ? rk : rv, k_role ? cm.gk : cm.gv);
+            }
+        }
+    };
+    auto store = [&](const Chunks<D> &p, int buf) __attribute__((always_inline)) {
+        if constexpr (!C::SPLIT) {
+            *reinterpret_cast<u32x4 *>(&sK[buf][cm.sk]) = p.k;
+            *reinterpret_cast<u32x4 *>(&sV[buf][cm.sv]) = p.v;
+        } else {
+            if (k_role)
+                *reinterpret_cast<u32x4 *>(&sK[buf][cm.sk]) = p.k;
+            else
+                *reinterpret_cast<u32x4 *>(&sV[buf][cm.sv]) = p.k;
+        }
+    };
+
+    KFrags<D> kf;
     VFrags<D> vf;
-    auto stage = [&](int t, bool masked, StageRegs<D> &p_st, StageRegs<D> &p_ld)
-        __attribute__((always_inline)) {
-        const int buf = t % NBUF;
-        fetch(p_ld, t + 3);
-        // V fragments first: they arrive while the score MFMAs run.
-        read_vfrags<D>(vf, sV[buf], l16, G);
-        score_stage<D>(cx, sK[buf], l16, G, sc);
-        if (masked)
-            mask_scores(sc, stage_j0(t), row, G, L, window, n_sink);
-        value_stage<D>(cx, sc, vf, c);
-        const int bst = (t + 2) % NBUF;
-        store_stage<D>(p_st, sK[bst], sV[bst], tid);
-        __syncthreads();
+    Scores sc;
+    Weights pw;
+    Chunks<D> p0, p1;  // stage s is in flight in p(s & 1)
+
+    // V phase that follows the scores of stage t: weights of stage t, K
+    // fragments of stage t+1, V fragments of stage t, this group's half of
+    // stage t+2 into LDS, loads of stage t+4.  It has no branch, so the
+    // scheduler can interleave all of it.
+    auto vphase = [&](int t, Chunks<D> &p) __attribute__((always_inline)) {
+        read_kfrags<D>(kf, sK[(t + 1) % NBUF], l16, G);
+        read_vfrags<D>(vf, sV[t % NBUF], l16, G);
+        weights<D>(cx, sc, pw, c);
+        pin(pw.p);
+        pin(pw.w);
+        pin(cx.ell);
+        pin(cx.ssum);
+        store(p, (t + 2) % NBUF);
+        fetch(p, t + 4);
     };
+    // End of the M phase, when the score MFMAs are done.  Masked stages: the
+    // mask of stage t's scores and the softmax offsets of rows that still
+    // have none.  Full stages come first and stage 0 sets every offset, so
+    // the other full stages need neither.
+    bool offsets_set = false;  // wave-uniform
+    auto finish_scores = [&](auto masked, int t) __attribute__((always_inline)) {
+        if constexpr (decltype(masked)::value) {
+            mask_scores(sc, stage_j0(t), row, G, L, window, n_sink);
+            if (!offsets_set)
+                offsets_set = init_offsets<D>(cx, sc, c);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            pin(sc.q[kt]);
+            pin(sc.r[kt]);
+        }
+        pin(cx.msub);
+    };
+    // One step: M phase of stage t, barrier, V phase of stage t, barrier.
+    auto step = [&](auto masked, int t, Chunks<D> &p) __attribute__((always_inline)) {
+        score_mfmas<D>(cx, kf, sc);
+        value_mfmas<D>(cx, vf, pw);
+        finish_scores(masked, t);
+        phase_barrier();
+        vphase(t, p);
+        phase_barrier();
+    };
+    const std::integral_constant<bool, true> kMasked;
+    const std::integral_constant<bool, false> kFull;
 
     // Pass 0 uses offsets fixed at each row's first visible stage; if any
     // row's scores later rose more than kTauHi above its offset, pass 1
@@ -443,32 +581,60 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         cx.ell = 0.f;
         cx.ssum = 0.f;
 
+        // Stages 0 and 1 into LDS, 2 and 3 in flight.
         fetch(p0, 0);
-        store_stage<D>(p0, sK[0], sV[0], tid);
-        fetch(p0, 1);
-        store_stage<D>(p0, sK[1], sV[1], tid);
+        fetch(p1, 1);
+        store(p0, 0);
         fetch(p0, 2);
+        store(p1, 1);
+        fetch(p1, 3);
         __syncthreads();
+        read_kfrags<D>(kf, sK[0], l16, G);
+        // The second group starts one phase later.
+        if (grp == 1)
+            phase_barrier();
+        // Step 0 has no value MFMAs; it sets the offsets of all rows that
+        // see any of its keys (all rows when it is a full stage).
+        score_mfmas<D>(cx, kf, sc);
+        if (n_full == 0)
+            mask_scores(sc, stage_j0(0), row, G, L, window, n_sink);
+        if (!offsets_set)
+            offsets_set = init_offsets<D>(cx, sc, c);
+        finish_scores(kFull, 0);
+        phase_barrier();
+        vphase(0, p0);
+        phase_barrier();
+        // Step t moves stage t+2, in flight in p((t + 2) & 1) = p(t & 1).
+        int t = 1;
+        const int t_mask = max(1, n_full);
+        for (; t + 1 < t_mask; t += 2) {
+            step(kFull, t, p1);
+            step(kFull, t + 1, p0);
+        }
+        if (t < t_mask)
+            step(kFull, t++, p1);
+        if (t < n && (t & 1) == 0)
+            step(kMasked, t++, p0);
+        for (; t + 1 < n; t += 2) {
+            step(kMasked, t, p1);
+            step(kMasked, t + 1, p0);
+        }
+        if (t < n)
+            step(kMasked, t, p1);
+        // Value MFMAs of the last stage; the first group catches up with the
+        // second group's extra barrier.
+        value_mfmas<D>(cx, vf, pw);
+        if (grp == 0)
+            phase_barrier();
 
-        int t = 0;
-        for (; t < f_lo; ++t) {
-            stage(t, true, p0, p1);
-            p0 = p1;
-        }
-        for (; t + 1 < f_hi; t += 2) {
-            stage(t, false, p0, p1);
-            stage(t + 1, false, p1, p0);
-        }
-        for (; t < n; ++t) {
-            stage(t, t >= f_hi, p0, p1);
-            p0 = p1;
-        }
-
-        const bool overflow = pass == 0 && cx.xmax * c > cx.m_ref + kTauHi;
+        const float xmax = row_max4(cx.xlane);
+        const bool overflow = pass == 0 && xmax * c > cx.m_ref + kTauHi;
         if (!__syncthreads_or(overflow))
             break;
         // Exact offsets for the recomputation: each row's true max.
-        cx.m_ref = cx.xmax * c;
+        cx.m_ref = xmax * c;
+        cx.msub = cx.m_ref == kNegInf ? 0.f : cx.m_ref;
+        offsets_set = true;
     }
 
     // Epilogue: combine the partial sums of the four lanes of each row.
@@ -491,14 +657,26 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     }
 }
 
+// Bytes from the first element of a [L, d] slice with row stride ld
+// (2-byte elements) through its last element.
+int64_t slice_bytes(int64_t L, int64_t ld, int d) { return (L - 1) * ld * 2 + (int64_t)d * 2; }
+
 template <int D>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.B * a.H * a.n_qtiles));
-    const dim3 block(NTHREADS);
     FwdArgs args = a;
     void *params[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&parallax_fwd_kernel<D>), grid, block,
-                           params, 0, stream);
+    const dim3 pgrid((unsigned)a.n_st, (unsigned)min(a.B * a.H, 65535));
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&parallax_vprep_kernel<D>),
+                                   pgrid, dim3(256), params, 0, stream);
+    if (e != hipSuccess)
+        return e;
+    const dim3 grid((unsigned)(a.B * a.H * a.n_qtiles));
+    const dim3 block(NTHREADS);
+    const bool whole = slice_bytes(a.L, a.k_l, D) <= INT32_MAX &&
+                       (int64_t)a.n_st * D * BN * 2 <= INT32_MAX;
+    const void *fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true>)
+                           : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false>);
+    return hipLaunchKernel(fn, grid, block, params, 0, stream);
 }
 
 }  // namespace

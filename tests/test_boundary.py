@@ -51,9 +51,35 @@ def test_status_strings(lib):
 
 def fwd(lib, q=A16, k=A16, v=A16, r=A16, o=A16, lse=A16, B=1, H=2, L=64, d=64,
         sq=CONTIG, sk=CONTIG, sv=CONTIG, sr=CONTIG, so=CONTIG, scale=0.125, window=0,
-        n_sink=0):
+        n_sink=0, ws=A16, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
     return lib.parallax_attn_fwd(q, k, v, r, o, lse, B, H, L, d, sq, sk, sv, sr, so, scale,
-                                 window, n_sink, None)
+                                 window, n_sink, ws, ws_bytes, None)
+
+
+def expected_workspace(B, H, L, d):
+    """float16 values of every 32-key stage: B*H*ceil(L/32)*32*d*2 bytes."""
+    return B * H * (-(-L // 32)) * 32 * d * 2
+
+
+@pytest.mark.parametrize("B,H,L,d", [(1, 1, 1, 64), (2, 3, 32, 128), (2, 16, 8192, 128),
+                                     (4, 16, 2048, 64), (1, 2, 33, 64), (3, 1, 100, 128)])
+def test_workspace_size(lib, B, H, L, d):
+    assert binding.parallax_attn_fwd_workspace_size(B, H, L, d) == expected_workspace(B, H, L, d)
+
+
+@pytest.mark.parametrize("B,H,L,d", [(0, 1, 64, 64), (1, 0, 64, 64), (1, 1, 0, 128),
+                                     (-1, 1, 64, 64), (1, 1, -2, 64), (1, 1, 64, 96)])
+def test_workspace_size_of_empty_or_invalid_is_zero(lib, B, H, L, d):
+    assert binding.parallax_attn_fwd_workspace_size(B, H, L, d) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(ws=None), dict(ws=A16 + 8),
+                                dict(ws_bytes=expected_workspace(1, 2, 64, 64) - 1),
+                                dict(ws_bytes=0)])
+def test_fwd_rejects_bad_workspace(lib, kw):
+    assert fwd(lib, **kw) == INVALID
 
 
 def dec(lib, q=A16, r=A16, k=A16, v=A16, seqlens=None, o=A16, lse=A16, B=2, H=2, Lmax=64,
@@ -95,7 +121,8 @@ def test_fwd_rejects(lib, kw, status):
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(L=0),
-                                dict(B=0, q=None, k=None, v=None, r=None, o=None, lse=None)])
+                                dict(B=0, q=None, k=None, v=None, r=None, o=None, lse=None),
+                                dict(L=0, ws=None, ws_bytes=0)])
 def test_fwd_empty_problem_is_a_no_op(lib, kw):
     assert fwd(lib, **kw) == OK
 
