@@ -139,12 +139,14 @@ __device__ __forceinline__ float row_max4(float x) { return xor32_max(xor16_max(
 
 __device__ __forceinline__ float row_sum4(float x) { return xor32_sum(xor16_sum(x)); }
 
-// Marks x as produced here: code that computes it cannot be moved past this
+// Marks x as needed here: code that computes it cannot be moved past this
 // point (neither by IR passes nor by the scheduler), which keeps each
-// ping-pong phase's work inside its phase.
+// ping-pong phase's work inside its phase.  The statement only reads x (it
+// emits nothing), so the compiler still sees the real producer of x, for
+// instance an MFMA, and keeps the wait states later readers need.
 template <typename T>
-__device__ __forceinline__ void pin(T &x) {
-    asm volatile("" : "+v"(x));
+__device__ __forceinline__ void pin(const T &x) {
+    asm volatile("" ::"v"(x));
 }
 
 // Workgroup barrier between ping-pong phases; the scheduler may not move
@@ -528,15 +530,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // fragments of stage t+1, V fragments of stage t, this group's half of
     // stage t+2 into LDS, loads of stage t+4.  It has no branch, so the
     // scheduler can interleave all of it.
-    auto vphase = [&](int t, Chunks<D> &p) __attribute__((always_inline)) {
-        read_kfrags<D>(kf, sK[(t + 1) % NBUF], l16, G);
-        read_vfrags<D>(vf, sV[t % NBUF], l16, G);
+    // b0 = t % NBUF, a compile-time constant in the unrolled main loop (the
+    // buffer offsets then fold into the LDS instructions' offset fields).
+    auto vphase = [&](auto b0, int t, Chunks<D> &p) __attribute__((always_inline)) {
+        // Fragment reads first: their LDS latency is the longest chain of
+        // the phase (measured faster than interleaving them with the VALU).
+        read_kfrags<D>(kf, sK[(b0 + 1) % NBUF], l16, G);
+        read_vfrags<D>(vf, sV[b0 % NBUF], l16, G);
+        __builtin_amdgcn_sched_barrier(0);
         weights<D>(cx, sc, pw, c);
         pin(pw.p);
         pin(pw.w);
         pin(cx.ell);
         pin(cx.ssum);
-        store(p, (t + 2) % NBUF);
+        store(p, (b0 + 2) % NBUF);
         fetch(p, t + 4);
     };
     // End of the M phase, when the score MFMAs are done.  Masked stages: the
@@ -558,16 +565,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         pin(cx.msub);
     };
     // One step: M phase of stage t, barrier, V phase of stage t, barrier.
-    auto step = [&](auto masked, int t, Chunks<D> &p) __attribute__((always_inline)) {
+    auto step = [&](auto masked, auto b0, int t, Chunks<D> &p) __attribute__((always_inline)) {
         score_mfmas<D>(cx, kf, sc);
         value_mfmas<D>(cx, vf, pw);
         finish_scores(masked, t);
         phase_barrier();
-        vphase(t, p);
+        vphase(b0, t, p);
         phase_barrier();
     };
     const std::integral_constant<bool, true> kMasked;
     const std::integral_constant<bool, false> kFull;
+    const std::integral_constant<int, 0> kB0;
+    const std::integral_constant<int, 1> kB1;
+    const std::integral_constant<int, 2> kB2;
 
     // Pass 0 uses offsets fixed at each row's first visible stage; if any
     // row's scores later rose more than kTauHi above its offset, pass 1
@@ -602,25 +612,39 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             offsets_set = init_offsets<D>(cx, sc, c);
         finish_scores(kFull, 0);
         phase_barrier();
-        vphase(0, p0);
+        vphase(kB0, 0, p0);
         phase_barrier();
-        // Step t moves stage t+2, in flight in p((t + 2) & 1) = p(t & 1).
+        // Step t moves stage t+2, in flight in p((t + 2) & 1) = p(t & 1),
+        // and uses LDS buffers t % 3 .. (t + 2) % 3.  The main loop runs six
+        // steps per iteration (t = 1 mod 6), so both are fixed per step.
         int t = 1;
         const int t_mask = max(1, n_full);
-        for (; t + 1 < t_mask; t += 2) {
-            step(kFull, t, p1);
-            step(kFull, t + 1, p0);
+        for (; t + 5 < t_mask; t += 6) {
+            step(kFull, kB1, t, p1);
+            step(kFull, kB2, t + 1, p0);
+            step(kFull, kB0, t + 2, p1);
+            step(kFull, kB1, t + 3, p0);
+            step(kFull, kB2, t + 4, p1);
+            step(kFull, kB0, t + 5, p0);
         }
-        if (t < t_mask)
-            step(kFull, t++, p1);
-        if (t < n && (t & 1) == 0)
-            step(kMasked, t++, p0);
+        for (; t + 1 < t_mask; t += 2) {
+            step(kFull, t % NBUF, t, p1);
+            step(kFull, (t + 1) % NBUF, t + 1, p0);
+        }
+        if (t < t_mask) {
+            step(kFull, t % NBUF, t, p1);
+            ++t;
+        }
+        if (t < n && (t & 1) == 0) {
+            step(kMasked, t % NBUF, t, p0);
+            ++t;
+        }
         for (; t + 1 < n; t += 2) {
-            step(kMasked, t, p1);
-            step(kMasked, t + 1, p0);
+            step(kMasked, t % NBUF, t, p1);
+            step(kMasked, (t + 1) % NBUF, t + 1, p0);
         }
         if (t < n)
-            step(kMasked, t, p1);
+            step(kMasked, t % NBUF, t, p1);
         // Value MFMAs of the last stage; the first group catches up with the
         // second group's extra barrier.
         value_mfmas<D>(cx, vf, pw);
