@@ -21,23 +21,28 @@
 //     per CU, two wavefronts per SIMD.  The wavefronts form two groups of
 //     four (waves 0-3 and 4-7, one of each on every SIMD) that run half a
 //     stage apart ("ping-pong"): while one group issues its matrix-core
-//     work, the other does its exponentials, LDS traffic and global loads,
-//     and a workgroup barrier after every phase swaps the roles.  Each wave
+//     work, the other does its exponentials and LDS traffic, and a
+//     workgroup barrier after every phase swaps the roles.  Each wave
 //     alternates
 //        M phase: score MFMAs of stage t, value MFMAs of stage t-1
-//        V phase: weights of stage t, LDS reads of the K fragments of stage
-//                 t+1 and the V fragments of stage t, its group's half of
-//                 stage t+2 into LDS, global loads of stage t+4.
+//        V phase: LDS reads of the K fragments of stage t+1 and the V
+//                 fragments of stage t, weights of stage t, and the copy of
+//                 its group's half of stage t+4 from global memory to LDS.
 //     Every operand of an M phase is in registers when it starts.
-//   * Keys stream through LDS in stages of 32 keys with three buffers; each
-//     group moves half of every stage, two stages ahead of use.  K comes
-//     from the K tensor (bf16, row-major in LDS) through buffer resources
-//     that end at the last valid row, so rows past the sequence end read as
-//     zeros without per-lane branches.  V comes from a workspace image that
-//     a small first kernel writes once per key: float16, transposed, with
-//     the keys of each stage permuted so that one 16-byte LDS read gives
-//     each lane the 8 keys the value MFMA needs.  Moving a stage into LDS
-//     is then 16-byte copies only, with no conversion in the main loop.
+//   * Keys stream through LDS in stages of 32 keys with five buffers.  The
+//     copies go straight from global memory into LDS (buffer loads with
+//     the LDS destination, which puts lane i's 16 bytes at 16 i), four
+//     stages ahead of use, and each wave waits for its own copies of two
+//     stages back at the end of its V phase.  K comes from the K tensor
+//     through a buffer resource that ends at the last valid row, so rows
+//     past the sequence end arrive as zeros.  V comes from a workspace
+//     image that a small first kernel writes once per key: float16,
+//     transposed, with the keys of each stage permuted so that one 16-byte
+//     LDS read gives each lane the 8 keys the value MFMA needs.
+//   * LDS layouts have no padding; an XOR swizzle of the 16-byte chunks of
+//     each row (K: chunk ^ row, V^T: chunk ^ (row / 4)) keeps the 16-row
+//     fragment reads free of bank conflicts, and the copy of each lane
+//     fetches the chunk that belongs to its LDS slot.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_16x16x32_bf16.  In that accumulator layout each lane holds
 //     one query row (4 lanes, l ^ 16 and l ^ 32 apart, share a row), so row
@@ -45,7 +50,7 @@
 //     f16-rounded weights are already in the B-operand layout of
 //     O^T = V^T P~^T (v_mfma_f32_16x16x32_f16): no LDS round trip for P.
 //   * ell and S are summed from the same f16-rounded weights that enter the
-//     value MFMAs (v_dot2_f32_f16), keeping A, C, ell and S consistent.
+//     value MFMAs, keeping A, C, ell and S consistent.
 //   * Each row's offset m is fixed at its first visible stage (that stage's
 //     max + kMargin), so the accumulators are never rescaled inside the
 //     loop.  Rows whose scores later exceed m + kTauHi make the workgroup
@@ -53,8 +58,8 @@
 //     <= 2^kTauHi in the first pass and <= 1 in the second.
 //   * Causal, sliding-window and sink masks ("Sliding-window beats linear
 //     attention" review, sec. 1) skip whole stages per workgroup.  Stages
-//     visible to every row of the workgroup run mask-free; the others apply
-//     per-element masks (selects, a wave-uniform branch around them).
+//     visible to every row of the workgroup run first and mask-free; the
+//     others apply per-element masks.
 //   * Workgroups are issued heaviest query tile first; the block index keeps
 //     all tiles of one (batch, head) on one XCD when B*H is a multiple of 8,
 //     so their K/V reuse stays in that XCD's L2.
@@ -69,37 +74,48 @@ namespace {
 constexpr int ROWS = 16;                  // query rows per wavefront
 constexpr int NWAVES = 8;                 // two groups of four wavefronts
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr int GTHREADS = NTHREADS / 2;    // threads per group
 constexpr int BM = ROWS * NWAVES;         // query rows per workgroup
 constexpr int BN = 32;                    // keys per stage
-constexpr int HALF = BN / 2;              // keys of a stage moved by one group
-constexpr int NBUF = 3;                   // LDS stage buffers
+constexpr int NBUF = 5;                   // LDS stage buffers
+constexpr int AHEAD = 4;                  // stages between a copy and its use
 // Softmax offsets, log2 units (see above).
 constexpr float kMargin = 3.0f;
 constexpr float kTauHi = 5.0f;
 
 static_assert(BM == fwd_block_rows(64) && BM == fwd_block_rows(128),
               "host and kernel must agree on the query tile");
+static_assert(NBUF >= AHEAD + 1, "a buffer is refilled only after its last read");
 
 template <int D>
 struct Cfg {
-    // Row pitches in LDS.  With the MFMA fragment reads (16 rows, 4 adjacent
-    // 16-byte blocks per row), a pitch of an odd multiple of 8 dwords keeps
-    // ds_read_b128 free of bank conflicts on gfx950 (measured).
-    static constexpr int KP = D + 16;   // K: 72 dwords at d = 128, 40 at d = 64
-    static constexpr int VP = BN + 16;  // V^T: 24 dwords
-    static constexpr int K_ELEMS = BN * KP;
-    static constexpr int V_ELEMS = D * VP;
-    static constexpr int KC = D / 32;   // reduction chunks of the score MFMA
-    static constexpr int DT = D / 16;   // output tiles of the value MFMA
-    // 16-byte chunks in a group's half stage of K (and of V).  At d = 128
-    // every thread of the group moves one K and one V chunk; at d = 64 the
-    // first two waves of the group move K chunks and the other two V chunks.
-    static constexpr int HALF_CHUNKS = HALF * (D / 8);
-    static constexpr bool SPLIT = HALF_CHUNKS < GTHREADS;
-    static_assert(HALF_CHUNKS == GTHREADS || 2 * HALF_CHUNKS == GTHREADS,
-                  "a half stage must split evenly over a group");
+    static constexpr int KC = D / 32;     // reduction chunks of the score MFMA
+    static constexpr int DT = D / 16;     // output tiles of the value MFMA
+    static constexpr int CPR = D / 8;     // 16-byte chunks per K row
+    static constexpr int K_ELEMS = BN * D;
+    static constexpr int V_ELEMS = D * BN;
+    // 16-byte copies of a half stage (one group's share) of K and of V^T.
+    // At d = 128 every wave of the group copies one K and one V^T chunk per
+    // lane; at d = 64 the group's first two waves copy K, the others V^T.
+    static constexpr int HALF_K = BN / 2 * CPR;
+    static constexpr int HALF_V = D / 2 * (BN / 8);
+    static constexpr bool SPLIT = HALF_K < 256;
+    static constexpr int COPIES = SPLIT ? 1 : 2;  // copy instructions per wave per stage
+    static_assert(HALF_K == HALF_V && (HALF_K == 256 || HALF_K == 128), "copy split");
 };
+
+// Row swizzle of the K layout: chunk c of row r sits in slot
+// r * CPR + (c ^ kswz(r)).  With 256-byte rows (d = 128) every row spans all
+// banks, so the 16 rows of a fragment read need 16 distinct chunk
+// positions; with 128-byte rows (d = 64) rows r and r+1 share the banks and
+// rows of equal parity need 8 distinct positions.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Slot of chunk q (positions 8q .. 8q+7) of V^T row f in a V^T stage: four
+// 64-byte rows share the banks, so the chunk index is rotated by f / 4.
+__device__ __forceinline__ int vswz_slot(int f, int q) { return 4 * f + (q ^ ((f >> 2) & 3)); }
 
 // Position of stage key j (0..31) inside the transposed V stage.  The score
 // accumulator gives lane group G (lane / 16) the keys 4G..4G+3 and
@@ -149,48 +165,28 @@ __device__ __forceinline__ void pin(const T &x) {
     asm volatile("" ::"v"(x));
 }
 
-// Workgroup barrier between ping-pong phases; the scheduler may not move
-// any instruction across it.
+// Workgroup barrier between ping-pong phases: this wave's LDS operations
+// complete first.  The scheduler may not move anything across it.
+// No memory fence: a fence would also wait for the copies into LDS that
+// are meant to stay in flight across phases (their completion is waited
+// for explicitly, see wait_copies).  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void phase_barrier() {
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// This thread's share of a half stage: where its 16-byte chunks come from
-// and where they go in LDS.  Group g moves keys 16g .. 16g+15 of K (from the
-// K tensor) and features g*d/2 .. (g+1)*d/2 - 1 of the stage's V^T image
-// (from the workspace, already float16, transposed and permuted).
-template <int D>
-struct ChunkMap {
-    uint32_t gk;  // K: byte offset from the stage's first row
-    uint32_t gv;  // V^T image: byte offset inside the stage's image
-    int sk;       // element offset of the K chunk in a K stage
-    int sv;       // element offset of the V^T chunk in a V^T stage
-};
-
-template <int D>
-__device__ __forceinline__ ChunkMap<D> chunk_map(int64_t k_l, int grp, int gt) {
-    using C = Cfg<D>;
-    const int c = C::SPLIT ? (gt % C::HALF_CHUNKS) : gt;
-    ChunkMap<D> m;
-    const int kr = HALF * grp + c / (D / 8);   // K: consecutive lanes walk along a row
-    const int col = (c % (D / 8)) * 8;
-    m.gk = (uint32_t)(kr * k_l * 2 + col * 2);
-    m.sk = kr * C::KP + col;
-    const int f = (D / 2) * grp + c / 4;       // V^T: 4 lanes per 32-position row
-    const int q = c % 4;
-    m.gv = (uint32_t)(f * BN * 2 + q * 16);
-    m.sv = f * C::VP + 8 * q;
-    return m;
+// Waits until at most n of this wave's global -> LDS copies are in flight
+// (s_waitcnt vmcnt(n); the LDS and export counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
-
-// Chunks of a half stage in flight between global memory and LDS.  At
-// d = 64 only `k` is used (holding a K or a V chunk, by wave).
-template <int D>
-struct Chunks {
-    u32x4 k, v;
-};
 
 // Floor and ceiling of a / BN for any sign of a.
 __device__ __forceinline__ int floor_div_bn(int a) { return a >= 0 ? a / BN : -((-a + BN - 1) / BN); }
@@ -230,21 +226,57 @@ struct Weights {
     f16x8 p, w;
 };
 
+// LDS stage buffer: K [32 keys][d] and V^T [d][32 positions], both in the
+// swizzled 16-byte-chunk layouts above.
 template <int D>
-__device__ __forceinline__ void read_kfrags(KFrags<D> &kf, const uint16_t *sk, int l16, int G) {
+struct __attribute__((aligned(16))) StageBuf {
+    uint16_t k[Cfg<D>::K_ELEMS];
+    uint16_t v[Cfg<D>::V_ELEMS];
+};
+
+// Compile-time stage buffer number.
+template <int I>
+using Buf = std::integral_constant<int, I % NBUF>;
+
+// Per-lane byte offsets of the fragment reads inside a K and a V^T stage:
+// ka[kc] for key tile 0 (tile 1 is 16 rows further), va for V^T tile 0
+// (tile dt is 16 dt rows further).
+template <int D>
+struct FragAddr {
+    uint32_t ka[Cfg<D>::KC];
+    uint32_t va;
+};
+
+template <int D>
+__device__ __forceinline__ FragAddr<D> frag_addr(int l16, int G) {
+    using C = Cfg<D>;
+    FragAddr<D> f;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc)
+        f.ka[kc] = (uint32_t)(l16 * C::CPR + ((4 * kc + G) ^ kswz<D>(l16))) * 16u;
+    f.va = (uint32_t)vswz_slot(l16, G) * 16u;
+    return f;
+}
+
+template <int D>
+__device__ __forceinline__ void read_kfrags(KFrags<D> &kf, const uint16_t *sk,
+                                            const FragAddr<D> &fa) {
+    const char *base = reinterpret_cast<const char *>(sk);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int kc = 0; kc < Cfg<D>::KC; ++kc)
-            kf.f[kt][kc] = *reinterpret_cast<const bf16x8 *>(sk + (16 * kt + l16) * Cfg<D>::KP +
-                                                             32 * kc + 8 * G);
+            kf.f[kt][kc] = *reinterpret_cast<const bf16x8 *>(base + fa.ka[kc] +
+                                                             kt * 16 * Cfg<D>::CPR * 16);
 }
 
 template <int D>
-__device__ __forceinline__ void read_vfrags(VFrags<D> &vf, const uint16_t *sv, int l16, int G) {
+__device__ __forceinline__ void read_vfrags(VFrags<D> &vf, const uint16_t *sv,
+                                            const FragAddr<D> &fa) {
+    const char *base = reinterpret_cast<const char *>(sv);
 #pragma unroll
     for (int dt = 0; dt < Cfg<D>::DT; ++dt)
-        vf.f[dt] = *reinterpret_cast<const f16x8 *>(sv + (16 * dt + l16) * Cfg<D>::VP + 8 * G);
+        vf.f[dt] = *reinterpret_cast<const f16x8 *>(base + fa.va + dt * 16 * 4 * 16);
 }
 
 // S^T = K Q^T and R K^T for one stage: 2 key tiles x KC chunks x 2 MFMAs,
@@ -308,7 +340,8 @@ __device__ __forceinline__ bool init_offsets(Ctx<D> &cx, const Scores &s, float 
 }
 
 // Weights of one stage: the per-lane running max of the raw scores, the f16
-// weights in the value MFMA's B-operand order, and their sums ell and S.
+// weights in the value MFMA's B-operand order, and their sums ell and S
+// taken from the same f16 values (v_dot2_f32_f16).
 template <int D>
 __device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights &pw, float c) {
     cx.xlane = fmaxf(fmaxf(fmaxf(cx.xlane, s.q[0][0]), s.q[0][1]),
@@ -337,9 +370,10 @@ __device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights &pw
 // Workspace image of the values: one workgroup per (32-key stage, batch *
 // head).  Keys 32s .. 32s+31 (zeros past L) are converted to float16 and
 // transposed through LDS into [d features][32 positions], position
-// vt_pos(key), so that the prefill moves each stage into LDS with plain
-// 16-byte copies.  The conversion and transposition happen once per key
-// instead of once per query tile.
+// vt_pos(key), and written in the prefill's swizzled LDS slot order, so
+// that the prefill moves each stage into LDS with plain 16-byte copies.
+// The conversion and transposition happen once per key instead of once per
+// query tile.
 template <int D>
 __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
     constexpr int TP = BN + 8;  // LDS row pitch (halves): 16-byte aligned rows
@@ -370,7 +404,7 @@ __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
         for (int c = threadIdx.x; c < D * (BN / 8); c += blockDim.x) {
             const int f = c / (BN / 8);
             const int q = c % (BN / 8);
-            *reinterpret_cast<u32x4 *>(dst + f * BN + 8 * q) =
+            *reinterpret_cast<u32x4 *>(dst + vswz_slot(f, q) * 8) =
                 *reinterpret_cast<const u32x4 *>(&T[f * TP + 8 * q]);
         }
         __syncthreads();
@@ -384,14 +418,34 @@ __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
 template <int D, bool WHOLE>
 __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][C::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][C::V_ELEMS];
+    // One LDS variable per stage buffer, each indexed only by compile-time
+    // buffer numbers: the compiler then tells the buffers apart and waits
+    // before a fragment read only for the copies into that buffer.
+    __shared__ StageBuf<D> sb0, sb1, sb2, sb3, sb4;
+    auto sbuf = [&](auto b) -> StageBuf<D> & {
+        if constexpr (std::is_same_v<decltype(b), int>) {
+            const int i = b % NBUF;
+            return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : i == 3 ? sb3 : sb4;
+        } else {
+            constexpr int i = decltype(b)::value % NBUF;
+            if constexpr (i == 0)
+                return sb0;
+            else if constexpr (i == 1)
+                return sb1;
+            else if constexpr (i == 2)
+                return sb2;
+            else if constexpr (i == 3)
+                return sb3;
+            else
+                return sb4;
+        }
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2;            // ping-pong group
-    const int gt = tid & (GTHREADS - 1);  // thread index inside the group
+    const int grp = wave >> 2;  // ping-pong group
+    const int wg = wave & 3;    // wave inside the group
     const int l16 = lane & 15;
     const int G = lane >> 4;
 
@@ -473,79 +527,58 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         return list_j0(t < n_full ? f_lo + t : (m < f_lo ? m : f_hi + (m - f_lo)));
     };
 
-    // Global <-> LDS movement of this group's half of a stage.  Loads past
-    // the last stage reload the last stage (into a buffer nobody reads
-    // again), which keeps the phases branch-free.
-    const ChunkMap<D> cm = chunk_map<D>(a.k_l, grp, gt);
-    const bool k_role = !C::SPLIT || (wave & 2) == 0;  // d = 64: waves moving K chunks
-    constexpr uint32_t kImage = D * BN * 2;           // bytes of one stage's V^T image
+    // Copies of this wave's share of a stage, global -> LDS.  The LDS
+    // destination of lane i is slot base + i of the stage (16-byte slots),
+    // so each lane fetches the chunk that the swizzled layout puts there.
+    // Copies past the last stage reload the last stage (into a buffer
+    // nobody reads again), which keeps the loop branch-free.
+    const bool k_role = !C::SPLIT || wg < 2;  // d = 64: waves copying K
+    const int kslot0 = grp * C::HALF_K + wg * 64;                       // K slots of this wave
+    const int vslot0 = grp * C::HALF_V + (C::SPLIT ? wg - 2 : wg) * 64;  // V^T slots of this wave
+    uint32_t kgoff;  // byte offset of this lane's K chunk from the stage's first row
+    {
+        const int s = kslot0 + lane;
+        const int r = s / C::CPR;
+        const int ch = (s % C::CPR) ^ kswz<D>(r);
+        kgoff = (uint32_t)(r * a.k_l * 2 + ch * 16);
+    }
+    const uint32_t vgoff = (uint32_t)(vslot0 + lane) * 16u;
+    constexpr uint32_t kImage = D * BN * 2;  // bytes of one stage's V^T image
     const __amdgpu_buffer_rsrc_t rk_all = make_rsrc(kb, WHOLE ? rows_bytes(0, L, a.k_l, D) : 0u);
     const __amdgpu_buffer_rsrc_t rv_all = make_rsrc(vtb, WHOLE ? (uint32_t)a.n_st * kImage : 0u);
-    auto fetch = [&](Chunks<D> &p, int t) __attribute__((always_inline)) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto copy = [&](int t, auto buf) __attribute__((always_inline)) {
         const int j0 = __builtin_amdgcn_readfirstlane(stage_j0(min(t, n - 1)));
         const int si = j0 / BN;
+        lds_void *kdst = (lds_void *)&sbuf(buf).k[kslot0 * 8];
+        lds_void *vdst = (lds_void *)&sbuf(buf).v[vslot0 * 8];
         if constexpr (WHOLE) {
             // Offsets stay below 2^32: the K slice is < 2^31 bytes and a
             // stage reaches at most 31 rows (< 2^30 bytes) past its end; the
             // V^T images of the slice span < 2^31 bytes.
             const uint32_t ko = (uint32_t)j0 * (uint32_t)a.k_l * 2u;
             const uint32_t vo = (uint32_t)si * kImage;
-            if constexpr (!C::SPLIT) {
-                p.k = bufld16(rk_all, cm.gk + ko);
-                p.v = bufld16(rv_all, cm.gv + vo);
-            } else {
-                p.k = bufld16(k_role ? rk_all : rv_all, k_role ? cm.gk + ko : cm.gv + vo);
-            }
+            if (k_role)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk_all, kdst, 16, (int)(kgoff + ko), 0, 0, 0);
+            if (!C::SPLIT || !k_role)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv_all, vdst, 16, (int)(vgoff + vo), 0, 0, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rk =
                 make_rsrc(kb + (int64_t)j0 * a.k_l, rows_bytes(j0, L, a.k_l, D));
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vtb + (int64_t)si * (D * BN), kImage);
-            if constexpr (!C::SPLIT) {
-                p.k = bufld16(rk, cm.gk);
-                p.v = bufld16(rv, cm.gv);
-            } else {
-                p.k = bufld16(k_role ? rk : rv, k_role ? cm.gk : cm.gv);
-            }
-        }
-    };
-    auto store = [&](const Chunks<D> &p, int buf) __attribute__((always_inline)) {
-        if constexpr (!C::SPLIT) {
-            *reinterpret_cast<u32x4 *>(&sK[buf][cm.sk]) = p.k;
-            *reinterpret_cast<u32x4 *>(&sV[buf][cm.sv]) = p.v;
-        } else {
             if (k_role)
-                *reinterpret_cast<u32x4 *>(&sK[buf][cm.sk]) = p.k;
-            else
-                *reinterpret_cast<u32x4 *>(&sV[buf][cm.sv]) = p.k;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, (int)kgoff, 0, 0, 0);
+            if (!C::SPLIT || !k_role)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, (int)vgoff, 0, 0, 0);
         }
     };
 
+    const FragAddr<D> fa = frag_addr<D>(l16, G);
     KFrags<D> kf;
     VFrags<D> vf;
     Scores sc;
     Weights pw;
-    Chunks<D> p0, p1;  // stage s is in flight in p(s & 1)
 
-    // V phase that follows the scores of stage t: weights of stage t, K
-    // fragments of stage t+1, V fragments of stage t, this group's half of
-    // stage t+2 into LDS, loads of stage t+4.  It has no branch, so the
-    // scheduler can interleave all of it.
-    // b0 = t % NBUF, a compile-time constant in the unrolled main loop (the
-    // buffer offsets then fold into the LDS instructions' offset fields).
-    auto vphase = [&](auto b0, int t, Chunks<D> &p) __attribute__((always_inline)) {
-        // Fragment reads first: their LDS latency is the longest chain of
-        // the phase (measured faster than interleaving them with the VALU).
-        read_kfrags<D>(kf, sK[(b0 + 1) % NBUF], l16, G);
-        read_vfrags<D>(vf, sV[b0 % NBUF], l16, G);
-        __builtin_amdgcn_sched_barrier(0);
-        weights<D>(cx, sc, pw, c);
-        pin(pw.p);
-        pin(pw.w);
-        pin(cx.ell);
-        pin(cx.ssum);
-        store(p, (b0 + 2) % NBUF);
-        fetch(p, t + 4);
-    };
     // End of the M phase, when the score MFMAs are done.  Masked stages: the
     // mask of stage t's scores and the softmax offsets of rows that still
     // have none.  Full stages come first and stage 0 sets every offset, so
@@ -564,20 +597,39 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         }
         pin(cx.msub);
     };
+    // V phase of step t (b0 = t % NBUF, always a compile-time constant):
+    // fragment reads first (their LDS latency is the longest chain of the
+    // phase), weights, the copy of stage t+4, then the wait for this wave's
+    // copies of stage t+2 so that the barrier publishes it.  Stage s lives
+    // in buffer s % 5 from its copy (step s-4) to its last read (step s).
+    auto vphase = [&](auto b0, int t) __attribute__((always_inline)) {
+        read_kfrags<D>(kf, sbuf(b0 + 1).k, fa);
+        read_vfrags<D>(vf, sbuf(b0).v, fa);
+        __builtin_amdgcn_sched_barrier(0);
+        weights<D>(cx, sc, pw, c);
+        pin(pw.p);
+        pin(pw.w);
+        pin(cx.ell);
+        pin(cx.ssum);
+        copy(t + AHEAD, b0 + AHEAD);
+        wait_copies<(AHEAD - 2) * C::COPIES>();
+    };
     // One step: M phase of stage t, barrier, V phase of stage t, barrier.
-    auto step = [&](auto masked, auto b0, int t, Chunks<D> &p) __attribute__((always_inline)) {
+    auto step = [&](auto masked, auto b0, int t) __attribute__((always_inline)) {
         score_mfmas<D>(cx, kf, sc);
         value_mfmas<D>(cx, vf, pw);
         finish_scores(masked, t);
         phase_barrier();
-        vphase(b0, t, p);
+        vphase(b0, t);
         phase_barrier();
     };
     const std::integral_constant<bool, true> kMasked;
     const std::integral_constant<bool, false> kFull;
-    const std::integral_constant<int, 0> kB0;
-    const std::integral_constant<int, 1> kB1;
-    const std::integral_constant<int, 2> kB2;
+    const Buf<0> kB0;
+    const Buf<1> kB1;
+    const Buf<2> kB2;
+    const Buf<3> kB3;
+    const Buf<4> kB4;
 
     // Pass 0 uses offsets fixed at each row's first visible stage; if any
     // row's scores later rose more than kTauHi above its offset, pass 1
@@ -591,15 +643,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         cx.ell = 0.f;
         cx.ssum = 0.f;
 
-        // Stages 0 and 1 into LDS, 2 and 3 in flight.
-        fetch(p0, 0);
-        fetch(p1, 1);
-        store(p0, 0);
-        fetch(p0, 2);
-        store(p1, 1);
-        fetch(p1, 3);
+        // Stages 0 .. AHEAD-1 into LDS.
+        copy(0, kB0);
+        copy(1, kB1);
+        copy(2, kB2);
+        copy(3, kB3);
+        wait_copies<0>();
         __syncthreads();
-        read_kfrags<D>(kf, sK[0], l16, G);
+        read_kfrags<D>(kf, sb0.k, fa);
         // The second group starts one phase later.
         if (grp == 1)
             phase_barrier();
@@ -612,39 +663,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             offsets_set = init_offsets<D>(cx, sc, c);
         finish_scores(kFull, 0);
         phase_barrier();
-        vphase(kB0, 0, p0);
+        vphase(kB0, 0);
         phase_barrier();
-        // Step t moves stage t+2, in flight in p((t + 2) & 1) = p(t & 1),
-        // and uses LDS buffers t % 3 .. (t + 2) % 3.  The main loop runs six
-        // steps per iteration (t = 1 mod 6), so both are fixed per step.
+        // The main loop runs NBUF steps per iteration (t = 1 mod 5), which
+        // fixes the LDS buffers of every step.
         int t = 1;
         const int t_mask = max(1, n_full);
-        for (; t + 5 < t_mask; t += 6) {
-            step(kFull, kB1, t, p1);
-            step(kFull, kB2, t + 1, p0);
-            step(kFull, kB0, t + 2, p1);
-            step(kFull, kB1, t + 3, p0);
-            step(kFull, kB2, t + 4, p1);
-            step(kFull, kB0, t + 5, p0);
+        for (; t + 4 < t_mask; t += 5) {
+            step(kFull, kB1, t);
+            step(kFull, kB2, t + 1);
+            step(kFull, kB3, t + 2);
+            step(kFull, kB4, t + 3);
+            step(kFull, kB0, t + 4);
         }
-        for (; t + 1 < t_mask; t += 2) {
-            step(kFull, t % NBUF, t, p1);
-            step(kFull, (t + 1) % NBUF, t + 1, p0);
-        }
-        if (t < t_mask) {
-            step(kFull, t % NBUF, t, p1);
-            ++t;
-        }
-        if (t < n && (t & 1) == 0) {
-            step(kMasked, t % NBUF, t, p0);
-            ++t;
-        }
-        for (; t + 1 < n; t += 2) {
-            step(kMasked, t % NBUF, t, p1);
-            step(kMasked, (t + 1) % NBUF, t + 1, p0);
-        }
-        if (t < n)
-            step(kMasked, t % NBUF, t, p1);
+        for (; t < t_mask; ++t)
+            step(kFull, t, t);
+        for (; t < n; ++t)
+            step(kMasked, t, t);
         // Value MFMAs of the last stage; the first group catches up with the
         // second group's extra barrier.
         value_mfmas<D>(cx, vf, pw);
@@ -653,6 +688,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
 
         const float xmax = row_max4(cx.xlane);
         const bool overflow = pass == 0 && xmax * c > cx.m_ref + kTauHi;
+        // Copies still in flight (stages past the end) land before LDS is
+        // reused by the next pass.
+        wait_copies<0>();
         if (!__syncthreads_or(overflow))
             break;
         // Exact offsets for the recomputation: each row's true max.
