@@ -24,15 +24,16 @@
 //     work, the other does its exponentials and LDS traffic, and a
 //     workgroup barrier after every phase swaps the roles.  Each wave
 //     alternates
-//        M phase: score MFMAs of stage t, value MFMAs of stage t-1
-//        V phase: LDS reads of the K fragments of stage t+1 and the V
-//                 fragments of stage t, weights of stage t, and the copy of
-//                 its group's half of stage t+4 from global memory to LDS.
-//     Every operand of an M phase is in registers when it starts.
-//   * Keys stream through LDS in stages of 32 keys with five buffers.  The
+//        M phase: score MFMAs of stage t, value and row-sum MFMAs of stage
+//                 t-1 with the LDS reads of stage t+1's K fragments
+//                 between them;
+//        V phase: LDS reads of the V fragments of stage t, weights of
+//                 stage t, and the copy of its group's half of stage t+5
+//                 from global memory to LDS.
+//   * Keys stream through LDS in stages of 32 keys with six buffers.  The
 //     copies go straight from global memory into LDS (buffer loads with
-//     the LDS destination, which puts lane i's 16 bytes at 16 i), four
-//     stages ahead of use, and each wave waits for its own copies of two
+//     the LDS destination, which puts lane i's 16 bytes at 16 i), five
+//     stages ahead of use, and each wave waits for its own copies of three
 //     stages back at the end of its V phase.  K comes from the K tensor
 //     through a buffer resource that ends at the last valid row, so rows
 //     past the sequence end arrive as zeros.  V comes from a workspace
@@ -45,12 +46,13 @@
 //     fetches the chunk that belongs to its LDS slot.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_16x16x32_bf16.  In that accumulator layout each lane holds
-//     one query row (4 lanes, l ^ 16 and l ^ 32 apart, share a row), so row
-//     max and row sums are in-lane reductions plus two exchanges, and the
+//     one query row (4 lanes, l ^ 16 and l ^ 32 apart, share a row), so the
+//     row max is an in-lane reduction plus two exchanges, and the
 //     f16-rounded weights are already in the B-operand layout of
 //     O^T = V^T P~^T (v_mfma_f32_16x16x32_f16): no LDS round trip for P.
-//   * ell and S are summed from the same f16-rounded weights that enter the
-//     value MFMAs, keeping A, C, ell and S consistent.
+//   * ell and S come from two more MFMAs of the same f16 weights against an
+//     all-ones operand, so A, C, ell and S are sums of the same values, and
+//     no VALU time goes to the sums.
 //   * Each row's offset m is fixed at its first visible stage (that stage's
 //     max + kMargin), so the accumulators are never rescaled inside the
 //     loop.  Rows whose scores later exceed m + kTauHi make the workgroup
@@ -76,8 +78,9 @@ constexpr int NWAVES = 8;                 // two groups of four wavefronts
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int BM = ROWS * NWAVES;         // query rows per workgroup
 constexpr int BN = 32;                    // keys per stage
-constexpr int NBUF = 5;                   // LDS stage buffers
-constexpr int AHEAD = 4;                  // stages between a copy and its use
+constexpr int NBUF = 6;                   // LDS stage buffers
+constexpr int AHEAD = 5;                  // stages between a copy and its use
+constexpr int IN_FLIGHT = 2;              // stages a wave's copies may still be in flight
 // Softmax offsets, log2 units (see above).
 constexpr float kMargin = 3.0f;
 constexpr float kTauHi = 5.0f;
@@ -85,6 +88,7 @@ constexpr float kTauHi = 5.0f;
 static_assert(BM == fwd_block_rows(64) && BM == fwd_block_rows(128),
               "host and kernel must agree on the query tile");
 static_assert(NBUF >= AHEAD + 1, "a buffer is refilled only after its last read");
+static_assert(AHEAD - IN_FLIGHT >= 3, "K of stage t+1 is read in the M phase of stage t");
 
 template <int D>
 struct Cfg {
@@ -130,12 +134,6 @@ __device__ __forceinline__ float xor32_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float xor32_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // Exchanges between 16-lane rows done on the VALU (v_permlane16_swap):
 // no LDS instruction, so they never wait behind outstanding LDS reads.
 __device__ __forceinline__ float xor16_max(float x) {
@@ -144,16 +142,8 @@ __device__ __forceinline__ float xor16_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float xor16_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // Reductions over the four lanes that share a query row (l, l^16, l^32, l^48).
 __device__ __forceinline__ float row_max4(float x) { return xor32_max(xor16_max(x)); }
-
-__device__ __forceinline__ float row_sum4(float x) { return xor32_sum(xor16_sum(x)); }
 
 // Marks x as needed here: code that computes it cannot be moved past this
 // point (neither by IR passes nor by the scheduler), which keeps each
@@ -199,7 +189,10 @@ struct Ctx {
     float m_ref;  // this row's softmax offset (scaled log2 units), -inf until set
     float msub;   // m_ref, or 0 while it is unset (all scores so far are -inf)
     float xlane;  // running max of this lane's raw scores of the row
-    float ell, ssum;
+    // Row sums ell and S on the matrix core: (ones x P~^T) puts each row's
+    // sum in every element of its column, so element 0 of the lane's
+    // accumulator is its row's sum.
+    f32x4 accL, accS;
 };
 
 // K fragments of one stage (A operand of the score MFMAs): key 16 kt + l16,
@@ -299,9 +292,14 @@ __device__ __forceinline__ void score_mfmas(const Ctx<D> &cx, const KFrags<D> &k
         }
 }
 
-// O^T += V^T P~^T and V^T (P~ o S)^T for one stage.
+// O^T += V^T P~^T and V^T (P~ o S)^T for one stage, and the row sums
+// ell += sum p~ and S += sum p~ s of the same f16 values.
 template <int D>
 __device__ __forceinline__ void value_mfmas(Ctx<D> &cx, const VFrags<D> &vf, const Weights &pw) {
+    const _Float16 one = (_Float16)1.0f;
+    const f16x8 ones = {one, one, one, one, one, one, one, one};
+    cx.accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw.p, cx.accL, 0, 0, 0);
+    cx.accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw.w, cx.accS, 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
         cx.accA[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], pw.p, cx.accA[dt], 0, 0, 0);
@@ -339,15 +337,14 @@ __device__ __forceinline__ bool init_offsets(Ctx<D> &cx, const Scores &s, float 
     return __builtin_amdgcn_ballot_w64(cx.m_ref == kNegInf) == 0;
 }
 
-// Weights of one stage: the per-lane running max of the raw scores, the f16
-// weights in the value MFMA's B-operand order, and their sums ell and S
-// taken from the same f16 values (v_dot2_f32_f16).
+// Weights of one stage: the per-lane running max of the raw scores, and the
+// f16 weights p~ and p~ s in the value MFMA's B-operand order (p~ s is
+// rounded once, from the f32 product).
 template <int D>
 __device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights &pw, float c) {
     cx.xlane = fmaxf(fmaxf(fmaxf(cx.xlane, s.q[0][0]), s.q[0][1]),
                      fmaxf(fmaxf(s.q[0][2], s.q[0][3]), s.q[1][0]));
     cx.xlane = fmaxf(fmaxf(fmaxf(cx.xlane, s.q[1][1]), s.q[1][2]), s.q[1][3]);
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -357,8 +354,6 @@ __device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights &pw
             const float p1 = exp2_fast(fmaf(s.q[kt][e + 1], c, -cx.msub));
             const f16x2 ph = cvt_f16x2(p0, p1);
             const f16x2 wh = cvt_f16x2(p0 * s.r[kt][e], p1 * s.r[kt][e + 1]);
-            cx.ell = __builtin_amdgcn_fdot2(ph, ones, cx.ell, false);
-            cx.ssum = __builtin_amdgcn_fdot2(wh, ones, cx.ssum, false);
             pw.p[4 * kt + e] = ph[0];
             pw.p[4 * kt + e + 1] = ph[1];
             pw.w[4 * kt + e] = wh[0];
@@ -421,11 +416,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // One LDS variable per stage buffer, each indexed only by compile-time
     // buffer numbers: the compiler then tells the buffers apart and waits
     // before a fragment read only for the copies into that buffer.
-    __shared__ StageBuf<D> sb0, sb1, sb2, sb3, sb4;
+    __shared__ StageBuf<D> sb0, sb1, sb2, sb3, sb4, sb5;
     auto sbuf = [&](auto b) -> StageBuf<D> & {
         if constexpr (std::is_same_v<decltype(b), int>) {
             const int i = b % NBUF;
-            return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : i == 3 ? sb3 : sb4;
+            return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : i == 3 ? sb3 : i == 4 ? sb4 : sb5;
         } else {
             constexpr int i = decltype(b)::value % NBUF;
             if constexpr (i == 0)
@@ -436,8 +431,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
                 return sb2;
             else if constexpr (i == 3)
                 return sb3;
-            else
+            else if constexpr (i == 4)
                 return sb4;
+            else
+                return sb5;
         }
     };
 
@@ -597,28 +594,42 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         }
         pin(cx.msub);
     };
-    // V phase of step t (b0 = t % NBUF, always a compile-time constant):
-    // fragment reads first (their LDS latency is the longest chain of the
-    // phase), weights, the copy of stage t+4, then the wait for this wave's
-    // copies of stage t+2 so that the barrier publishes it.  Stage s lives
-    // in buffer s % 5 from its copy (step s-4) to its last read (step s).
-    auto vphase = [&](auto b0, int t) __attribute__((always_inline)) {
+    // M phase of step t (b0 = t % NBUF, always a compile-time constant):
+    // the score MFMAs of stage t, then the value MFMAs of stage t-1 with the
+    // reads of stage t+1's K fragments between them (the K registers are
+    // free once the score MFMAs have issued).  An M-phase wave has idle
+    // issue slots between its MFMAs, while a V-phase wave stalls on each
+    // LDS read that the busy LDS cannot take yet.
+    auto mphase = [&](auto masked, auto b0, int t, bool values) __attribute__((always_inline)) {
+        score_mfmas<D>(cx, kf, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (values)
+            value_mfmas<D>(cx, vf, pw);
         read_kfrags<D>(kf, sbuf(b0 + 1).k, fa);
+#pragma unroll
+        for (int i = 0; i < 2 * C::KC; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, C::DT / C::KC, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        finish_scores(masked, t);
+    };
+    // V phase of step t: V fragment reads first, weights, the copy of stage
+    // t+5, then the wait for this wave's copies of stage t+3, which the
+    // barrier then publishes to both groups before their M phases read its
+    // K.  Stage s lives in buffer s % 6 from its copy (step s-5) to its last
+    // read (V phase of step s).
+    auto vphase = [&](auto b0, int t) __attribute__((always_inline)) {
         read_vfrags<D>(vf, sbuf(b0).v, fa);
         __builtin_amdgcn_sched_barrier(0);
         weights<D>(cx, sc, pw, c);
         pin(pw.p);
         pin(pw.w);
-        pin(cx.ell);
-        pin(cx.ssum);
         copy(t + AHEAD, b0 + AHEAD);
-        wait_copies<(AHEAD - 2) * C::COPIES>();
+        wait_copies<IN_FLIGHT * C::COPIES>();
     };
-    // One step: M phase of stage t, barrier, V phase of stage t, barrier.
+    // One step: M phase, barrier, V phase, barrier.
     auto step = [&](auto masked, auto b0, int t) __attribute__((always_inline)) {
-        score_mfmas<D>(cx, kf, sc);
-        value_mfmas<D>(cx, vf, pw);
-        finish_scores(masked, t);
+        mphase(masked, b0, t, true);
         phase_barrier();
         vphase(b0, t);
         phase_barrier();
@@ -630,6 +641,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     const Buf<2> kB2;
     const Buf<3> kB3;
     const Buf<4> kB4;
+    const Buf<5> kB5;
 
     // Pass 0 uses offsets fixed at each row's first visible stage; if any
     // row's scores later rose more than kTauHi above its offset, pass 1
@@ -640,14 +652,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             cx.accA[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
             cx.accC[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
-        cx.ell = 0.f;
-        cx.ssum = 0.f;
+        cx.accL = (f32x4){0.f, 0.f, 0.f, 0.f};
+        cx.accS = (f32x4){0.f, 0.f, 0.f, 0.f};
 
         // Stages 0 .. AHEAD-1 into LDS.
         copy(0, kB0);
         copy(1, kB1);
         copy(2, kB2);
         copy(3, kB3);
+        copy(4, kB4);
         wait_copies<0>();
         __syncthreads();
         read_kfrags<D>(kf, sb0.k, fa);
@@ -656,25 +669,27 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             phase_barrier();
         // Step 0 has no value MFMAs; it sets the offsets of all rows that
         // see any of its keys (all rows when it is a full stage).
-        score_mfmas<D>(cx, kf, sc);
-        if (n_full == 0)
-            mask_scores(sc, stage_j0(0), row, G, L, window, n_sink);
-        if (!offsets_set)
-            offsets_set = init_offsets<D>(cx, sc, c);
-        finish_scores(kFull, 0);
+        if (n_full == 0) {
+            mphase(kMasked, kB0, 0, false);
+        } else {
+            mphase(kFull, kB0, 0, false);
+            if (!offsets_set)
+                offsets_set = init_offsets<D>(cx, sc, c);
+        }
         phase_barrier();
         vphase(kB0, 0);
         phase_barrier();
-        // The main loop runs NBUF steps per iteration (t = 1 mod 5), which
+        // The main loop runs NBUF steps per iteration (t = 1 mod 6), which
         // fixes the LDS buffers of every step.
         int t = 1;
         const int t_mask = max(1, n_full);
-        for (; t + 4 < t_mask; t += 5) {
+        for (; t + 5 < t_mask; t += 6) {
             step(kFull, kB1, t);
             step(kFull, kB2, t + 1);
             step(kFull, kB3, t + 2);
             step(kFull, kB4, t + 3);
-            step(kFull, kB0, t + 4);
+            step(kFull, kB5, t + 4);
+            step(kFull, kB0, t + 5);
         }
         for (; t < t_mask; ++t)
             step(kFull, t, t);
@@ -699,9 +714,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         offsets_set = true;
     }
 
-    // Epilogue: combine the partial sums of the four lanes of each row.
-    const float ell_t = row_sum4(cx.ell);
-    const float s_t = row_sum4(cx.ssum);
+    // Epilogue.
+    const float ell_t = cx.accL[0];
+    const float s_t = cx.accS[0];
     if (row < L) {
         const float inv = 1.f / ell_t;
         const float keep = 1.f - s_t * inv;
