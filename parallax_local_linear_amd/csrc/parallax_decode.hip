@@ -13,7 +13,12 @@
 // Work split: one workgroup per (b, h) with NS wavefronts; wavefront s owns
 // one contiguous chunk of the cache.  Inside a wavefront, D/8 lanes share a
 // key (16 bytes = 8 features each), so a wave step covers 512/D keys and
-// every global load is fully coalesced.  Each lane group keeps running
+// every global load is fully coalesced.  Loads go through buffer resources
+// that end at the chunk's last row (rows past it read as zeros, no
+// branches), the per-key dot products are summed across the D/8 lanes with
+// DPP moves, and two wave steps per iteration keep the kernel within 64
+// VGPRs: eight wavefronts per SIMD, so two workgroups share a CU and one
+// streams while the other merges.  Each lane group keeps running
 //     m, ell = sum p~, S = sum p~ s, A = sum p~ v, C = sum p~ s v
 // (s = rho . k, p~ = 2^(x - m)) for its 8 features.  The partial states are
 // merged first across lane groups with shuffles, then across wavefronts
@@ -24,21 +29,41 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace plx {
 namespace {
+
+// Sum over aligned groups of N lanes (N = 8 or 16) with DPP moves on the
+// VALU: quad swaps, then the half-row and row mirrors pair the quads and the
+// half-rows.  Every lane of a group ends with the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                               0xF, 0xF, false));
+    };
+    x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    if constexpr (N == 16)
+        x += dpp(x, std::integral_constant<int, 0x140>{});  // row_mirror
+    return x;
+}
 
 template <int D, int NS>
 __global__ __launch_bounds__(64 * NS) void parallax_decode_kernel(DecodeArgs a) {
     constexpr int LPK = D / 8;     // lanes per key
     constexpr int KPS = 64 / LPK;  // keys per wave step
-    constexpr int U = 4;           // wave steps per iteration (loads in flight)
+    constexpr int U = 2;           // wave steps per iteration (loads in flight)
 
     __shared__ float s_m[NS], s_l[NS], s_s[NS];
     __shared__ float s_A[NS][D], s_C[NS][D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = lane / LPK;
     const int sub = lane % LPK;
     const int bh = blockIdx.x;
@@ -64,8 +89,14 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_kernel(DecodeArgs a) 
             rv[2 * w + 1] = bf16_hi(rw[w]);
         }
     }
-    const uint16_t *kb = a.k + (int64_t)b * a.k_b + (int64_t)h * a.k_h + 8 * sub;
-    const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h + 8 * sub;
+    // Each iteration reads rows [j, j + KPS*U) through buffer resources that
+    // end at the chunk's last row, so rows past it read as zeros.
+    const uint16_t *kb = a.k + (int64_t)b * a.k_b + (int64_t)h * a.k_h + (int64_t)start * a.k_l;
+    const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h + (int64_t)start * a.v_l;
+    const uint32_t koff = (uint32_t)(grp * a.k_l * 2 + 16 * sub);
+    const uint32_t voff = (uint32_t)(grp * a.v_l * 2 + 16 * sub);
+    const uint32_t kstep = (uint32_t)(KPS * a.k_l * 2);
+    const uint32_t vstep = (uint32_t)(KPS * a.v_l * 2);
 
     float m = kNegInf, ell = 0.f, ssum = 0.f;
     float A[8], C[8];
@@ -76,15 +107,17 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_kernel(DecodeArgs a) 
     }
 
     for (int j = start; j < end; j += KPS * U) {
+        const __amdgpu_buffer_rsrc_t ks =
+            make_rsrc(kb + (int64_t)(j - start) * a.k_l, rows_bytes(j, end, a.k_l, D));
+        const __amdgpu_buffer_rsrc_t vs =
+            make_rsrc(vb + (int64_t)(j - start) * a.v_l, rows_bytes(j, end, a.v_l, D));
         u32x4 kw[U], vw[U];
         bool valid[U];
-        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int key = j + u * KPS + grp;
-            valid[u] = key < end;
-            kw[u] = valid[u] ? ldg16(kb + (int64_t)key * a.k_l) : zero;
-            vw[u] = valid[u] ? ldg16(vb + (int64_t)key * a.v_l) : zero;
+            valid[u] = j + u * KPS + grp < end;
+            kw[u] = __builtin_amdgcn_raw_buffer_load_b128(ks, (int)koff, (int)(u * kstep), 0);
+            vw[u] = __builtin_amdgcn_raw_buffer_load_b128(vs, (int)voff, (int)(u * vstep), 0);
         }
         float x[U], sr[U];
 #pragma unroll
@@ -99,11 +132,8 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_kernel(DecodeArgs a) 
                 dr = fmaf(rv[2 * w], k0, dr);
                 dr = fmaf(rv[2 * w + 1], k1, dr);
             }
-#pragma unroll
-            for (int off = 1; off < LPK; off <<= 1) {
-                dq += __shfl_xor(dq, off, 64);
-                dr += __shfl_xor(dr, off, 64);
-            }
+            dq = group_sum<LPK>(dq);
+            dr = group_sum<LPK>(dr);
             x[u] = valid[u] ? dq * c : kNegInf;
             sr[u] = dr;
         }
