@@ -242,7 +242,7 @@ def main():
             "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4),
             "traffic": measured_traffic("prefill"),
             "algorithmic_flop_per_launch": p_flops,
-            "kernel": "parallax_fwd_kernel<128>",
+            "kernel": "parallax_attn_fwd call = parallax_vprep_kernel<128> + parallax_fwd_kernel<128>",
         },
         "decode": {
             "value": round(d_gbs, 1),
