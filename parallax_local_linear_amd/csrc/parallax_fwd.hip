@@ -579,10 +579,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // End of the M phase, when the score MFMAs are done.  Masked stages: the
     // mask of stage t's scores and the softmax offsets of rows that still
     // have none.  Full stages come first and stage 0 sets every offset, so
-    // the other full stages need neither.
+    // the other full stages need neither.  `masked` is kFull (0), kMasked (1)
+    // or kCausal (2): a causal-only mask (no window; then the sinks are
+    // inside the causal span) once every offset is set.
     bool offsets_set = false;  // wave-uniform
     auto finish_scores = [&](auto masked, int t) __attribute__((always_inline)) {
-        if constexpr (decltype(masked)::value) {
+        if constexpr (decltype(masked)::value == 2) {
+            const int dlim = min(row, L - 1) - stage_j0(t) - 4 * G;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sc.q[kt][e] = (16 * kt + e <= dlim) ? sc.q[kt][e] : kNegInf;
+        } else if constexpr (decltype(masked)::value) {
             mask_scores(sc, stage_j0(t), row, G, L, window, n_sink);
             if (!offsets_set)
                 offsets_set = init_offsets<D>(cx, sc, c);
@@ -690,6 +699,40 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             step(kFull, kB4, t + 3);
             step(kFull, kB5, t + 4);
             step(kFull, kB0, t + 5);
+        }
+        // Causal tiles whose offsets are all set (the common case): the
+        // remaining full stages and the diagonal ones go through a lean
+        // causal step, unrolled like the main loop so that every LDS buffer
+        // number stays a compile-time constant; the last partial group uses
+        // nested guards (a loop with early exits makes the register
+        // allocator spill heavily).  Otherwise: steps with a runtime buffer
+        // number, before whose LDS reads the compiler waits for every copy
+        // in flight.
+        if (n_full > 0 && window <= 0) {
+            const std::integral_constant<int, 2> kCausal;
+            for (; t + 5 < n; t += 6) {
+                step(kCausal, kB1, t);
+                step(kCausal, kB2, t + 1);
+                step(kCausal, kB3, t + 2);
+                step(kCausal, kB4, t + 3);
+                step(kCausal, kB5, t + 4);
+                step(kCausal, kB0, t + 5);
+            }
+            if (t < n) {
+                step(kCausal, kB1, t);
+                if (t + 1 < n) {
+                    step(kCausal, kB2, t + 1);
+                    if (t + 2 < n) {
+                        step(kCausal, kB3, t + 2);
+                        if (t + 3 < n) {
+                            step(kCausal, kB4, t + 3);
+                            if (t + 4 < n)
+                                step(kCausal, kB5, t + 4);
+                        }
+                    }
+                }
+            }
+            t = n;
         }
         for (; t < t_mask; ++t)
             step(kFull, t, t);
