@@ -362,47 +362,67 @@ __device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights &pw
     }
 }
 
-// Workspace image of the values: one workgroup per (32-key stage, batch *
-// head).  Keys 32s .. 32s+31 (zeros past L) are converted to float16 and
-// transposed through LDS into [d features][32 positions], position
-// vt_pos(key), and written in the prefill's swizzled LDS slot order, so
-// that the prefill moves each stage into LDS with plain 16-byte copies.
-// The conversion and transposition happen once per key instead of once per
+// Workspace image of the values.  For each 32-key stage (keys 32s .. 32s+31,
+// zeros past L) of each (batch, head): float16 values transposed to [d
+// features][32 positions], key j at position vt_pos(j), each feature row's
+// four 16-byte chunks in the prefill's swizzled LDS slot order, so that the
+// prefill moves each stage into LDS with plain 16-byte copies.  The
+// conversion and transposition happen once per key instead of once per
 // query tile.
+//
+// A thread owns 8 keys x 8 features: the keys that fill positions 8G ..
+// 8G+7 (4G..4G+3 and 16+4G..16+4G+3) and features 8fg .. 8fg+7.  It loads
+// the 8 key rows' 16-byte pieces (adjacent fg on adjacent lanes, so each key
+// row is read contiguously), converts, transposes the 8 x 8 block in
+// registers and stores 8 feature rows' chunk G.  No LDS, no barrier.
 template <int D>
 __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
-    constexpr int TP = BN + 8;  // LDS row pitch (halves): 16-byte aligned rows
-    __shared__ __attribute__((aligned(16))) uint16_t T[D * TP];
-    const int s = blockIdx.x;
+    constexpr int FG = D / 8;          // feature groups
+    constexpr int TPS = 4 * FG;        // threads per stage
+    constexpr int SPB = 256 / TPS;     // stages per block
+    constexpr int SPW = 64 / TPS;      // stages per wavefront (1 or 2)
+    const int li = threadIdx.x % TPS;
+    const int G = li / FG;
+    const int fg = li % FG;
+    const int s = blockIdx.x * SPB + threadIdx.x / TPS;
+    // First stage of this wavefront: the buffer resource starts there, so
+    // it is uniform and offsets stay small for any row stride.
+    const int s_wave = blockIdx.x * SPB + (threadIdx.x / 64) * SPW;
+    if (s_wave >= a.n_st)
+        return;
     const int j0 = s * BN;
+    const int jw = s_wave * BN;
     for (int bh = blockIdx.y; bh < a.B * a.H; bh += gridDim.y) {
         const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
         const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h;
-        for (int c = threadIdx.x; c < BN * (D / 8); c += blockDim.x) {
-            const int key = c / (D / 8);
-            const int col = (c % (D / 8)) * 8;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (j0 + key < a.L)
-                x = ldg16(vb + (int64_t)(j0 + key) * a.v_l + col);
-            const int pos = vt_pos(key);
+        const __amdgpu_buffer_rsrc_t rv =
+            make_rsrc(vb + (int64_t)jw * a.v_l, rows_bytes(jw, a.L, a.v_l, D));
+        uint32_t hv[8][4];  // [key k][feature pair]: f16x2 bits
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const uint32_t w = x[e2];
-                const uint32_t bits =
-                    __builtin_bit_cast(uint32_t, cvt_f16x2(bf16_lo(w), bf16_hi(w)));
-                T[(col + 2 * e2) * TP + pos] = (uint16_t)(bits & 0xffffu);
-                T[(col + 2 * e2 + 1) * TP + pos] = (uint16_t)(bits >> 16);
-            }
+        for (int k = 0; k < 8; ++k) {
+            const int key = j0 - jw + (k < 4 ? 4 * G + k : 16 + 4 * G + (k - 4));
+            const u32x4 x = bufld16(rv, (uint32_t)(key * a.v_l * 2 + 16 * fg));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hv[k][i] = __builtin_bit_cast(uint32_t, cvt_f16x2(bf16_lo(x[i]), bf16_hi(x[i])));
         }
-        __syncthreads();
+        if (s >= a.n_st)
+            continue;
         uint16_t *dst = a.vt + ((int64_t)bh * a.n_st + s) * (D * BN);
-        for (int c = threadIdx.x; c < D * (BN / 8); c += blockDim.x) {
-            const int f = c / (BN / 8);
-            const int q = c % (BN / 8);
-            *reinterpret_cast<u32x4 *>(dst + vswz_slot(f, q) * 8) =
-                *reinterpret_cast<const u32x4 *>(&T[f * TP + 8 * q]);
+#pragma unroll
+        for (int cf = 0; cf < 8; ++cf) {
+            // Feature 8fg+cf at positions 8G .. 8G+7: half cf%2 of word cf/2
+            // of keys k = 0..7.
+            u32x4 out;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const uint32_t lo = hv[2 * pp][cf / 2], hi = hv[2 * pp + 1][cf / 2];
+                out[pp] = (cf & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                                   : ((lo & 0xffffu) | (hi << 16));
+            }
+            const int f = 8 * fg + cf;
+            *reinterpret_cast<u32x4 *>(dst + vswz_slot(f, G) * 8) = out;
         }
-        __syncthreads();
     }
 }
 
@@ -785,7 +805,8 @@ template <int D>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     FwdArgs args = a;
     void *params[] = {&args};
-    const dim3 pgrid((unsigned)a.n_st, (unsigned)min(a.B * a.H, 65535));
+    constexpr int SPB = 256 / (4 * (D / 8));  // stages per prepass block
+    const dim3 pgrid((unsigned)((a.n_st + SPB - 1) / SPB), (unsigned)min(a.B * a.H, 65535));
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&parallax_vprep_kernel<D>),
                                    pgrid, dim3(256), params, 0, stream);
     if (e != hipSuccess)
