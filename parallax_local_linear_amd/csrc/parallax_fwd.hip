@@ -155,16 +155,19 @@ __device__ __forceinline__ void pin(const T &x) {
     asm volatile("" ::"v"(x));
 }
 
-// Workgroup barrier between ping-pong phases: this wave's LDS operations
-// complete first.  The scheduler may not move anything across it.
+// Workgroup barrier between ping-pong phases.  With WAIT_LDS, this wave's
+// LDS reads complete first (needed where another wave's next copy reuses
+// the buffer just read).  The scheduler may not move anything across it.
 // No memory fence: a fence would also wait for the copies into LDS that
 // are meant to stay in flight across phases (their completion is waited
 // for explicitly, see wait_copies).  The empty asm statements keep the
 // compiler from moving memory accesses across the barrier.
+template <bool WAIT_LDS = true>
 __device__ __forceinline__ void phase_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (WAIT_LDS)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -656,10 +659,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         copy(t + AHEAD, b0 + AHEAD);
         wait_copies<IN_FLIGHT * C::COPIES>();
     };
-    // One step: M phase, barrier, V phase, barrier.
+    // One step: M phase, barrier, V phase, barrier.  The M phase's K reads
+    // need no wait at its barrier: they feed this wave's next M phase, and
+    // their buffer is refilled two phases after that.  The V phase's reads
+    // do: the other group's next copy reuses that buffer.
     auto step = [&](auto masked, auto b0, int t) __attribute__((always_inline)) {
         mphase(masked, b0, t, true);
-        phase_barrier();
+        phase_barrier<false>();
         vphase(b0, t);
         phase_barrier();
     };
@@ -705,7 +711,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             if (!offsets_set)
                 offsets_set = init_offsets<D>(cx, sc, c);
         }
-        phase_barrier();
+        phase_barrier<false>();
         vphase(kB0, 0);
         phase_barrier();
         // The main loop runs NBUF steps per iteration (t = 1 mod 6), which
