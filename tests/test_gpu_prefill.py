@@ -86,6 +86,21 @@ SMALL = [
 ]
 
 
+# Causal tiles end with 2 to 9 steps after the main loop (their remaining
+# full stages and the diagonal), taken as whole groups of six plus a partial
+# group.  These lengths give tiles with each of those counts (2: L=257,
+# 3: 289, 4: 129, 5: 161, 6: 193, 7: 225, 8: 449, 9: 481), from the stage
+# schedule: 32-key stages, 128-row tiles, fully visible stages first.
+TAIL_LENGTHS = [129, 161, 193, 225, 257, 289, 449, 481]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_tail_step_counts(orc, d):
+    for i, L in enumerate(TAIL_LENGTHS):
+        q, k, v, r = (rand((1, 1, L, d), 60 + 4 * i + j) for j in range(4))
+        full_check(orc, q, k, v, r, what="causal tail L=%d d=%d" % (L, d))
+
+
 @pytest.mark.parametrize("B,H,L,d,window,n_sink", SMALL)
 def test_small_shapes(orc, B, H, L, d, window, n_sink):
     seed = B * 1000003 + H * 10007 + L * 101 + d + window * 7 + n_sink
