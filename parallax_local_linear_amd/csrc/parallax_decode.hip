@@ -113,11 +113,14 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_kernel(DecodeArgs a) 
             make_rsrc(vb + (int64_t)(j - start) * a.v_l, rows_bytes(j, end, a.v_l, D));
         u32x4 kw[U], vw[U];
         bool valid[U];
+        // The cache is read once per call: non-temporal loads (nt) keep it
+        // from displacing other data in L2 and the MALL.
+        constexpr int kNonTemporal = 2;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             valid[u] = j + u * KPS + grp < end;
-            kw[u] = __builtin_amdgcn_raw_buffer_load_b128(ks, (int)koff, (int)(u * kstep), 0);
-            vw[u] = __builtin_amdgcn_raw_buffer_load_b128(vs, (int)voff, (int)(u * vstep), 0);
+            kw[u] = __builtin_amdgcn_raw_buffer_load_b128(ks, (int)koff, (int)(u * kstep), kNonTemporal);
+            vw[u] = __builtin_amdgcn_raw_buffer_load_b128(vs, (int)voff, (int)(u * vstep), kNonTemporal);
         }
         float x[U], sr[U];
 #pragma unroll
