@@ -121,6 +121,33 @@ def test_scaled_inputs_and_custom_scale(orc):
     full_check(orc, q, k, v, r, scale=0.3, what="custom scale 0.3")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_scores_rising_late(orc, d):
+    """Keys whose scores grow along the sequence (about 25 log2 units from the
+    first to the last key): each row's softmax offset, fixed from its first
+    stage plus a margin of 3, is overtaken by more than 5 for most rows, so
+    the workgroups recompute with the exact row max.  The data is checked to
+    have that property before the kernel is compared with the oracle."""
+    L = 512
+    g = torch.Generator().manual_seed(4321 + d)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    ramp = 46.0 * (d / 64) ** 0.5 * torch.arange(L, dtype=torch.float32) / L
+    q = (3.0 * u + 0.1 * torch.randn(1, 1, L, d, generator=g)).to(torch.bfloat16)
+    k = (ramp[:, None] * u + 0.1 * torch.randn(1, 1, L, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(1, 1, L, d, generator=g).to(torch.bfloat16)
+    # Probe scores |rho . k| stay below about 60 here: the O error of the f16
+    # value path grows with them, and this case is about the offsets.
+    r = (0.25 * torch.randn(1, 1, L, d, generator=g)).to(torch.bfloat16)
+    scale = default_scale(d)
+    x = (f64(q)[0, 0] @ f64(k)[0, 0].T) * scale * np.log2(np.e)
+    rows = np.arange(32, L)
+    first = x[rows, :32].max(axis=1)
+    last = np.array([x[i, :i + 1].max() for i in rows])
+    assert (last > first + 3 + 5).mean() > 0.5, "the data must overtake the first-stage offsets"
+    full_check(orc, q, k, v, r, what="scores rising late d=%d" % d)
+
+
 @pytest.mark.parametrize("cfg", [workloads.PREFILL_06B, workloads.PREFILL_17B, workloads.LOCAL],
                          ids=lambda c: c.name)
 def test_full_size_sampled_rows(orc, cfg):
