@@ -228,3 +228,21 @@ def test_64bit_offsets(orc):
                                   scale, 0, 0)
         compare(f64(o[0, 1, i:i + 1]), f64(lse[0, 1, i:i + 1]), o_ref, lse_ref,
                 "64-bit offsets row %d" % i)
+
+
+def test_many_slices(orc):
+    """B*H above 65535 (the prepass's grid then loops over slices): short
+    sequences, every output finite, and whole slices on both sides of that
+    bound against the oracle."""
+    B, H, L, d = 2, 33000, 40, 64
+    say("[case] many slices B=%d H=%d L=%d d=%d" % (B, H, L, d))
+    q, k, v, r = (workloads.random_tensor((B, H, L, d), 1400 + t, device=DEV) for t in range(4))
+    o0, l0 = nan_outputs(q)
+    o, lse = parallax_attn_fwd(q, k, v, r, out=o0, lse=l0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    scale = default_scale(d)
+    for b, h in ((0, 0), (0, 32999), (1, 32534), (1, 32535), (1, 32999)):
+        rows = list(range(L))
+        o_ref, lse_ref = oracle_rows(orc, q, k, v, r, b, h, rows, scale)
+        compare(f64(o[b, h]), f64(lse[b, h]), o_ref, lse_ref, "many slices b=%d h=%d" % (b, h))
