@@ -8,7 +8,9 @@ The oracle computes the Parallax forward from its definition (review page
 "Parallax: Parameterized Local Linear Attention for Language Modeling",
 sec. 1 and sec. 3): softmax weights over the visible keys, the weighted key
 mean, the probe correction rho.(k_j - kbar) and the corrected weighted sum of
-values, all in fp64.  Everything here converts arrays to contiguous float64
+values, all in fp64; and its backward (the gradients of a loss through o with
+respect to q, k, v and rho) by reverse-mode steps of the same definition.
+Everything here converts arrays to contiguous float64
 and calls the C code; no arithmetic of the method lives in this file.
 """
 from __future__ import annotations
@@ -46,7 +48,8 @@ class Oracle:
     """ctypes handle on one build of the oracle library."""
 
     def __init__(self, path: str = LIBRARY):
-        if not os.path.exists(path):
+        if not os.path.exists(path) or (
+                path == LIBRARY and os.path.getmtime(SOURCE) > os.path.getmtime(path)):
             build(path)
         self.path = path
         lib = ctypes.CDLL(path)
@@ -57,6 +60,10 @@ class Oracle:
         lib.parallax_oracle_fwd.restype = ctypes.c_int
         lib.parallax_oracle_fwd.argtypes = [
             _D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            ctypes.c_int, ctypes.c_double, ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        lib.parallax_oracle_bwd.restype = ctypes.c_int
+        lib.parallax_oracle_bwd.argtypes = [
+            _D, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
             ctypes.c_int, ctypes.c_double, ctypes.c_long, ctypes.c_long, ctypes.c_int]
         lib.parallax_oracle_decode.restype = ctypes.c_int
         lib.parallax_oracle_decode.argtypes = [
@@ -90,6 +97,26 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return o, lse
+
+    def bwd(self, q, k, v, r, dout, scale=None, window=0, n_sink=0, nthreads=None):
+        """Prefill backward on [B,H,L,d] arrays: gradients of a loss through o
+        (dout = dLoss/do; lse carries none).  Returns (dq, dk, dv, dr)."""
+        q, k, v, r, dout = (self._f64(x) for x in (q, k, v, r, dout))
+        B, H, L, d = q.shape
+        for x in (k, v, r, dout):
+            if x.shape != q.shape:
+                raise ValueError("q, k, v, r, dout must share one [B,H,L,d] shape")
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        dq, dk, dv, dr = (np.zeros_like(q) for _ in range(4))
+        rc = self.lib.parallax_oracle_bwd(
+            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(r), self._ptr(dout),
+            self._ptr(dq), self._ptr(dk), self._ptr(dv), self._ptr(dr),
+            B, H, L, d, float(scale), int(window), int(n_sink),
+            int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return dq, dk, dv, dr
 
     def rows(self, q_rows, r_rows, pos, k, v, scale, window=0, n_sink=0, nthreads=None):
         """Selected rows of one (batch, head) slice.

@@ -1,6 +1,6 @@
 /*
  * Plain fp64 CPU oracle for the Parallax attention forward (prefill rows and
- * decode rows).
+ * decode rows) and for the prefill backward.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
  * GPU kernels are compared against.  Only the tests, the smoke check and the
@@ -297,4 +297,217 @@ int parallax_oracle_decode(const double *q, const double *r,
         }
     }
     return rc;
+}
+
+/*
+ * Backward of the prefill forward.
+ *
+ * Gradients of a scalar loss that depends on the outputs through o alone
+ * (the log-sum-exp output carries no gradient: dlse = 0), with respect to
+ * q, k, v and the probe rho.  This is reverse-mode differentiation of the
+ * five forward steps of one_row(), taken in reverse order for each query
+ * row i; step (n') is the adjoint of step (n):
+ *
+ *   (5')  u_j = p_j (1 + c_j),  o = sum_j u_j v_j:
+ *           dv_j += u_j dO;          du_j = dO . v_j;
+ *           dp_j  = du_j (1 + c_j);  dc_j = du_j p_j
+ *   (4')  c_j = rho . (k_j - kbar):
+ *           drho += sum_j dc_j (k_j - kbar);  dk_j += dc_j rho;
+ *           dkbar = -(sum_j dc_j) rho
+ *   (3')  kbar = sum_j p_j k_j:
+ *           dp_j += dkbar . k_j;     dk_j += p_j dkbar
+ *   (2')  p = softmax(z) over the visible keys:
+ *           dz_j = p_j (dp_j - sum_l p_l dp_l)
+ *   (1')  z_j = scale q . k_j:
+ *           dq += scale sum_j dz_j k_j;  dk_j += scale dz_j q
+ *
+ * Rows are independent in the forward, so each row's adjoint adds into the
+ * key and value gradients of the keys it sees.  Rows are dealt to the
+ * threads round-robin; each thread keeps its own dk and dv sums, and these
+ * are added in thread order at the end, so a fixed thread count gives a
+ * fixed result.
+ */
+
+/* Adjoint of one row; adds into dk, dv ([n_ctx][d]) and writes dq_i, dr_i.
+ * work: scratch of 4 * n_ctx + 2 * d doubles. */
+static void one_row_bwd(const double *q_i, const double *r_i, const double *do_i, long i,
+                        const double *k, const double *v, long n_ctx, int d,
+                        double scale, long window, long n_sink,
+                        double *dq_i, double *dr_i, double *dk, double *dv, double *work)
+{
+    double *p = work;                 /* softmax weights p_j            */
+    double *c = work + n_ctx;         /* correction coefficients c_j    */
+    double *dp = work + 2 * n_ctx;    /* adjoint of p_j                 */
+    double *dc = work + 3 * n_ctx;    /* adjoint of c_j                 */
+    double *kbar = work + 4 * n_ctx;
+    double *dkbar = kbar + d;
+
+    for (int t = 0; t < d; ++t)
+        dq_i[t] = dr_i[t] = 0.0;
+
+    /* forward steps (1)-(4) again: scores, weights, key mean, corrections */
+    double m = -INFINITY;
+    long n_vis = 0;
+    for (long j = 0; j < n_ctx; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+        p[j] = scale * dot(q_i, k + j * (long)d, d);
+        if (p[j] > m)
+            m = p[j];
+        ++n_vis;
+    }
+    if (n_vis == 0)
+        return;
+    double ell = 0.0;
+    for (long j = 0; j < n_ctx; ++j)
+        if (visible(i, j, window, n_sink)) {
+            p[j] = exp(p[j] - m);
+            ell += p[j];
+        }
+    for (long j = 0; j < n_ctx; ++j)
+        if (visible(i, j, window, n_sink))
+            p[j] /= ell;
+    for (int t = 0; t < d; ++t)
+        kbar[t] = 0.0;
+    for (long j = 0; j < n_ctx; ++j)
+        if (visible(i, j, window, n_sink))
+            for (int t = 0; t < d; ++t)
+                kbar[t] += p[j] * k[j * (long)d + t];
+    for (long j = 0; j < n_ctx; ++j)
+        if (visible(i, j, window, n_sink)) {
+            double s = 0.0;
+            for (int t = 0; t < d; ++t)
+                s += r_i[t] * (k[j * (long)d + t] - kbar[t]);
+            c[j] = s;
+        }
+
+    /* (5') */
+    for (long j = 0; j < n_ctx; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+#if ORACLE_MUTANT == 14
+        /* planted mistake: value gradient without the probe correction */
+        double u = p[j];
+#else
+        double u = p[j] * (1.0 + c[j]);
+#endif
+        for (int t = 0; t < d; ++t)
+            dv[j * (long)d + t] += u * do_i[t];
+        double du = dot(do_i, v + j * (long)d, d);
+        dp[j] = du * (1.0 + c[j]);
+        dc[j] = du * p[j];
+    }
+
+    /* (4') */
+    double sum_dc = 0.0;
+    for (long j = 0; j < n_ctx; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+        const double *kj = k + j * (long)d;
+        for (int t = 0; t < d; ++t) {
+#if ORACLE_MUTANT == 15
+            /* planted mistake: probe gradient not centred on kbar */
+            dr_i[t] += dc[j] * kj[t];
+#else
+            dr_i[t] += dc[j] * (kj[t] - kbar[t]);
+#endif
+            dk[j * (long)d + t] += dc[j] * r_i[t];
+        }
+        sum_dc += dc[j];
+    }
+    for (int t = 0; t < d; ++t)
+#if ORACLE_MUTANT == 12
+        /* planted mistake: adjoint of the key mean with the wrong sign */
+        dkbar[t] = sum_dc * r_i[t];
+#else
+        dkbar[t] = -sum_dc * r_i[t];
+#endif
+
+    /* (3') */
+    for (long j = 0; j < n_ctx; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+        dp[j] += dot(dkbar, k + j * (long)d, d);
+#if ORACLE_MUTANT != 16
+        for (int t = 0; t < d; ++t)
+            dk[j * (long)d + t] += p[j] * dkbar[t];
+#endif
+    }
+
+    /* (2') */
+    double mean_dp = 0.0;
+    for (long j = 0; j < n_ctx; ++j)
+        if (visible(i, j, window, n_sink))
+            mean_dp += p[j] * dp[j];
+#if ORACLE_MUTANT == 11
+    /* planted mistake: softmax adjoint without its mean term */
+    mean_dp = 0.0;
+#endif
+
+    /* (1'), with dz_j formed on the fly */
+    for (long j = 0; j < n_ctx; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+        double dz = p[j] * (dp[j] - mean_dp);
+        const double *kj = k + j * (long)d;
+        for (int t = 0; t < d; ++t) {
+#if ORACLE_MUTANT == 13
+            /* planted mistake: query gradient without the softmax scale */
+            dq_i[t] += dz * kj[t];
+#else
+            dq_i[t] += scale * dz * kj[t];
+#endif
+            dk[j * (long)d + t] += scale * dz * q_i[t];
+        }
+    }
+}
+
+/*
+ * Whole prefill backward over contiguous [B][H][L][d] tensors.
+ *   q, k, v, r : forward inputs;  dout: gradient of the loss w.r.t. o
+ *   dq, dk, dv, dr: outputs, same shape.
+ * Returns 0, -1 on an invalid argument, -2 when scratch memory is short.
+ */
+int parallax_oracle_bwd(const double *q, const double *k, const double *v,
+                        const double *r, const double *dout,
+                        double *dq, double *dk, double *dv, double *dr,
+                        long B, long H, long L, int d,
+                        double scale, long window, long n_sink, int nthreads)
+{
+    if (B < 0 || H < 0 || L < 0 || d <= 0 || n_sink < 0)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    const long sz = L * (long)d;
+    double *acc = (double *)calloc((size_t)nthreads * (size_t)(2 * sz) + 1, sizeof(double));
+    double *work = (double *)malloc(sizeof(double) * (size_t)nthreads * (size_t)(4 * L + 2 * d + 1));
+    int failed = !acc || !work;
+    for (long bh = 0; bh < B * H && !failed; ++bh) {
+        const long off = bh * sz;
+        memset(acc, 0, sizeof(double) * (size_t)nthreads * (size_t)(2 * sz));
+#pragma omp parallel for num_threads(nthreads) schedule(static, 1)
+        for (long i = 0; i < L; ++i) {
+            int tid = 0;
+#ifdef _OPENMP
+            tid = omp_get_thread_num();
+#endif
+            double *a = acc + (size_t)tid * (size_t)(2 * sz);
+            one_row_bwd(q + off + i * d, r + off + i * d, dout + off + i * d, i,
+                        k + off, v + off, L, d, scale, window, n_sink,
+                        dq + off + i * d, dr + off + i * d, a, a + sz,
+                        work + (size_t)tid * (size_t)(4 * L + 2 * d + 1));
+        }
+        for (long e = 0; e < sz; ++e) {
+            double sk = 0.0, sv = 0.0;
+            for (int t = 0; t < nthreads; ++t) {
+                sk += acc[(size_t)t * (size_t)(2 * sz) + e];
+                sv += acc[(size_t)t * (size_t)(2 * sz) + sz + e];
+            }
+            dk[off + e] = sk;
+            dv[off + e] = sv;
+        }
+    }
+    free(acc);
+    free(work);
+    return failed ? -2 : 0;
 }

@@ -16,7 +16,10 @@ Facts used (none of them re-types the oracle's own two-pass algorithm):
     parameterises), solved by numpy.linalg.lstsq;
   * closed forms: a single visible key gives o = v, lse = scale q.k;
   * invariants: key translation, value affinity, linearity in rho;
-  * a hand-worked example with exact rational results (tests/golden).
+  * a hand-worked example with exact rational results (tests/golden);
+  * backward: central differences of the (pinned) forward, torch's autograd
+    of softmax attention at rho = 0, and exact identities (key translation,
+    value shift, linearity in V, affinity in rho).
 Sources: review page "Parallax: Parameterized Local Linear Attention for
 Language Modeling", sec. 1-3; tilnote note on Parallax, section on Local
 Linear Attention as the starting point; "Sliding-window beats linear
@@ -221,6 +224,115 @@ def pin_decode(orc):
         _close(lse[b], lse2[0, :, n - 1], what="decode lse b=%d" % b)
 
 
+# ---------------------------------------------------------------------------
+# Backward.  The loss is Lambda = sum dO . o (so dO is dLambda/do); lse takes
+# no part in it.  The pins below use the forward oracle (itself pinned above)
+# through finite differences, torch's autograd of softmax attention, and four
+# exact identities of the method.
+
+BWD_MASKS = [(0, 0), (3, 1), (2, 3), (1, 0)]
+
+
+def _loss(orc, q, k, v, r, dout, **kw):
+    o, _ = orc.fwd(q, k, v, r, nthreads=1, **kw)
+    return float(np.sum(o * dout))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient element equals the central difference of the forward.
+
+    h = 1e-5 in fp64: the truncation error (h^2 times a third derivative of
+    order one) and the rounding error (1e-16 / h) both stay below 1e-8.
+    """
+    B, H, L, d = 1, 2, 7, 4
+    for seed, (window, n_sink) in enumerate(BWD_MASKS):
+        ins = [_rand((B, H, L, d), 200 + 10 * seed + t) for t in range(5)]
+        q, k, v, r, dout = ins
+        kw = dict(scale=0.6, window=window, n_sink=n_sink)
+        grads = orc.bwd(q, k, v, r, dout, nthreads=1, **kw)
+        h = 1e-5
+        for x_idx, (name, g) in enumerate(zip("qkvr", grads)):
+            fd = np.zeros_like(g)
+            for e in np.ndindex(*g.shape):
+                xs = [a.copy() for a in (q, k, v, r)]
+                xs[x_idx][e] += h
+                up = _loss(orc, *xs, dout, **kw)
+                xs[x_idx][e] -= 2 * h
+                dn = _loss(orc, *xs, dout, **kw)
+                fd[e] = (up - dn) / (2 * h)
+            _close(g, fd, tol=1e-7, what="d%s vs finite differences W=%d S=%d"
+                   % (name, window, n_sink))
+
+
+def pin_bwd_directional(orc):
+    """Directional derivatives on larger slices (several tiles of keys)."""
+    B, H, L, d = 2, 1, 33, 16
+    for seed, (window, n_sink) in enumerate(((0, 0), (8, 2), (5, 0))):
+        q, k, v, r, dout = (_rand((B, H, L, d), 300 + 10 * seed + t) for t in range(5))
+        kw = dict(scale=d ** -0.5, window=window, n_sink=n_sink)
+        grads = orc.bwd(q, k, v, r, dout, **kw)
+        h = 1e-5
+        for x_idx, (name, g) in enumerate(zip("qkvr", grads)):
+            u = _rand(g.shape, 400 + 10 * seed + x_idx)
+            xs = [a.copy() for a in (q, k, v, r)]
+            xs[x_idx] += h * u
+            up = _loss(orc, *xs, dout, **kw)
+            xs[x_idx] -= 2 * h * u
+            dn = _loss(orc, *xs, dout, **kw)
+            fd = (up - dn) / (2 * h)
+            got = float(np.sum(g * u))
+            assert abs(got - fd) <= 1e-7 * (1.0 + abs(fd)), \
+                "d%s along a direction: %.12g vs %.12g (W=%d S=%d)" % (name, got, fd, window, n_sink)
+
+
+def pin_bwd_softmax_case(orc):
+    """rho = 0: dq, dk, dv equal torch's autograd of softmax attention (fp64)."""
+    import torch
+    import torch.nn.functional as F
+    B, H, L, d = 1, 2, 13, 8
+    for seed, (window, n_sink) in enumerate(MASKS):
+        q, k, v, dout = (_rand((B, H, L, d), 500 + 5 * seed + t) for t in range(4))
+        scale = d ** -0.5
+        dq, dk, dv, _ = orc.bwd(q, k, v, np.zeros_like(q), dout, scale=scale,
+                                window=window, n_sink=n_sink)
+        mask = torch.from_numpy(visible_mask(L, window, n_sink))
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+        o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+        o.backward(torch.from_numpy(dout))
+        for name, a, t in (("dq", dq, tq), ("dk", dk, tk), ("dv", dv, tv)):
+            _close(a, t.grad.numpy(), what="%s vs autograd SDPA W=%d S=%d" % (name, window, n_sink))
+
+
+def pin_bwd_identities(orc):
+    """Four exact identities of the method.
+
+    * Translating every key by u leaves o unchanged (the scores move by
+      scale q.u for all keys of a row, and k_j - kbar is unchanged), so the
+      key gradients of a slice sum to zero.
+    * sum_j p_j (1 + c_j) = 1, so adding w to every value adds w to every
+      output: the value gradients sum to the output gradients.
+    * o is linear in V, so sum_j dv_j . v_j = sum_i dO_i . o_i.
+    * o is affine in rho, so sum_i drho_i . rho_i = sum_i dO_i . (o_i - o_i|rho=0).
+    """
+    B, H, L, d = 1, 3, 64, 8
+    for seed, (window, n_sink) in enumerate(((0, 0), (16, 4), (7, 0))):
+        q, k, v, r, dout = (_rand((B, H, L, d), 600 + 10 * seed + t) for t in range(5))
+        kw = dict(scale=0.4, window=window, n_sink=n_sink)
+        dq, dk, dv, dr = orc.bwd(q, k, v, r, dout, **kw)
+        o, _ = orc.fwd(q, k, v, r, **kw)
+        o0, _ = orc.fwd(q, k, v, np.zeros_like(r), **kw)
+        tag = " W=%d S=%d" % (window, n_sink)
+        mag = np.abs(dk).sum(axis=2)
+        assert np.all(np.abs(dk.sum(axis=2)) <= 1e-11 * (1.0 + mag)), "sum of dk" + tag
+        _close(dv.sum(axis=2), dout.sum(axis=2), tol=1e-11, what="sum of dv" + tag)
+        _close(np.sum(dv * v, axis=(2, 3)), np.sum(dout * o, axis=(2, 3)), tol=1e-11,
+               what="dv . v" + tag)
+        _close(np.sum(dr * r, axis=(2, 3)), np.sum(dout * (o - o0), axis=(2, 3)), tol=1e-11,
+               what="drho . rho" + tag)
+
+
 ALL_PINS = [pin_closed_form, pin_softmax_special_case, pin_local_linear_fit,
             pin_single_key, pin_key_translation, pin_value_affine, pin_rho_linearity,
-            pin_masks, pin_golden, pin_decode]
+            pin_masks, pin_golden, pin_decode,
+            pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_softmax_case,
+            pin_bwd_identities]

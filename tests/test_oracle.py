@@ -8,7 +8,7 @@ import pytest
 import oracle
 from oracle_pins import ALL_PINS
 
-N_MUTANTS = 10
+N_MUTANTS = 16
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -58,3 +58,24 @@ def test_thread_count_does_not_change_result(orc):
     b = orc.fwd(q, k, v, r, nthreads=max(2, os.cpu_count() or 2))
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_backward_thread_count(orc):
+    """Backward: row gradients are exact per row; key and value gradients are
+    sums whose order depends on the thread count only (fixed count: fixed result)."""
+    rng = np.random.default_rng(7)
+    q, k, v, r, do = (rng.standard_normal((1, 2, 64, 16)) for _ in range(5))
+    a = orc.bwd(q, k, v, r, do, window=9, n_sink=2, nthreads=1)
+    b = orc.bwd(q, k, v, r, do, window=9, n_sink=2, nthreads=3)
+    c = orc.bwd(q, k, v, r, do, window=9, n_sink=2, nthreads=3)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[3], b[3])
+    for x, y, z in zip(a, b, c):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(y, z)
+
+
+def test_backward_rejects_bad_shapes(orc):
+    x = np.zeros((1, 1, 4, 2))
+    with pytest.raises(ValueError):
+        orc.bwd(x, x, x, x, np.zeros((1, 1, 4, 3)))
