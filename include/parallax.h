@@ -118,6 +118,77 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
                                   void *stream);
 
 /*
+ * Prefill forward for training: parallax_attn_fwd plus two saved
+ * quantities that parallax_attn_bwd needs (same arguments otherwise).
+ *
+ *   sbar : fp32 [B, H, L] contiguous (4-byte aligned): sbar_i =
+ *          sum_j p_ij rho_i . k_j, the softmax-weighted mean of the probe
+ *          scores (so that rho_i . (k_j - kbar_i) = rho_i . k_j - sbar_i).
+ *   pv   : fp32 [B, H, L, d] contiguous (16-byte aligned): pv_i =
+ *          sum_j p_ij v_j, the plain softmax-attention output of row i.
+ *
+ * o and lse are bit-identical to those of parallax_attn_fwd.
+ */
+parallax_status parallax_attn_fwd_train(const void *q, const void *k, const void *v,
+                                        const void *r, float *o, float *lse, float *sbar,
+                                        float *pv, int B, int H, int L, int d,
+                                        parallax_strides sq, parallax_strides sk,
+                                        parallax_strides sv, parallax_strides sr,
+                                        parallax_strides so, float softmax_scale, int window,
+                                        int n_sink, void *workspace, size_t workspace_bytes,
+                                        void *stream);
+
+/*
+ * Bytes of device workspace parallax_attn_bwd needs: per (b, h) and 32-row
+ * stage, 512 bytes of row statistics plus four bf16 operand images of
+ * 32 * d elements, i.e. B * H * ceil(L / 32) * (512 + 256 * d) bytes (0 when
+ * B, H or L is 0, or for sizes parallax_attn_bwd would reject).
+ */
+size_t parallax_attn_bwd_workspace_size(int B, int H, int L, int d);
+
+/*
+ * Prefill backward: gradients of a scalar loss through o (lse carries no
+ * gradient) with respect to q, k, v and the probe r.  With
+ * s_ij = rho_i . k_j, t_ij = 1 + s_ij - sbar_i, g_ij = dout_i . v_j,
+ * G_i = dout_i . pv_i and Y_i = dout_i . o_i (review page "Parallax:
+ * Parameterized Local Linear Attention for Language Modeling", sec. 1 and
+ * sec. 3 define the forward; this is its derivative):
+ *
+ *     dv_j   = sum_i p_ij t_ij dout_i
+ *     dS_ij  = p_ij (g_ij - G_i)
+ *     dZ_ij  = p_ij ((g_ij - G_i) t_ij + G_i - Y_i)
+ *     dq_i   = scale sum_j dZ_ij k_j          dr_i = sum_j dS_ij k_j
+ *     dk_j   = scale sum_i dZ_ij q_i + sum_i dS_ij r_i
+ *
+ * over the same visible pairs as the forward.
+ *
+ *   q, k, v, r : the forward's bf16 inputs (same rules as parallax_attn_fwd).
+ *   dout       : bf16 [B, H, L, d] with strides sdo: gradient of the loss
+ *                with respect to o.
+ *   o, lse, sbar, pv : the outputs of parallax_attn_fwd_train for these
+ *                inputs, all contiguous (o 16-byte aligned).
+ *   dq, dk, dv, dr : fp32 [B, H, L, d] contiguous, 16-byte aligned, written
+ *                in full (no accumulation into existing contents).
+ *   softmax_scale, window, n_sink : as passed to the forward.
+ *   workspace  : at least parallax_attn_bwd_workspace_size(B, H, L, d)
+ *                bytes, 256-byte aligned; scratch after the call.
+ *
+ * Four kernels run on `stream`: row statistics, transposed operand images,
+ * then dk/dv and dq/dr.  With window > 0 and n_sink > 0 the rows past the
+ * window add into the sink keys' dk and dv with float atomics, so those
+ * rows of dk and dv can differ from run to run by rounding; everything
+ * else is deterministic.
+ */
+parallax_status parallax_attn_bwd(const void *q, const void *k, const void *v, const void *r,
+                                  const void *dout, const float *o, const float *lse,
+                                  const float *sbar, const float *pv, float *dq, float *dk,
+                                  float *dv, float *dr, int B, int H, int L, int d,
+                                  parallax_strides sq, parallax_strides sk, parallax_strides sv,
+                                  parallax_strides sr, parallax_strides sdo,
+                                  float softmax_scale, int window, int n_sink, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * Decode step: one query (and probe) per sequence against a contiguous KV
  * cache.  A decoding Parallax model reads a KV cache like softmax attention
  * does (tilnote note on Parallax, section explaining that it is a different

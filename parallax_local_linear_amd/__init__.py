@@ -1,12 +1,15 @@
-"""Parallax (parameterized Local Linear Attention) forward on AMD MI355X.
+"""Parallax (parameterized Local Linear Attention) forward and backward on AMD MI355X.
 
 The compute path is the gfx950 HIP library ``libparallax.so`` (C ABI in
 ``include/parallax.h``); this package only builds it and marshals torch
 tensors into it.
 """
-from .binding import (EXPORTED, LIBRARY, ParallaxError, load_library, parallax_attn_decode,
-                      parallax_attn_fwd, parallax_attn_fwd_workspace_size,
+from .binding import (EXPORTED, LIBRARY, ParallaxError, load_library, parallax_attn_bwd,
+                      parallax_attn_bwd_workspace_size, parallax_attn_decode, parallax_attn_fwd,
+                      parallax_attn_fwd_train, parallax_attn_fwd_workspace_size,
                       parallax_status_string)
 
-__all__ = ["EXPORTED", "LIBRARY", "ParallaxError", "load_library", "parallax_attn_decode",
-           "parallax_attn_fwd", "parallax_attn_fwd_workspace_size", "parallax_status_string"]
+__all__ = ["EXPORTED", "LIBRARY", "ParallaxError", "load_library", "parallax_attn_bwd",
+           "parallax_attn_bwd_workspace_size", "parallax_attn_decode", "parallax_attn_fwd",
+           "parallax_attn_fwd_train", "parallax_attn_fwd_workspace_size",
+           "parallax_status_string"]

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
                 2: "PARALLAX_ERR_UNSUPPORTED", 3: "PARALLAX_ERR_LAUNCH"}
 
 # Every symbol include/parallax.h declares.
-EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_decode",
+EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_train",
+            "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
             "parallax_status_string")
 
 
@@ -60,6 +61,15 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.parallax_attn_fwd.restype = ctypes.c_int
     lib.parallax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, S, S, S, S, S,
                                       f, i, i, vp, ctypes.c_size_t, vp]
+    lib.parallax_attn_fwd_train.restype = ctypes.c_int
+    lib.parallax_attn_fwd_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                            S, S, S, S, S, f, i, i, vp, ctypes.c_size_t, vp]
+    lib.parallax_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.parallax_attn_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.parallax_attn_bwd.restype = ctypes.c_int
+    lib.parallax_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      i, i, i, i, S, S, S, S, S, f, i, i, vp,
+                                      ctypes.c_size_t, vp]
     lib.parallax_attn_decode.restype = ctypes.c_int
     lib.parallax_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, S, S,
                                          f, i, vp]
@@ -146,6 +156,87 @@ def parallax_attn_fwd(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
         _stream_handle(q.device, stream))
     _check(st)
     return out, lse
+
+
+def _workspace(workspace, nbytes: int, device):
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a device tensor")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def parallax_attn_fwd_train(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
+                            workspace=None, stream=None):
+    """Prefill forward that also saves what the backward needs.
+
+    Returns (o [B,H,L,d], lse [B,H,L], sbar [B,H,L], pv [B,H,L,d]), all fp32
+    and contiguous.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (r, "r")):
+        _need(t, n, torch.bfloat16, 4)
+        if t.shape != q.shape:
+            raise ValueError("q, k, v and r must share one [B,H,L,d] shape")
+    B, H, L, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = torch.empty((B, H, L, d), **f32)
+    lse = torch.empty((B, H, L), **f32)
+    sbar = torch.empty((B, H, L), **f32)
+    pv = torch.empty((B, H, L, d), **f32)
+    lib = load_library()
+    workspace, have = _workspace(workspace, parallax_attn_fwd_workspace_size(B, H, L, d), q.device)
+    st = lib.parallax_attn_fwd_train(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        sbar.data_ptr(), pv.data_ptr(), B, H, L, d, _strides(q), _strides(k), _strides(v),
+        _strides(r), _strides(out), float(softmax_scale), int(window), int(n_sink),
+        workspace.data_ptr(), have, _stream_handle(q.device, stream))
+    _check(st)
+    return out, lse, sbar, pv
+
+
+def parallax_attn_bwd_workspace_size(B: int, H: int, L: int, d: int) -> int:
+    """Bytes of device workspace the backward needs for these sizes."""
+    return int(load_library().parallax_attn_bwd_workspace_size(int(B), int(H), int(L), int(d)))
+
+
+def parallax_attn_bwd(q, k, v, r, dout, o, lse, sbar, pv, *, softmax_scale=None, window=0,
+                      n_sink=0, grads=None, workspace=None, stream=None):
+    """Prefill backward.  q, k, v, r, dout: bf16 [B,H,L,d]; o, lse, sbar, pv from
+    parallax_attn_fwd_train.  Returns (dq, dk, dv, dr), fp32 [B,H,L,d] contiguous
+    (``grads`` may supply the four output tensors)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (r, "r"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+        if t.shape != q.shape:
+            raise ValueError("q, k, v, r and dout must share one [B,H,L,d] shape")
+    B, H, L, d = q.shape
+    for t, n, shape in ((o, "o", (B, H, L, d)), (lse, "lse", (B, H, L)),
+                        (sbar, "sbar", (B, H, L)), (pv, "pv", (B, H, L, d))):
+        _need(t, n, torch.float32, len(shape))
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous fp32 tensor of shape %s" % (n, shape))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if grads is None:
+        grads = tuple(torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+                      for _ in range(4))
+    for t, n in zip(grads, ("dq", "dk", "dv", "dr")):
+        _need(t, n, torch.float32, 4)
+        if tuple(t.shape) != (B, H, L, d) or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous fp32 [B,H,L,d] tensor" % n)
+    dq, dk, dv, dr = grads
+    lib = load_library()
+    workspace, have = _workspace(workspace, parallax_attn_bwd_workspace_size(B, H, L, d), q.device)
+    st = lib.parallax_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), dout.data_ptr(),
+        o.data_ptr(), lse.data_ptr(), sbar.data_ptr(), pv.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dr.data_ptr(), B, H, L, d,
+        _strides(q), _strides(k), _strides(v), _strides(r), _strides(dout),
+        float(softmax_scale), int(window), int(n_sink), workspace.data_ptr(), have,
+        _stream_handle(q.device, stream))
+    _check(st)
+    return dq, dk, dv, dr
 
 
 def parallax_attn_decode(q, r, k_cache, v_cache, seqlens=None, *, softmax_scale=None,

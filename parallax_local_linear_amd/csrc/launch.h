@@ -12,6 +12,8 @@ struct FwdArgs {
     const uint16_t *q, *k, *v, *r;  // bf16 bits, [B,H,L,d] with the strides below
     float *o;                       // [B,H,L,d] with o strides
     float *lse;                     // [B,H,L] contiguous
+    float *sbar;                    // optional [B,H,L] contiguous: sum_j p_ij rho_i.k_j
+    float *pv;                      // optional [B,H,L,d] contiguous: sum_j p_ij v_j
     uint16_t *vt;                   // workspace: f16 bits, [B*H][n_st][d][32] (see below)
     int64_t q_b, q_h, q_l;
     int64_t k_b, k_h, k_l;
@@ -47,12 +49,54 @@ struct DecodeArgs {
     float scale_log2;
 };
 
+struct BwdArgs {
+    const uint16_t *q, *k, *v, *r, *dout;  // bf16 bits, [B,H,L,d] with the strides below
+    const float *o, *lse, *sbar, *pv;      // from the forward, contiguous
+    float *dq, *dk, *dv, *dr;              // [B,H,L,d] contiguous
+    float *stats;                          // workspace, see below
+    uint16_t *img;                         // workspace, see below
+    int64_t q_b, q_h, q_l;
+    int64_t k_b, k_h, k_l;
+    int64_t v_b, v_h, v_l;
+    int64_t r_b, r_h, r_l;
+    int64_t do_b, do_h, do_l;
+    int B, H, L;
+    int n_st;          // ceil(L / 32): 32-row stages per (batch, head)
+    float scale;       // softmax scale
+    int window;        // 0 = none
+    int n_sink;
+    // Key-block work split (see the backward kernels): key blocks below
+    // n_sb hold sink keys; their rows past the window are cut into chunks
+    // of kBwdChunk stages and added into dk and dv atomically.
+    int n_sb;
+    int n_chunks;
+    int zero_rows;     // rows of dk and dv that the first kernel clears
+};
+
+// Backward workspace, per (batch, head) and 32-row stage s:
+//   stats: float [4][32] -- lse*log2(e) (+inf for rows >= L), 1 - sbar,
+//          G = dout.pv, G - dout.o
+//   img:   four bf16 images (q, r, dout, k in that order), each
+//          [B*H][n_st][d/16][64 lanes][8]: rows 4g..4g+3 and 16+4g..16+4g+3
+//          of the stage at feature 16t + m for lane m + 16g of block t
+//          (zeros for rows >= L).
+constexpr int kBwdChunk = 16;
+__host__ __device__ inline size_t bwd_stats_bytes(int64_t BH, int64_t n_st) { return (size_t)(BH * n_st * 128 * 4); }
+__host__ __device__ inline size_t bwd_image_bytes(int64_t BH, int64_t n_st, int d) {
+    return (size_t)(BH * n_st * kStageKeys * d * 2);
+}
+inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
+    const int64_t n_st = (L + kStageKeys - 1) / kStageKeys;
+    return bwd_stats_bytes(B * H, n_st) + 4 * bwd_image_bytes(B * H, n_st, d);
+}
+
 // Prefill workgroup shape: 8 wavefronts of 16 query rows for either feature
 // dimension.
 constexpr int fwd_waves(int) { return 8; }
 constexpr int fwd_block_rows(int d) { return 16 * fwd_waves(d); }
 
 hipError_t launch_fwd(const FwdArgs &a, int d, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int d, int num_splits, hipStream_t stream);
 
 }  // namespace plx

@@ -1,6 +1,7 @@
 // C-ABI entry points of the Parallax library: host-side argument checks,
 // then the kernel launches on the caller's stream.  No allocation, no
 // synchronisation, no global state.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -51,12 +52,16 @@ size_t parallax_attn_fwd_workspace_size(int B, int H, int L, int d) {
     return plx::fwd_workspace_bytes(B, H, L, d);
 }
 
-parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, const void *r,
-                                  float *o, float *lse, int B, int H, int L, int d,
-                                  parallax_strides sq, parallax_strides sk, parallax_strides sv,
-                                  parallax_strides sr, parallax_strides so, float softmax_scale,
-                                  int window, int n_sink, void *workspace,
-                                  size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+parallax_status fwd_common(const void *q, const void *k, const void *v, const void *r, float *o,
+                           float *lse, float *sbar, float *pv, int B, int H, int L, int d,
+                           parallax_strides sq, parallax_strides sk, parallax_strides sv,
+                           parallax_strides sr, parallax_strides so, float softmax_scale,
+                           int window, int n_sink, void *workspace, size_t workspace_bytes,
+                           void *stream, bool train) {
     if (B < 0 || H < 0 || L < 0)
         return PARALLAX_ERR_INVALID_ARG;
     if (d != 64 && d != 128)
@@ -65,10 +70,10 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
         return PARALLAX_ERR_INVALID_ARG;
     if ((int64_t)B * H * L == 0)
         return PARALLAX_OK;
-    if (!q || !k || !v || !r || !o || !lse)
+    if (!q || !k || !v || !r || !o || !lse || (train && (!sbar || !pv)))
         return PARALLAX_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(r, 16) ||
-        !aligned(o, 16) || !aligned(lse, 4))
+        !aligned(o, 16) || !aligned(lse, 4) || !aligned(sbar, 4) || !aligned(pv, 16))
         return PARALLAX_ERR_INVALID_ARG;
     if (!bf16_strides_ok(sq) || !bf16_strides_ok(sk) || !bf16_strides_ok(sv) ||
         !bf16_strides_ok(sr) || !f32_strides_ok(so))
@@ -91,6 +96,8 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
     a.r = static_cast<const uint16_t *>(r);
     a.o = o;
     a.lse = lse;
+    a.sbar = train ? sbar : nullptr;
+    a.pv = train ? pv : nullptr;
     a.vt = static_cast<uint16_t *>(workspace);
     a.q_b = sq.b; a.q_h = sq.h; a.q_l = sq.l;
     a.k_b = sk.b; a.k_h = sk.h; a.k_l = sk.l;
@@ -106,6 +113,122 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
     a.window = window;
     a.n_sink = n_sink;
     hipError_t e = plx::launch_fwd(a, d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, const void *r,
+                                  float *o, float *lse, int B, int H, int L, int d,
+                                  parallax_strides sq, parallax_strides sk, parallax_strides sv,
+                                  parallax_strides sr, parallax_strides so, float softmax_scale,
+                                  int window, int n_sink, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return fwd_common(q, k, v, r, o, lse, nullptr, nullptr, B, H, L, d, sq, sk, sv, sr, so,
+                      softmax_scale, window, n_sink, workspace, workspace_bytes, stream, false);
+}
+
+parallax_status parallax_attn_fwd_train(const void *q, const void *k, const void *v,
+                                        const void *r, float *o, float *lse, float *sbar,
+                                        float *pv, int B, int H, int L, int d,
+                                        parallax_strides sq, parallax_strides sk,
+                                        parallax_strides sv, parallax_strides sr,
+                                        parallax_strides so, float softmax_scale, int window,
+                                        int n_sink, void *workspace, size_t workspace_bytes,
+                                        void *stream) {
+    return fwd_common(q, k, v, r, o, lse, sbar, pv, B, H, L, d, sq, sk, sv, sr, so,
+                      softmax_scale, window, n_sink, workspace, workspace_bytes, stream, true);
+}
+
+size_t parallax_attn_bwd_workspace_size(int B, int H, int L, int d) {
+    if (B < 0 || H < 0 || L < 0 || (d != 64 && d != 128))
+        return 0;
+    return plx::bwd_workspace_bytes(B, H, L, d);
+}
+
+parallax_status parallax_attn_bwd(const void *q, const void *k, const void *v, const void *r,
+                                  const void *dout, const float *o, const float *lse,
+                                  const float *sbar, const float *pv, float *dq, float *dk,
+                                  float *dv, float *dr, int B, int H, int L, int d,
+                                  parallax_strides sq, parallax_strides sk, parallax_strides sv,
+                                  parallax_strides sr, parallax_strides sdo,
+                                  float softmax_scale, int window, int n_sink, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    if (B < 0 || H < 0 || L < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!scale_ok(softmax_scale) || window < 0 || n_sink < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * H * L == 0)
+        return PARALLAX_OK;
+    if (!q || !k || !v || !r || !dout || !o || !lse || !sbar || !pv || !dq || !dk || !dv || !dr)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(r, 16) ||
+        !aligned(dout, 16) || !aligned(o, 16) || !aligned(lse, 4) || !aligned(sbar, 4) ||
+        !aligned(pv, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(dr, 16))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!bf16_strides_ok(sq) || !bf16_strides_ok(sk) || !bf16_strides_ok(sv) ||
+        !bf16_strides_ok(sr) || !bf16_strides_ok(sdo))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!row_stride_ok(sq) || !row_stride_ok(sk) || !row_stride_ok(sv) || !row_stride_ok(sr) ||
+        !row_stride_ok(sdo))
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, 256) ||
+        workspace_bytes < plx::bwd_workspace_bytes(B, H, L, d))
+        return PARALLAX_ERR_INVALID_ARG;
+
+    const int64_t BH = (int64_t)B * H;
+    const int64_t n_st = ((int64_t)L + plx::kStageKeys - 1) / plx::kStageKeys;
+    const int64_t bt = 128;  // rows per workgroup of the backward kernels
+    const int64_t n_kb = ((int64_t)L + bt - 1) / bt;
+    // Key blocks holding sink keys, and the chunks of rows past their window.
+    int64_t n_sb = 0, n_chunks = 0;
+    if (window > 0 && n_sink > 0) {
+        n_sb = (std::min<int64_t>(n_sink, L) + bt - 1) / bt;
+        const int64_t first_past = std::min<int64_t>(n_st, (bt - 1 + window - 1) / 32 + 1);
+        n_chunks = (n_st - first_past + plx::kBwdChunk - 1) / plx::kBwdChunk;
+    }
+    if (BH * (n_kb + n_sb * n_chunks) > INT_MAX || n_st * 32 * d * 2 > INT32_MAX ||
+        n_st * 512 > INT32_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+
+    char *ws = static_cast<char *>(workspace);
+    plx::BwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.r = static_cast<const uint16_t *>(r);
+    a.dout = static_cast<const uint16_t *>(dout);
+    a.o = o;
+    a.lse = lse;
+    a.sbar = sbar;
+    a.pv = pv;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dr = dr;
+    a.stats = reinterpret_cast<float *>(ws);
+    a.img = reinterpret_cast<uint16_t *>(ws + plx::bwd_stats_bytes(BH, n_st));
+    a.q_b = sq.b; a.q_h = sq.h; a.q_l = sq.l;
+    a.k_b = sk.b; a.k_h = sk.h; a.k_l = sk.l;
+    a.v_b = sv.b; a.v_h = sv.h; a.v_l = sv.l;
+    a.r_b = sr.b; a.r_h = sr.h; a.r_l = sr.l;
+    a.do_b = sdo.b; a.do_h = sdo.h; a.do_l = sdo.l;
+    a.B = B;
+    a.H = H;
+    a.L = L;
+    a.n_st = (int)n_st;
+    a.scale = softmax_scale;
+    a.window = window;
+    a.n_sink = n_sink;
+    a.n_sb = (int)n_sb;
+    a.n_chunks = (int)n_chunks;
+    a.zero_rows = (int)std::min<int64_t>(L, n_sb * bt);
+    hipError_t e = plx::launch_bwd(a, d, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
 }
 

@@ -800,6 +800,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         }
         if (G == 0)
             a.lse[(int64_t)bh * L + row] = (cx.m_ref + log2f(ell_t)) * kLn2;
+        // Saved for the backward: sbar = S / ell and pv = A / ell.
+        if (a.pv) {
+            float *pb = a.pv + ((int64_t)bh * L + row) * D;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                f32x4 out;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    out[u] = cx.accA[dt][u] * inv;
+                *reinterpret_cast<f32x4 *>(pb + 16 * dt + 4 * G) = out;
+            }
+            if (G == 0)
+                a.sbar[(int64_t)bh * L + row] = s_t * inv;
+        }
     }
 }
 

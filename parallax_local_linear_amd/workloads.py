@@ -75,6 +75,14 @@ def prefill_inputs(cfg: Prefill, device="cpu", dtype=torch.bfloat16):
     return tuple(out)
 
 
+def prefill_grad(cfg: Prefill, device="cpu", dtype=torch.bfloat16):
+    """Output gradient dO for the backward of a prefill workload: i.i.d.
+    N(0, 1) of shape [B,H,L,d], seeded with 1000 + the workload's number."""
+    g = _gen(device, 1000 + cfg.seed)
+    shape = (cfg.B, cfg.H, cfg.L, cfg.d)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
 def decode_inputs(cfg: Decode, device="cpu", dtype=torch.bfloat16):
     """(q [B,H,d], k_cache [B,H,Lmax,d], v_cache, r [B,H,d]), drawn in that order."""
     g = _gen(device, cfg.seed)

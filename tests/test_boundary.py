@@ -157,6 +157,77 @@ def test_decode_empty_batch_is_a_no_op(lib):
     assert dec(lib, B=0, q=None, r=None, k=None, v=None, o=None, lse=None) == OK
 
 
+def fwd_train(lib, sbar=A16, pv=A16, **kw):
+    args = dict(q=A16, k=A16, v=A16, r=A16, o=A16, lse=A16, B=1, H=2, L=64, d=64,
+                sq=CONTIG, sk=CONTIG, sv=CONTIG, sr=CONTIG, so=CONTIG, scale=0.125, window=0,
+                n_sink=0, ws=A16, ws_bytes=1 << 40)
+    args.update(kw)
+    a = args
+    return lib.parallax_attn_fwd_train(a["q"], a["k"], a["v"], a["r"], a["o"], a["lse"], sbar, pv,
+                                       a["B"], a["H"], a["L"], a["d"], a["sq"], a["sk"], a["sv"],
+                                       a["sr"], a["so"], a["scale"], a["window"], a["n_sink"],
+                                       a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sbar=None), INVALID), (dict(pv=None), INVALID), (dict(pv=A16 + 4), INVALID),
+    (dict(sbar=A16 + 2), INVALID), (dict(d=96), UNSUPPORTED), (dict(q=None), INVALID),
+])
+def test_fwd_train_rejects(lib, kw, status):
+    assert fwd_train(lib, **kw) == status
+
+
+def test_fwd_train_empty_is_a_no_op(lib):
+    assert fwd_train(lib, L=0, sbar=None, pv=None) == OK
+
+
+def expected_bwd_workspace(B, H, L, d):
+    """Per 32-row stage: 512 bytes of row statistics + four bf16 images of 32*d."""
+    return B * H * (-(-L // 32)) * (512 + 4 * 32 * d * 2)
+
+
+@pytest.mark.parametrize("B,H,L,d", [(1, 1, 1, 64), (2, 3, 32, 128), (2, 16, 8192, 128),
+                                     (1, 2, 33, 64)])
+def test_bwd_workspace_size(lib, B, H, L, d):
+    assert binding.parallax_attn_bwd_workspace_size(B, H, L, d) == expected_bwd_workspace(B, H, L, d)
+
+
+@pytest.mark.parametrize("B,H,L,d", [(0, 1, 64, 64), (1, 1, 0, 128), (1, 1, -2, 64),
+                                     (1, 1, 64, 96)])
+def test_bwd_workspace_size_of_empty_or_invalid_is_zero(lib, B, H, L, d):
+    assert binding.parallax_attn_bwd_workspace_size(B, H, L, d) == 0
+
+
+def bwd(lib, **kw):
+    names = ["q", "k", "v", "r", "dout", "o", "lse", "sbar", "pv", "dq", "dk", "dv", "dr"]
+    a = {n: A16 for n in names}
+    a.update(B=1, H=2, L=64, d=64, sq=CONTIG, sk=CONTIG, sv=CONTIG, sr=CONTIG, sdo=CONTIG,
+             scale=0.125, window=0, n_sink=0, ws=A16 * 16, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.parallax_attn_bwd(*[a[n] for n in names], a["B"], a["H"], a["L"], a["d"],
+                                 a["sq"], a["sk"], a["sv"], a["sr"], a["sdo"], a["scale"],
+                                 a["window"], a["n_sink"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(B=-1), INVALID), (dict(L=-1), INVALID),
+    (dict(dout=None), INVALID), (dict(o=None), INVALID), (dict(sbar=None), INVALID),
+    (dict(pv=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
+    (dict(dv=None), INVALID), (dict(dr=None), INVALID), (dict(dout=A16 + 8), INVALID),
+    (dict(dq=A16 + 4), INVALID), (dict(pv=A16 + 4), INVALID), (dict(window=-1), INVALID),
+    (dict(n_sink=-1), INVALID), (dict(scale=0.0), INVALID),
+    (dict(sdo=S(8 * 128 * 64, 128 * 64, 60)), INVALID),
+    (dict(ws=None), INVALID), (dict(ws=A16 * 16 + 16), INVALID),
+    (dict(ws_bytes=expected_bwd_workspace(1, 2, 64, 64) - 1), INVALID),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_empty_is_a_no_op(lib):
+    assert bwd(lib, H=0, q=None, dq=None, ws=None, ws_bytes=0) == OK
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
