@@ -140,9 +140,11 @@ parallax_status parallax_attn_fwd_train(const void *q, const void *k, const void
 
 /*
  * Bytes of device workspace parallax_attn_bwd needs: per (b, h) and 32-row
- * stage, 512 bytes of row statistics plus four bf16 operand images of
- * 32 * d elements, i.e. B * H * ceil(L / 32) * (512 + 256 * d) bytes (0 when
- * B, H or L is 0, or for sizes parallax_attn_bwd would reject).
+ * stage, 512 bytes of row statistics plus nine bf16 operand blocks of
+ * 32 * d elements (q, r, dout row-major and transposed; k row-major and
+ * transposed; v row-major), i.e. B * H * ceil(L / 32) * (512 + 576 * d)
+ * bytes (0 when B, H or L is 0, or for sizes parallax_attn_bwd would
+ * reject).
  */
 size_t parallax_attn_bwd_workspace_size(int B, int H, int L, int d);
 
@@ -173,8 +175,8 @@ size_t parallax_attn_bwd_workspace_size(int B, int H, int L, int d);
  *   workspace  : at least parallax_attn_bwd_workspace_size(B, H, L, d)
  *                bytes, 256-byte aligned; scratch after the call.
  *
- * Four kernels run on `stream`: row statistics, transposed operand images,
- * then dk/dv and dq/dr.  With window > 0 and n_sink > 0 the rows past the
+ * Four kernels run on `stream`: row statistics, operand blocks in the
+ * workspace, then dk/dv and dq/dr.  With window > 0 and n_sink > 0 the rows past the
  * window add into the sink keys' dk and dv with float atomics, so those
  * rows of dk and dv can differ from run to run by rounding; everything
  * else is deterministic.

@@ -6,6 +6,11 @@ p v and p s v.  Exponentials, masked-out work and rescaling are not counted.
 Algorithmic HBM bytes are the inputs read once and the outputs written once.
 Decode counts the same 8d FLOP per cached key; its bytes are dominated by the
 K and V caches.
+
+The backward counts 16d FLOP per visible pair: eight products of 2d FLOP --
+the three score products q.k, rho.k and dO.v (recomputed once), dv, the two
+terms of dk (from q and from rho), dq and drho.  A second recomputation of
+the scores, which the query kernel does, is not counted.
 """
 from __future__ import annotations
 
@@ -31,6 +36,10 @@ def prefill_pairs(cfg: Prefill) -> int:
 
 def prefill_flops(cfg: Prefill) -> int:
     return 8 * cfg.d * prefill_pairs(cfg)
+
+
+def prefill_bwd_flops(cfg: Prefill) -> int:
+    return 16 * cfg.d * prefill_pairs(cfg)
 
 
 def prefill_bytes(cfg: Prefill) -> int:

@@ -54,7 +54,8 @@ struct BwdArgs {
     const float *o, *lse, *sbar, *pv;      // from the forward, contiguous
     float *dq, *dk, *dv, *dr;              // [B,H,L,d] contiguous
     float *stats;                          // workspace, see below
-    uint16_t *img;                         // workspace, see below
+    uint16_t *kvrec;                       // workspace: key-kernel stage records
+    uint16_t *qrec;                        // workspace: query-kernel stage records
     int64_t q_b, q_h, q_l;
     int64_t k_b, k_h, k_l;
     int64_t v_b, v_h, v_l;
@@ -73,21 +74,29 @@ struct BwdArgs {
     int zero_rows;     // rows of dk and dv that the first kernel clears
 };
 
-// Backward workspace, per (batch, head) and 32-row stage s:
+// Backward workspace.  Per (batch, head) and 32-row stage s:
 //   stats: float [4][32] -- lse*log2(e) (+inf for rows >= L), 1 - sbar,
 //          G = dout.pv, G - dout.o
-//   img:   four bf16 images (q, r, dout, k in that order), each
-//          [B*H][n_st][d/16][64 lanes][8]: rows 4g..4g+3 and 16+4g..16+4g+3
-//          of the stage at feature 16t + m for lane m + 16g of block t
-//          (zeros for rows >= L).
+//   key-kernel record (the query side of the stage, as the key kernel's LDS
+//          stage holds it): 6 groups of 1 KiB operand blocks, each block 64
+//          lanes x 16 bytes in lane order --
+//            row-major q, rho, dout: block (t, c) for rows 16t + (l % 16),
+//              features 32c + 8 (l / 16) .. +7          (2 * d/32 blocks each)
+//            transposed q, rho, dout: block u for feature 16u + (l % 16),
+//              rows 4g .. 4g+3 and 16+4g .. 16+4g+3, g = l / 16  (d/16 each)
+//   query-kernel record (the key side of the stage): row-major k, row-major
+//          v, transposed k, in the same block formats.
+// Rows >= L are zeros.
 constexpr int kBwdChunk = 16;
-__host__ __device__ inline size_t bwd_stats_bytes(int64_t BH, int64_t n_st) { return (size_t)(BH * n_st * 128 * 4); }
-__host__ __device__ inline size_t bwd_image_bytes(int64_t BH, int64_t n_st, int d) {
-    return (size_t)(BH * n_st * kStageKeys * d * 2);
+__host__ __device__ inline size_t bwd_stats_bytes(int64_t BH, int64_t n_st) {
+    return (size_t)(BH * n_st * 128 * 4);
 }
+__host__ __device__ constexpr size_t bwd_kv_record_bytes(int d) { return (size_t)6 * kStageKeys * d * 2; }
+__host__ __device__ constexpr size_t bwd_q_record_bytes(int d) { return (size_t)3 * kStageKeys * d * 2; }
 inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     const int64_t n_st = (L + kStageKeys - 1) / kStageKeys;
-    return bwd_stats_bytes(B * H, n_st) + 4 * bwd_image_bytes(B * H, n_st, d);
+    return bwd_stats_bytes(B * H, n_st) +
+           (size_t)(B * H * n_st) * (bwd_kv_record_bytes(d) + bwd_q_record_bytes(d));
 }
 
 // Prefill workgroup shape: 8 wavefronts of 16 query rows for either feature

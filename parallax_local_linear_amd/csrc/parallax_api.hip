@@ -192,8 +192,8 @@ parallax_status parallax_attn_bwd(const void *q, const void *k, const void *v, c
         const int64_t first_past = std::min<int64_t>(n_st, (bt - 1 + window - 1) / 32 + 1);
         n_chunks = (n_st - first_past + plx::kBwdChunk - 1) / plx::kBwdChunk;
     }
-    if (BH * (n_kb + n_sb * n_chunks) > INT_MAX || n_st * 32 * d * 2 > INT32_MAX ||
-        n_st * 512 > INT32_MAX)
+    if (BH * (n_kb + n_sb * n_chunks) > INT_MAX ||
+        n_st * (int64_t)plx::bwd_kv_record_bytes(d) > INT32_MAX || n_st * 512 > INT32_MAX)
         return PARALLAX_ERR_UNSUPPORTED;
 
     char *ws = static_cast<char *>(workspace);
@@ -212,7 +212,9 @@ parallax_status parallax_attn_bwd(const void *q, const void *k, const void *v, c
     a.dv = dv;
     a.dr = dr;
     a.stats = reinterpret_cast<float *>(ws);
-    a.img = reinterpret_cast<uint16_t *>(ws + plx::bwd_stats_bytes(BH, n_st));
+    a.kvrec = reinterpret_cast<uint16_t *>(ws + plx::bwd_stats_bytes(BH, n_st));
+    a.qrec = reinterpret_cast<uint16_t *>(ws + plx::bwd_stats_bytes(BH, n_st) +
+                                          (size_t)(BH * n_st) * plx::bwd_kv_record_bytes(d));
     a.q_b = sq.b; a.q_h = sq.h; a.q_l = sq.l;
     a.k_b = sk.b; a.k_h = sk.h; a.k_l = sk.l;
     a.v_b = sv.b; a.v_h = sv.h; a.v_l = sv.l;

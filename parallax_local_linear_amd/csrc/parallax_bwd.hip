@@ -18,13 +18,18 @@
 // Four kernels run in order:
 //   * stats: per row lse*log2(e), 1 - sbar, G and G - Y (sbar and pv are
 //     saved by the forward);
-//   * images: q, rho, dO and k transposed into matrix-core operand order
-//     (below), so that the products that reduce over rows read them with
-//     one 16-byte LDS read per lane;
-//   * key kernel: a workgroup owns 128 keys (32 per wavefront), streams the
+//   * records: q, rho, dO, k and v rearranged per 32-row stage into
+//     matrix-core operand blocks (below), row-major and, for q, rho, dO and
+//     k, transposed, so that every LDS read is one 16-byte read per lane
+//     and every stage is copied into LDS as contiguous 1 KiB blocks;
+//   * key kernel: a workgroup owns 128 keys (16 per wavefront), streams the
 //     query rows that see them and accumulates dv and dk;
-//   * query kernel: a workgroup owns 128 query rows (32 per wavefront),
+//   * query kernel: a workgroup owns 128 query rows (16 per wavefront),
 //     streams the keys they see and accumulates dq and drho.
+// Eight wavefronts per workgroup, two per SIMD: LDS reads of 16 bytes per
+// lane reach about twice the bandwidth with two wavefronts per SIMD as
+// with one, and the two overlap each other's exponentials with their
+// matrix-core work.
 // Both recompute the scores (q.k, rho.k and dO.v) of every visible pair
 // with v_mfma_f32_16x16x32_bf16; the weights p t, dS and scale dZ go to
 // bfloat16 operands of the accumulating products.
@@ -33,7 +38,7 @@
 // positions 8 (l / 16) .. +7 of A; column l % 16 and the same positions of
 // B; holds rows 4 (l / 16) .. +3 of column l % 16 of C):
 //   * The key kernel computes C = Q K^T per 16 x 16 tile: a lane holds one
-//     key and four consecutive query rows.  Two query tiles give a lane the
+//     of the wavefront's 16 keys and four consecutive query rows.  Two query tiles give a lane the
 //     rows {4g .. 4g+3, 16+4g .. 16+4g+3} (g = l / 16) of a 32-row stage,
 //     which it uses directly as the B operand of dv^T += dO^T (p t) over the
 //     stage's 32 rows, provided the A operand lists the rows in the same
@@ -42,13 +47,20 @@
 //     four consecutive keys), so with the k image the same holds for
 //     dq^T += K^T dZ^T.
 //   * Row-major operands (q, rho, dO in the key kernel; k, v in the query
-//     kernel) are copied straight from the inputs into LDS, one 16-byte
-//     fragment per lane, so each 1 KiB block is read back at lane * 16.
+//     kernel) are stored as one 16-byte fragment per lane as well, so each
+//     1 KiB block is read back at lane * 16.  All of a stage's blocks are
+//     one contiguous record, copied with one buffer resource and a scalar
+//     offset per stage (no per-copy address arithmetic).
 //
 // Stages of 32 rows stream through three LDS buffers with direct
 // global-to-LDS copies, two stages ahead.  Workgroups are issued heaviest
 // first; the block index keeps all tiles of one (batch, head) on one XCD
-// when B*H is a multiple of 8.  Sink keys (sliding-window masks, "Sliding-
+// when B*H is a multiple of 8.  The key kernel walks its query stages from
+// the last one down, so the workgroups of one (batch, head) that run at the
+// same time read the same stage at about the same time and share it in L2
+// (walking up from each block's diagonal would spread them over the
+// sequence); the query kernel walks its key stages up from the first one,
+// with the same effect.  Sink keys (sliding-window masks, "Sliding-
 // window beats linear attention" review, sec. 1) are seen by every later
 // row; the key blocks holding them split the rows past the window into
 // chunks handled by separate workgroups that add into dk and dv atomically,
@@ -64,9 +76,12 @@ namespace {
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 constexpr int BS = 32;        // rows per stage
-constexpr int NW = 4;         // wavefronts per workgroup
-constexpr int BT = 32 * NW;   // rows (keys or queries) per workgroup
+constexpr int NW = 8;         // wavefronts per workgroup (two per SIMD)
+constexpr int RT = 1;         // 16-row tiles per wavefront (keys or queries it owns)
+constexpr int BT = 16 * RT * NW;  // rows (keys or queries) per workgroup
 constexpr int NB = 3;         // LDS stage buffers
+constexpr int NTHREADS = 64 * NW;
+static_assert(BT == 128, "the host sizes the sink-block split for 128-row workgroups");
 constexpr float kPosInf = __builtin_inff();
 
 static_assert(BS == kStageKeys, "stage size shared with the workspace layout");
@@ -176,17 +191,20 @@ __global__ __launch_bounds__(256) void parallax_bwd_stats_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Transposed operand images.  A thread reads 16 bytes (8 features) of the 8
-// rows that lane group g of a stage holds, transposes the 8 x 8 block in
-// registers and writes the 16-byte operands of 8 lanes.  blockIdx.y picks
-// the tensor: 0 q, 1 rho, 2 dO, 3 k.
+// Stage records.  A thread reads 16 bytes (8 features) of the 8 rows that
+// lane group g of a stage holds: it stores each 16-byte chunk as it is into
+// the row-major blocks, and transposes the 8 x 8 block in registers for the
+// transposed blocks (8 lanes' operands).  blockIdx.y picks the tensor:
+// 0 q, 1 rho, 2 dO (key-kernel record), 3 k, 4 v (query-kernel record).
 
 template <int D>
-__global__ __launch_bounds__(256) void parallax_bwd_image_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
+    constexpr int KC = D / 32;
+    constexpr int DT = D / 16;
     constexpr int FC = D / 8;        // 16-byte feature chunks per row
     constexpr int TPS = 4 * FC;      // threads per stage
     constexpr int SPB = 256 / TPS;   // stages per block
-    constexpr int DT = D / 16;
+    constexpr int BLK = 64 * 8;      // bf16 elements per operand block
     const int t = threadIdx.x;
     const int s = blockIdx.x * SPB + t / TPS;
     const int G = (t % TPS) / FC;
@@ -196,24 +214,42 @@ __global__ __launch_bounds__(256) void parallax_bwd_image_kernel(BwdArgs a) {
     const int BH = a.B * a.H;
     if (s >= a.n_st)
         return;
-    const uint16_t *src = which == 0 ? a.q : which == 1 ? a.r : which == 2 ? a.dout : a.k;
-    const int64_t sb = which == 0 ? a.q_b : which == 1 ? a.r_b : which == 2 ? a.do_b : a.k_b;
-    const int64_t sh = which == 0 ? a.q_h : which == 1 ? a.r_h : which == 2 ? a.do_h : a.k_h;
-    const int64_t sl = which == 0 ? a.q_l : which == 1 ? a.r_l : which == 2 ? a.do_l : a.k_l;
-    uint16_t *img = a.img + (size_t)which * bwd_image_bytes(BH, a.n_st, D) / 2;
+    const uint16_t *src = which == 0 ? a.q : which == 1 ? a.r : which == 2 ? a.dout
+                        : which == 3 ? a.k : a.v;
+    const int64_t sb = which == 0 ? a.q_b : which == 1 ? a.r_b : which == 2 ? a.do_b
+                     : which == 3 ? a.k_b : a.v_b;
+    const int64_t sh = which == 0 ? a.q_h : which == 1 ? a.r_h : which == 2 ? a.do_h
+                     : which == 3 ? a.k_h : a.v_h;
+    const int64_t sl = which == 0 ? a.q_l : which == 1 ? a.r_l : which == 2 ? a.do_l
+                     : which == 3 ? a.k_l : a.v_l;
+    // Record of this tensor, and the positions of its row-major and
+    // transposed groups in it.
+    const bool kv_side = which < 3;
+    const int x = kv_side ? which : which - 3;
+    const size_t rec_elems = kv_side ? bwd_kv_record_bytes(D) / 2 : bwd_q_record_bytes(D) / 2;
+    uint16_t *recs = kv_side ? a.kvrec : a.qrec;
+    const int rm_block0 = x * 2 * KC;
+    const int tr_block0 = kv_side ? 3 * 2 * KC + x * DT : 2 * 2 * KC;
+    const bool has_tr = which != 4;
     for (int bh = blockIdx.z; bh < BH; bh += gridDim.z) {
         const int b = bh / a.H;
         const int h = bh - b * a.H;
         const int i0 = s * BS;
         const uint16_t *base = src + b * sb + h * sh + (int64_t)i0 * sl;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows_bytes(i0, L, sl, D));
+        uint16_t *rec = recs + ((size_t)bh * a.n_st + s) * rec_elems;
         u32x4 in[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int row = e < 4 ? 4 * G + e : 16 + 4 * G + (e - 4);
             in[e] = bufld16(rs, (uint32_t)(row * sl * 2 + fc * 16));
+            // Row-major block (row / 16, fc / 4), lane row % 16 + 16 (fc % 4).
+            const int blk = rm_block0 + (row / 16) * KC + fc / 4;
+            const int lane = (row % 16) + 16 * (fc % 4);
+            *reinterpret_cast<u32x4 *>(rec + (size_t)blk * BLK + lane * 8) = in[e];
         }
-        uint16_t *blk = img + ((size_t)bh * a.n_st + s) * (DT * 64 * 8);
+        if (!has_tr)
+            continue;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             u32x4 out;
@@ -224,9 +260,9 @@ __global__ __launch_bounds__(256) void parallax_bwd_image_kernel(BwdArgs a) {
                 out[w] = lo | (hi << 16);
             }
             const int f = 8 * fc + u;
-            const int dt = f / 16;
+            const int blk = tr_block0 + f / 16;
             const int lane = (f % 16) + 16 * G;
-            *reinterpret_cast<u32x4 *>(blk + ((size_t)dt * 64 + lane) * 8) = out;
+            *reinterpret_cast<u32x4 *>(rec + (size_t)blk * BLK + lane * 8) = out;
         }
     }
 }
@@ -245,14 +281,13 @@ template <int I>
 using BufI = std::integral_constant<int, I % NB>;
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void parallax_bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTHREADS) void parallax_bwd_kv_kernel(BwdArgs a) {
     using C = BCfg<D>;
     constexpr int KC = C::KC, DT = C::DT;
     constexpr int NRM = 3 * 2 * KC;      // row-major blocks per stage
     constexpr int NTR = 3 * DT;          // image blocks per stage
-    constexpr int NCP = (NRM + NTR) / NW;  // block copies per wave per stage
-    constexpr int COPIES = NCP + 1;      // + a quarter of the stage's statistics
-    static_assert((NRM + NTR) % NW == 0 && NRM % NW == 0, "copy split");
+    constexpr int NCP = (NRM + NTR + NW - 1) / NW;  // block copies per wave per stage
+    constexpr int COPIES = NCP + 1;      // + an eighth of the stage's statistics
     __shared__ KvStage<D> sb0, sb1, sb2;
     auto sbuf = [&](auto b) -> KvStage<D> & {
         constexpr int i = decltype(b)::value % NB;
@@ -304,31 +339,26 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_kv_kernel(BwdArgs a) {
     if (n <= 0)
         return;
     const int j0 = kb * BT;
-    const int jw = j0 + 32 * wave;  // this wave's first key
+    constexpr int KW = 16 * RT;     // keys per wave
+    const int jw = j0 + KW * wave;  // this wave's first key
 
-    const uint16_t *qb = a.q + b * a.q_b + h * a.q_h;
-    const uint16_t *rb = a.r + b * a.r_b + h * a.r_h;
-    const uint16_t *ob = a.dout + b * a.do_b + h * a.do_h;
-    const size_t img_elems = bwd_image_bytes(BH, n_st, D) / 2;
-    const size_t slice_img = (size_t)n_st * BS * D;  // elements of one slice's image
-    const uint16_t *img_q = a.img + (size_t)bh * slice_img;
-    const __amdgpu_buffer_rsrc_t r_img[3] = {
-        make_rsrc(img_q, (uint32_t)(slice_img * 2)),
-        make_rsrc(img_q + img_elems, (uint32_t)(slice_img * 2)),
-        make_rsrc(img_q + 2 * img_elems, (uint32_t)(slice_img * 2))};
+    // This slice's stage records (one buffer resource for all of them).
+    constexpr uint32_t kRec = (uint32_t)bwd_kv_record_bytes(D);
+    const __amdgpu_buffer_rsrc_t r_rec =
+        make_rsrc(a.kvrec + (size_t)bh * n_st * (kRec / 2), (uint32_t)n_st * kRec);
     const __amdgpu_buffer_rsrc_t r_st =
         make_rsrc(a.stats + (size_t)bh * n_st * 128, (uint32_t)(n_st * 512));
 
     // This wave's keys as B operands: key jw + 16 kt + l16, features
     // 32 kc + 8 G .. +7 (zeros past the end).
-    bf16x8 kf[2][KC], vf[2][KC];
+    bf16x8 kf[RT][KC], vf[RT][KC];
     {
         const uint16_t *kbase = a.k + b * a.k_b + h * a.k_h + (int64_t)jw * a.k_l;
         const uint16_t *vbase = a.v + b * a.v_b + h * a.v_h + (int64_t)jw * a.v_l;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, rows_bytes(jw, L, a.k_l, D));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, rows_bytes(jw, L, a.v_l, D));
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < RT; ++kt)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int row = 16 * kt + l16;
@@ -338,63 +368,49 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_kv_kernel(BwdArgs a) {
             }
     }
 
-    f32x4 dv[DT][2], dk[DT][2];
+    f32x4 dv[DT][RT], dk[DT][RT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < RT; ++kt)
             dv[dt][kt] = dk[dt][kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // Copies of this wave's share of stage t (clamped: copies past the last
-    // stage reload it into a buffer nobody reads again).
+    // stage reload it into a buffer nobody reads again): record blocks
+    // wave, wave + NW, ...; a spare slot repeats a block another wave also
+    // copies (the same bytes), so every wave issues the same number of
+    // copies.  The record's layout is the LDS stage's layout.
     auto copy = [&](int t, auto buf) __attribute__((always_inline)) {
-        const int s = s_begin + min(t, n - 1);
-        const int i0 = s * BS;
+        const int s = s_end - 1 - min(t, n - 1);
         KvStage<D> &S = sbuf(buf);
-        const __amdgpu_buffer_rsrc_t rr[3] = {
-            make_rsrc(qb + (int64_t)i0 * a.q_l, rows_bytes(i0, L, a.q_l, D)),
-            make_rsrc(rb + (int64_t)i0 * a.r_l, rows_bytes(i0, L, a.r_l, D)),
-            make_rsrc(ob + (int64_t)i0 * a.do_l, rows_bytes(i0, L, a.do_l, D))};
-        const int64_t ld[3] = {a.q_l, a.r_l, a.do_l};
 #pragma unroll
         for (int c = 0; c < NCP; ++c) {
-            const int bi = NW * c + wave;
-            if (NW * c < NRM) {
-                constexpr int PER_X = 2 * KC;
-                const int x = (NW * c) / PER_X;  // the same tensor for every wave
-                const int blk = bi - x * PER_X;
-                const int qt = blk / KC;
-                const int kc = blk - qt * KC;
-                const uint32_t off =
-                    (uint32_t)(((16 * qt + l16) * ld[x] + 32 * kc + 8 * G) * 2);
-                dma16(rr[x], &S.rm[bi][0], off);
-            } else {
-                const int ii = bi - NRM;
-                const int x = (NW * c - NRM) / DT;
-                const int dt = ii - x * DT;
-                const uint32_t off = (uint32_t)((((size_t)s * DT + dt) * 64 + lane) * 16);
-                dma16(r_img[x], &S.tr[ii][0], off);
-            }
+            int bi = NW * c + wave;
+            if (NW * (c + 1) > NRM + NTR && bi >= NRM + NTR)
+                bi -= NRM + NTR;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r_rec, (lds_void *)(reinterpret_cast<char *>(&S) + bi * 1024), 16,
+                (int)(bi * 1024 + lane * 16), (int)(s * kRec), 0, 0);
         }
-        if (lane < 8)
-            dma16(r_st, &S.st[0][0] + 32 * wave,
-                  (uint32_t)(s * 512 + wave * 128 + lane * 16));
+        if (lane < 4)
+            dma16(r_st, &S.st[0][0] + 16 * wave,
+                  (uint32_t)(s * 512 + wave * 64 + lane * 16));
     };
 
     const float c2 = a.scale * kLog2e;
     const float scale = a.scale;
 
     auto compute = [&](int t, auto buf) __attribute__((always_inline)) {
-        const int i0 = (s_begin + t) * BS;
+        const int i0 = (s_end - 1 - t) * BS;
         // Visibility of this wave's 32 keys from the stage's 32 rows.
         const bool none = jw > i0 + BS - 1 ||
-                          (window > 0 && i0 - (jw + 31) >= window && jw >= n_sink);
+                          (window > 0 && i0 - (jw + KW - 1) >= window && jw >= n_sink);
         if (none)
             return;
-        const bool full = jw + 31 <= i0 &&
-                          (window <= 0 || (i0 + BS - 1) - jw < window || jw + 31 < n_sink);
+        const bool full = jw + KW - 1 <= i0 &&
+                          (window <= 0 || (i0 + BS - 1) - jw < window || jw + KW - 1 < n_sink);
         KvStage<D> &S = sbuf(buf);
-        f32x4 z[2][2], sr[2][2], g[2][2];  // [qt][kt]
+        f32x4 z[2][RT], sr[2][RT], g[2][RT];  // [qt][kt]
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -403,7 +419,7 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_kv_kernel(BwdArgs a) {
                 const bf16x8 ar = lds_frag(S.rm[1 * 2 * KC + qt * KC + kc], lane);
                 const bf16x8 ao = lds_frag(S.rm[2 * 2 * KC + qt * KC + kc], lane);
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
+                for (int kt = 0; kt < RT; ++kt) {
                     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                     z[qt][kt] = mfma(aq, kf[kt][kc], kc ? z[qt][kt] : zero);
                     sr[qt][kt] = mfma(ar, kf[kt][kc], kc ? sr[qt][kt] : zero);
@@ -419,9 +435,9 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_kv_kernel(BwdArgs a) {
             gg[qt] = *reinterpret_cast<const f32x4 *>(&S.st[2][16 * qt + 4 * G]);
             hh[qt] = *reinterpret_cast<const f32x4 *>(&S.st[3][16 * qt + 4 * G]);
         }
-        bf16x8 wb[2], zb[2], sb[2];
+        bf16x8 wb[RT], zb[RT], sb[RT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < RT; ++kt) {
             uint32_t pw[4], pz[4], ps[4];
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt)
@@ -458,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_kv_kernel(BwdArgs a) {
             const bf16x8 tr = lds_frag(S.tr[1 * DT + dt], lane);
             const bf16x8 to = lds_frag(S.tr[2 * DT + dt], lane);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < RT; ++kt) {
                 dv[dt][kt] = mfma(to, wb[kt], dv[dt][kt]);
                 dk[dt][kt] = mfma(tq, zb[kt], dk[dt][kt]);
                 dk[dt][kt] = mfma(tr, sb[kt], dk[dt][kt]);
@@ -490,7 +506,7 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_kv_kernel(BwdArgs a) {
 
     // dk and dv of keys jw + 16 kt + l16, features 16 dt + 4 G .. +3.
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < RT; ++kt) {
         const int j = jw + 16 * kt + l16;
         if (j >= L)
             continue;
@@ -522,12 +538,11 @@ struct QStage {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTHREADS) void parallax_bwd_q_kernel(BwdArgs a) {
     using C = BCfg<D>;
     constexpr int KC = C::KC, DT = C::DT;
     constexpr int NRM = 2 * 2 * KC;
-    constexpr int NCP = (NRM + DT) / NW;
-    static_assert((NRM + DT) % NW == 0 && NRM % NW == 0, "copy split");
+    constexpr int NCP = (NRM + DT + NW - 1) / NW;
     __shared__ QStage<D> sb0, sb1, sb2;
     auto sbuf = [&](auto b) -> QStage<D> & {
         constexpr int i = decltype(b)::value % NB;
@@ -556,7 +571,8 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
     const int b = bh / a.H;
     const int h = bh - b * a.H;
     const int i0 = qblk * BT;
-    const int iw = i0 + 32 * wave;  // this wave's first row
+    constexpr int QW = 16 * RT;     // rows per wave
+    const int iw = i0 + QW * wave;  // this wave's first row
 
     // Key stages: sink stages below the window, then the window up to the
     // diagonal.
@@ -566,16 +582,13 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
     const int n = ns + hi - lo + 1;
     auto stage_of = [&](int t) { return t < ns ? t : lo + (t - ns); };
 
-    const uint16_t *kb = a.k + b * a.k_b + h * a.k_h;
-    const uint16_t *vb = a.v + b * a.v_b + h * a.v_h;
-    const size_t img_elems = bwd_image_bytes(BH, n_st, D) / 2;
-    const size_t slice_img = (size_t)n_st * BS * D;
-    const __amdgpu_buffer_rsrc_t r_img =
-        make_rsrc(a.img + 3 * img_elems + (size_t)bh * slice_img, (uint32_t)(slice_img * 2));
+    constexpr uint32_t kRec = (uint32_t)bwd_q_record_bytes(D);
+    const __amdgpu_buffer_rsrc_t r_rec =
+        make_rsrc(a.qrec + (size_t)bh * n_st * (kRec / 2), (uint32_t)n_st * kRec);
 
     // This wave's rows as B operands: row iw + 16 qt + l16, features
     // 32 kc + 8 G .. +7.
-    bf16x8 qf[2][KC], rf[2][KC], of[2][KC];
+    bf16x8 qf[RT][KC], rf[RT][KC], of[RT][KC];
     {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(
             a.q + b * a.q_b + h * a.q_h + (int64_t)iw * a.q_l, rows_bytes(iw, L, a.q_l, D));
@@ -584,7 +597,7 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(
             a.dout + b * a.do_b + h * a.do_h + (int64_t)iw * a.do_l, rows_bytes(iw, L, a.do_l, D));
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < RT; ++qt)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int row = 16 * qt + l16;
@@ -595,9 +608,9 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
             }
     }
     // Statistics of rows iw + 16 qt + l16 (+inf offset past the end).
-    float lse2[2], aa[2], gg[2], hh[2];
+    float lse2[RT], aa[RT], gg[RT], hh[RT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < RT; ++qt) {
         const int i = iw + 16 * qt + l16;
         const float *st = a.stats + ((int64_t)bh * n_st + i / BS) * 128 + (i % BS);
         const bool in = i < n_st * BS;
@@ -607,38 +620,25 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
         hh[qt] = in ? st[96] : 0.f;
     }
 
-    f32x4 dq[DT][2], dr[DT][2];
+    f32x4 dq[DT][RT], dr[DT][RT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < RT; ++qt)
             dq[dt][qt] = dr[dt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+    // Copies as in the key kernel.
     auto copy = [&](int t, auto buf) __attribute__((always_inline)) {
         const int s = stage_of(min(t, n - 1));
-        const int j0 = s * BS;
         QStage<D> &S = sbuf(buf);
-        const __amdgpu_buffer_rsrc_t rr[2] = {
-            make_rsrc(kb + (int64_t)j0 * a.k_l, rows_bytes(j0, L, a.k_l, D)),
-            make_rsrc(vb + (int64_t)j0 * a.v_l, rows_bytes(j0, L, a.v_l, D))};
-        const int64_t ld[2] = {a.k_l, a.v_l};
 #pragma unroll
         for (int c = 0; c < NCP; ++c) {
-            const int bi = NW * c + wave;
-            if (NW * c < NRM) {
-                constexpr int PER_X = 2 * KC;
-                const int x = (NW * c) / PER_X;
-                const int blk = bi - x * PER_X;
-                const int kt = blk / KC;
-                const int kc = blk - kt * KC;
-                const uint32_t off =
-                    (uint32_t)(((16 * kt + l16) * ld[x] + 32 * kc + 8 * G) * 2);
-                dma16(rr[x], &S.rm[bi][0], off);
-            } else {
-                const int dt = bi - NRM;
-                const uint32_t off = (uint32_t)((((size_t)s * DT + dt) * 64 + lane) * 16);
-                dma16(r_img, &S.tr[dt][0], off);
-            }
+            int bi = NW * c + wave;
+            if (NW * (c + 1) > NRM + DT && bi >= NRM + DT)
+                bi -= NRM + DT;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r_rec, (lds_void *)(reinterpret_cast<char *>(&S) + bi * 1024), 16,
+                (int)(bi * 1024 + lane * 16), (int)(s * kRec), 0, 0);
         }
     };
 
@@ -646,14 +646,14 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
 
     auto compute = [&](int t, auto buf) __attribute__((always_inline)) {
         const int j0 = stage_of(t) * BS;
-        const bool none = j0 > iw + 31 ||
+        const bool none = j0 > iw + QW - 1 ||
                           (window > 0 && iw - (j0 + BS - 1) >= window && j0 >= n_sink);
         if (none)
             return;
         const bool full = j0 + BS - 1 <= iw &&
-                          (window <= 0 || (iw + 31) - j0 < window || j0 + BS - 1 < n_sink);
+                          (window <= 0 || (iw + QW - 1) - j0 < window || j0 + BS - 1 < n_sink);
         QStage<D> &S = sbuf(buf);
-        f32x4 z[2][2], sr[2][2], g[2][2];  // [kt][qt]
+        f32x4 z[2][RT], sr[2][RT], g[2][RT];  // [kt][qt]
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -661,16 +661,16 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
                 const bf16x8 ak = lds_frag(S.rm[0 * 2 * KC + kt * KC + kc], lane);
                 const bf16x8 av = lds_frag(S.rm[1 * 2 * KC + kt * KC + kc], lane);
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
+                for (int qt = 0; qt < RT; ++qt) {
                     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                     z[kt][qt] = mfma(ak, qf[qt][kc], kc ? z[kt][qt] : zero);
                     sr[kt][qt] = mfma(ak, rf[qt][kc], kc ? sr[kt][qt] : zero);
                     g[kt][qt] = mfma(av, of[qt][kc], kc ? g[kt][qt] : zero);
                 }
             }
-        bf16x8 zb[2], sb[2];
+        bf16x8 zb[RT], sb[RT];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < RT; ++qt) {
             uint32_t pz[4], ps[4];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -702,7 +702,7 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
         for (int dt = 0; dt < DT; ++dt) {
             const bf16x8 tk = lds_frag(S.tr[dt], lane);
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
+            for (int qt = 0; qt < RT; ++qt) {
                 dq[dt][qt] = mfma(tk, zb[qt], dq[dt][qt]);
                 dr[dt][qt] = mfma(tk, sb[qt], dr[dt][qt]);
             }
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(256, 1) void parallax_bwd_q_kernel(BwdArgs a) {
 
     const float scale = a.scale;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < RT; ++qt) {
         const int i = iw + 16 * qt + l16;
         if (i >= L)
             continue;
@@ -767,8 +767,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     }
     {
         constexpr int SPB = 256 / (4 * (D / 8));
-        const dim3 grid((unsigned)((a.n_st + SPB - 1) / SPB), 4, gz);
-        e = hipLaunchKernel(reinterpret_cast<const void *>(&parallax_bwd_image_kernel<D>), grid,
+        const dim3 grid((unsigned)((a.n_st + SPB - 1) / SPB), 5, gz);
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&parallax_bwd_record_kernel<D>), grid,
                             dim3(256), params, 0, stream);
         if (e != hipSuccess)
             return e;
@@ -777,13 +777,13 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
     {
         const dim3 grid((unsigned)(BH * (n_kb + a.n_sb * a.n_chunks)));
         e = hipLaunchKernel(reinterpret_cast<const void *>(&parallax_bwd_kv_kernel<D>), grid,
-                            dim3(256), params, 0, stream);
+                            dim3(NTHREADS), params, 0, stream);
         if (e != hipSuccess)
             return e;
     }
     const dim3 grid((unsigned)(BH * n_kb));
     return hipLaunchKernel(reinterpret_cast<const void *>(&parallax_bwd_q_kernel<D>), grid,
-                           dim3(256), params, 0, stream);
+                           dim3(NTHREADS), params, 0, stream);
 }
 
 }  // namespace

@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
 // fewer than 2^31 bytes, so one buffer resource per tensor covers every
 // stage and a stage needs only an offset; otherwise every stage builds its
 // own resources.
-template <int D, bool WHOLE>
+template <int D, bool WHOLE, bool STATS>
 __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     using C = Cfg<D>;
     // One LDS variable per stage buffer, each indexed only by compile-time
@@ -801,7 +801,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         if (G == 0)
             a.lse[(int64_t)bh * L + row] = (cx.m_ref + log2f(ell_t)) * kLn2;
         // Saved for the backward: sbar = S / ell and pv = A / ell.
-        if (a.pv) {
+        if constexpr (STATS) {
             float *pb = a.pv + ((int64_t)bh * L + row) * D;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) {
@@ -835,8 +835,13 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
     const dim3 block(NTHREADS);
     const bool whole = slice_bytes(a.L, a.k_l, D) <= INT32_MAX &&
                        (int64_t)a.n_st * D * BN * 2 <= INT32_MAX;
-    const void *fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true>)
-                           : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false>);
+    const void *fn;
+    if (a.pv)
+        fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true, true>)
+                   : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false, true>);
+    else
+        fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true, false>)
+                   : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false, false>);
     return hipLaunchKernel(fn, grid, block, params, 0, stream);
 }
 
