@@ -14,6 +14,11 @@ value products -- divided by the prefill kernel time measured with HIP events
 on its own stream); the decode throughput in GB/s is reported beside it.
 `roofline` describes the dominant kernel (the prefill); `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same prefill workload.
+
+After the timed steps, the prefill backward (parallax_attn_bwd: dq, dk, dv,
+drho of the same prefill workload, with a seeded N(0,1) output gradient) is
+timed separately and reported under "backward" (algorithmic FLOP: 16d per
+visible pair); it is not part of a step.
 """
 from __future__ import annotations
 
@@ -36,6 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_fwd.hip"),
     "decode": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
+    "backward": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_bwd.hip"),
 }
 
 
@@ -50,6 +56,8 @@ def parse():
                    help="(b,h) slices of the prefill workload the CPU oracle computes")
     p.add_argument("--extra", action="store_true",
                    help="also time the other prefill workloads (printed to stderr)")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip timing the prefill backward")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a plain 1 GiB device-to-device copy kernel three times, "
                         "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -127,6 +135,59 @@ def time_prefill_only(cfg, steps, warmup, stream):
     return {"workload": cfg.name, "ms": ms,
             "tflops": accounting.prefill_flops(cfg) / (ms * 1e-3) / 1e12,
             "gbs": accounting.prefill_bytes(cfg) / (ms * 1e-3) / 1e9}
+
+
+def time_backward(cfg, steps, warmup, stream):
+    """Mean time (HIP events on `stream`) of parallax_attn_bwd on one prefill workload."""
+    import torch
+
+    from parallax_local_linear_amd import (accounting, parallax_attn_bwd,
+                                           parallax_attn_bwd_workspace_size,
+                                           parallax_attn_fwd_train, workloads)
+    dev = torch.device("cuda:0")
+    q, k, v, r = workloads.prefill_inputs(cfg, device=dev)
+    dout = workloads.prefill_grad(cfg, device=dev)
+    o, lse, sbar, pv = parallax_attn_fwd_train(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink,
+                                               stream=stream)
+    grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(4))
+    ws = torch.empty(parallax_attn_bwd_workspace_size(cfg.B, cfg.H, cfg.L, cfg.d),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        parallax_attn_bwd(q, k, v, r, dout, o, lse, sbar, pv, window=cfg.window,
+                          n_sink=cfg.n_sink, grads=grads, workspace=ws, stream=stream)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = accounting.prefill_bwd_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": cfg.name,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "ms": round(ms, 4),
+        "steps": steps,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+            "traffic": measured_traffic("backward"),
+            "algorithmic_flop_per_launch": flops,
+            "kernel": "parallax_attn_bwd call = parallax_bwd_stats_kernel<128> + "
+                      "parallax_bwd_record_kernel<128> + parallax_bwd_kv_kernel<128> + "
+                      "parallax_bwd_q_kernel<128>",
+        },
+    }
 
 
 def main():
@@ -242,7 +303,8 @@ def main():
             "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4),
             "traffic": measured_traffic("prefill"),
             "algorithmic_flop_per_launch": p_flops,
-            "kernel": "parallax_attn_fwd call = parallax_vprep_kernel<128> + parallax_fwd_kernel<128>",
+            "kernel": "parallax_attn_fwd call = parallax_vprep_kernel<128> + "
+                      "parallax_fwd_kernel<128, true, false>",
         },
         "decode": {
             "value": round(d_gbs, 1),
@@ -260,6 +322,10 @@ def main():
             },
         },
     }
+    if not args.no_backward:
+        print("[bench] timing the backward", file=sys.stderr, flush=True)
+        res["backward"] = time_backward(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
+                                        stream)
     if args.extra:
         for cfg in (workloads.PREFILL_06B, workloads.LOCAL, workloads.TINY):
             print(json.dumps(time_prefill_only(cfg, 20, 3, stream)), file=sys.stderr, flush=True)
