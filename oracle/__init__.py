@@ -65,6 +65,11 @@ class Oracle:
         lib.parallax_oracle_bwd.argtypes = [
             _D, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
             ctypes.c_int, ctypes.c_double, ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        lib.parallax_oracle_decode_ext.restype = ctypes.c_int
+        lib.parallax_oracle_decode_ext.argtypes = [
+            _D, _D, _D, _D, _I, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_long, ctypes.c_long,
+            ctypes.c_int]
         lib.parallax_oracle_decode.restype = ctypes.c_int
         lib.parallax_oracle_decode.argtypes = [
             _D, _D, _D, _D, _I, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
@@ -153,6 +158,33 @@ class Oracle:
             self._ptr(q), self._ptr(r), self._ptr(k_cache), self._ptr(v_cache),
             sl.ctypes.data_as(_I) if sl is not None else None, self._ptr(o), self._ptr(lse),
             B, H, Lmax, d, float(scale), int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return o, lse
+
+
+    def decode_ext(self, q, r, k_cache, v_cache, seqlens=None, scale=None, window=0, n_sink=0,
+                   nthreads=None):
+        """General decode: q, r [B,Hq,d]; caches [B,Hkv,Lmax,d] (Hq a multiple of
+        Hkv; query head h reads kv head h // (Hq // Hkv)); window and sinks as
+        in the prefill.  Returns (o [B,Hq,d], lse [B,Hq])."""
+        q, r, k_cache, v_cache = (self._f64(x) for x in (q, r, k_cache, v_cache))
+        B, Hkv, Lmax, d = k_cache.shape
+        Hq = q.shape[1]
+        if q.shape != (B, Hq, d) or r.shape != q.shape or v_cache.shape != k_cache.shape:
+            raise ValueError("decode shapes disagree")
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        sl = None
+        if seqlens is not None:
+            sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+        o = np.zeros((B, Hq, d), dtype=np.float64)
+        lse = np.zeros((B, Hq), dtype=np.float64)
+        rc = self.lib.parallax_oracle_decode_ext(
+            self._ptr(q), self._ptr(r), self._ptr(k_cache), self._ptr(v_cache),
+            sl.ctypes.data_as(_I) if sl is not None else None, self._ptr(o), self._ptr(lse),
+            B, Hq, Hkv, Lmax, d, float(scale), int(window), int(n_sink),
+            int(nthreads or default_threads()))
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return o, lse

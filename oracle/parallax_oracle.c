@@ -268,19 +268,25 @@ int parallax_oracle_fwd(const double *q, const double *k, const double *v,
 }
 
 /*
- * Decode: one query per sequence against a contiguous cache.
- *   q, r   : [B][H][d];  k_cache, v_cache: [B][H][Lmax][d]
+ * Decode, general form: one query per (sequence, query head) against a
+ * contiguous cache of Hkv key/value heads.  Query head h reads kv head
+ * h / (Hq / Hkv) (grouped-query attention; Hkv = Hq is the plain case,
+ * Hkv = 1 multi-query).  The query sits at position seqlen-1 and sees the
+ * keys visible() allows there (causal, optional window and sinks).
+ *   q, r   : [B][Hq][d];  k_cache, v_cache: [B][Hkv][Lmax][d]
  *   seqlens: [B] host array or NULL (all Lmax); each clamped to [0, Lmax].
- * The query sits at position seqlen-1 and sees keys 0..seqlen-1.
- * o: [B][H][d], lse: [B][H].  Returns 0 or -1.
+ * o: [B][Hq][d], lse: [B][Hq].  Returns 0 or -1.
  */
-int parallax_oracle_decode(const double *q, const double *r,
-                           const double *k_cache, const double *v_cache,
-                           const int *seqlens, double *o, double *lse,
-                           long B, long H, long Lmax, int d, double scale, int nthreads)
+int parallax_oracle_decode_ext(const double *q, const double *r,
+                               const double *k_cache, const double *v_cache,
+                               const int *seqlens, double *o, double *lse,
+                               long B, long Hq, long Hkv, long Lmax, int d, double scale,
+                               long window, long n_sink, int nthreads)
 {
-    if (B < 0 || H < 0 || Lmax < 0 || d <= 0)
+    if (B < 0 || Hq < 0 || Hkv <= 0 || Lmax < 0 || d <= 0 || window < 0 || n_sink < 0 ||
+        Hq % Hkv != 0)
         return -1;
+    const long g = Hq / Hkv;
     int rc = 0;
     for (long b = 0; b < B && rc == 0; ++b) {
         long n = seqlens ? seqlens[b] : Lmax;
@@ -288,15 +294,35 @@ int parallax_oracle_decode(const double *q, const double *r,
             n = 0;
         if (n > Lmax)
             n = Lmax;
-        for (long h = 0; h < H && rc == 0; ++h) {
-            long bh = b * H + h;
+        for (long h = 0; h < Hq && rc == 0; ++h) {
+#if ORACLE_MUTANT == 17
+            /* planted mistake: query heads mapped to kv heads round-robin */
+            long hk = h % Hkv;
+#else
+            long hk = h / g;
+#endif
+            long bh = b * Hq + h;
             long p = n - 1;
-            rc = parallax_oracle_rows(q + bh * d, r + bh * d, &p, 1,
-                                      k_cache + bh * Lmax * d, v_cache + bh * Lmax * d,
-                                      Lmax, d, scale, 0, 0, o + bh * d, lse + bh, nthreads);
+            const double *kc = k_cache + (b * Hkv + hk) * Lmax * d;
+            const double *vc = v_cache + (b * Hkv + hk) * Lmax * d;
+            rc = parallax_oracle_rows(q + bh * d, r + bh * d, &p, 1, kc, vc, Lmax, d, scale,
+                                      window, n_sink, o + bh * d, lse + bh, nthreads);
         }
     }
     return rc;
+}
+
+/* Decode against a contiguous cache with one kv head per query head and
+ * no window: the general form with Hkv = H. */
+int parallax_oracle_decode(const double *q, const double *r,
+                           const double *k_cache, const double *v_cache,
+                           const int *seqlens, double *o, double *lse,
+                           long B, long H, long Lmax, int d, double scale, int nthreads)
+{
+    if (H <= 0)
+        return (B < 0 || H < 0 || Lmax < 0 || d <= 0) ? -1 : 0;
+    return parallax_oracle_decode_ext(q, r, k_cache, v_cache, seqlens, o, lse, B, H, H, Lmax,
+                                      d, scale, 0, 0, nthreads);
 }
 
 /*

@@ -48,7 +48,6 @@ def _close(a, b, tol=TOL, what=""):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     assert a.shape == b.shape, (what, a.shape, b.shape)
-    err = np.max(np.abs(a - b) / (1.0 + np.abs(b))) if a.size else 0.0
     assert np.all(np.isfinite(a) == np.isfinite(b)), what + ": finiteness differs"
     fin = np.isfinite(b)
     if fin.any():
@@ -224,6 +223,39 @@ def pin_decode(orc):
         _close(lse[b], lse2[0, :, n - 1], what="decode lse b=%d" % b)
 
 
+def pin_decode_general(orc):
+    """General decode: a row with a window and sinks equals the prefill row at
+    position seqlen-1 (matrix closed form), and grouped kv heads equal the
+    plain decode with each kv head repeated for its query heads."""
+    B, Hq, Hkv, Lmax, d = 3, 4, 2, 40, 5
+    k, v = (_rand((B, Hkv, Lmax, d), 130 + t) for t in range(2))
+    q, r = (_rand((B, Hq, d), 140 + t) for t in range(2))
+    seqlens = [40, 17, 0]
+    g = Hq // Hkv
+    for window, n_sink in ((0, 0), (6, 2), (3, 0), (1, 4)):
+        o, lse = orc.decode_ext(q, r, k, v, seqlens=seqlens, scale=0.45, window=window,
+                                n_sink=n_sink)
+        o_rep, lse_rep = orc.decode_ext(q, r, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1),
+                                        seqlens=seqlens, scale=0.45, window=window, n_sink=n_sink)
+        _close(o, o_rep, what="grouped kv heads vs repeated W=%d S=%d" % (window, n_sink))
+        _close(lse, lse_rep, what="grouped kv lse vs repeated W=%d S=%d" % (window, n_sink))
+        for b, n in enumerate(seqlens):
+            if n == 0:
+                assert np.all(o[b] == 0.0) and np.all(np.isneginf(lse[b])), "empty decode row"
+                continue
+            for h in range(Hq):
+                qq = np.zeros((1, 1, n, d))
+                rr = np.zeros((1, 1, n, d))
+                qq[0, 0, n - 1] = q[b, h]
+                rr[0, 0, n - 1] = r[b, h]
+                kk = k[b:b + 1, h // g:h // g + 1, :n]
+                vv = v[b:b + 1, h // g:h // g + 1, :n]
+                o2, lse2 = closed_form(qq, kk, vv, rr, scale=0.45, window=window, n_sink=n_sink)
+                _close(o[b, h], o2[0, 0, n - 1], what="decode row b=%d h=%d W=%d S=%d"
+                       % (b, h, window, n_sink))
+                _close(lse[b, h], lse2[0, 0, n - 1], what="decode lse b=%d h=%d" % (b, h))
+
+
 # ---------------------------------------------------------------------------
 # Backward.  The loss is Lambda = sum dO . o (so dO is dLambda/do); lse takes
 # no part in it.  The pins below use the forward oracle (itself pinned above)
@@ -333,6 +365,6 @@ def pin_bwd_identities(orc):
 
 ALL_PINS = [pin_closed_form, pin_softmax_special_case, pin_local_linear_fit,
             pin_single_key, pin_key_translation, pin_value_affine, pin_rho_linearity,
-            pin_masks, pin_golden, pin_decode,
+            pin_masks, pin_golden, pin_decode, pin_decode_general,
             pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_softmax_case,
             pin_bwd_identities]
