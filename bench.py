@@ -15,7 +15,10 @@ on its own stream); the decode throughput in GB/s is reported beside it.
 `roofline` describes the dominant kernel (the prefill); `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same prefill workload.
 
-After the timed steps, the prefill backward (parallax_attn_bwd: dq, dk, dv,
+After the timed steps, the general decode (parallax_attn_decode_paged) is
+timed on the decode workload's size in 64-token pages, with 16 and with 4 kv
+heads (GQA), reported under "decode_paged" (bytes: the cache read once); then
+the prefill backward (parallax_attn_bwd: dq, dk, dv,
 drho of the same prefill workload, with a seeded N(0,1) output gradient) is
 timed separately and reported under "backward" (algorithmic FLOP: 16d per
 visible pair); it is not part of a step.
@@ -190,6 +193,53 @@ def time_backward(cfg, steps, warmup, stream):
     }
 
 
+def time_decode_paged(dcfg, steps, warmup, stream):
+    """General decode on the decode workload's size: 64-token pages in a shuffled
+    pool, 16 query heads over 16 or 4 kv heads.  GB/s counts the cache once."""
+    import torch
+
+    from parallax_local_linear_amd import parallax_attn_decode_paged
+    dev = torch.device("cuda:0")
+    B, Hq, Lmax, d, page = dcfg.B, dcfg.H, dcfg.Lmax, dcfg.d, 64
+    out = []
+    for Hkv in (16, 4):
+        g = torch.Generator(device=dev).manual_seed(2024 + Hkv)
+        q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+        r = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+        n_pages = B * Lmax // page
+        kp = torch.randn((n_pages, page, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+        vp = torch.randn((n_pages, page, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+        perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(Hkv))
+        table = perm.view(B, Lmax // page).to(torch.int32).to(dev)
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+
+        def call():
+            parallax_attn_decode_paged(q, r, kp, vp, table, None, num_splits=dcfg.num_splits,
+                                       out=o, lse=lse, stream=stream)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbytes = 2 * B * Hkv * Lmax * d * 2 + B * Hq * (2 * d * 2 + d * 4 + 4) + B * Lmax // page * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append({"Hq": Hq, "Hkv": Hkv, "page": page, "ms": round(ms, 4),
+                    "value": round(gbs, 1), "unit": "GB/s",
+                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                 "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                                 "kernel": "parallax_decode_paged_kernel<128,...>"}})
+        del kp, vp
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -322,6 +372,9 @@ def main():
             },
         },
     }
+    print("[bench] timing the general decode", file=sys.stderr, flush=True)
+    res["decode_paged"] = time_decode_paged(dcfg, min(args.steps, 20),
+                                            max(1, min(args.warmup, 3)), stream)
     if not args.no_backward:
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         res["backward"] = time_backward(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),

@@ -223,6 +223,55 @@ parallax_status parallax_attn_decode(const void *q, const void *r,
                                      float softmax_scale, int num_splits,
                                      void *stream);
 
+/*
+ * General decode step: paged or contiguous KV cache, grouped kv heads
+ * (GQA/MQA) and an optional sliding window with attention sinks.  The
+ * arithmetic is parallax_attn_decode's; a windowed query at position
+ * seqlen-1 sees keys j with seqlen-1-j < window or j < n_sink, the
+ * prefill's visibility rule ("Sliding-window beats linear attention"
+ * review, sec. 1: window over preceding tokens plus sink tokens kept
+ * visible, which bounds the KV cache).
+ *
+ *   q, r       : bf16 [B, Hq, d], contiguous, 16-byte aligned.
+ *   k_cache,
+ *   v_cache    : bf16 caches addressed by element strides sk, sv with the
+ *                fields meaning (b: page, h: kv head, l: row in the page);
+ *                d contiguous, 16-byte aligned base, strides multiples of
+ *                8.  A vLLM-style pool [num_pages, page_size, Hkv, d] has
+ *                strides (page_size*Hkv*d, d, Hkv*d).
+ *   block_table: DEVICE int32 [B, max_pages] or NULL.  Paged: key j of
+ *                sequence b lives in page block_table[b*max_pages +
+ *                j / page_size] at row j % page_size; page_size must be a
+ *                power of two; entries for the pages that hold keys
+ *                0 .. seqlen-1 must be in [0, num_pages) (others are never
+ *                read; out-of-range entries are clamped into the pool, so
+ *                a bad table gives wrong results, not a fault).
+ *                NULL: contiguous cache, sequence b is "page" b and
+ *                page_size is the cache length Lmax (num_pages and
+ *                max_pages are ignored).
+ *   seqlens    : DEVICE int32 [B] or NULL (= the cache length: max_pages *
+ *                page_size when paged, page_size when contiguous); clamped
+ *                to [0, that length].
+ *   o, lse     : fp32 [B, Hq, d] and [B, Hq], contiguous.
+ *   Hq, Hkv    : query and kv heads, Hq a multiple of Hkv; query head h
+ *                reads kv head h / (Hq / Hkv).
+ *   window, n_sink : as for the prefill (0 = no window).
+ *   num_splits : 1, 2, 4, 8 or 16 key chunks per (sequence, query head),
+ *                as for parallax_attn_decode.  A workgroup serves
+ *                16 / num_splits query heads of one kv head when Hq/Hkv
+ *                allows (the largest power of two dividing it), so that
+ *                they share the rows they read.
+ */
+parallax_status parallax_attn_decode_paged(const void *q, const void *r,
+                                           const void *k_cache, const void *v_cache,
+                                           const int32_t *block_table, int num_pages,
+                                           int page_size, int max_pages,
+                                           const int32_t *seqlens, float *o, float *lse,
+                                           int B, int Hq, int Hkv, int d,
+                                           parallax_strides sk, parallax_strides sv,
+                                           float softmax_scale, int window, int n_sink,
+                                           int num_splits, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *parallax_status_string(parallax_status s);
 

@@ -5,11 +5,13 @@ The compute path is the gfx950 HIP library ``libparallax.so`` (C ABI in
 tensors into it.
 """
 from .binding import (EXPORTED, LIBRARY, ParallaxError, load_library, parallax_attn_bwd,
-                      parallax_attn_bwd_workspace_size, parallax_attn_decode, parallax_attn_fwd,
+                      parallax_attn_bwd_workspace_size, parallax_attn_decode,
+                      parallax_attn_decode_paged, parallax_attn_fwd,
                       parallax_attn_fwd_train, parallax_attn_fwd_workspace_size,
                       parallax_status_string)
 
 __all__ = ["EXPORTED", "LIBRARY", "ParallaxError", "load_library", "parallax_attn_bwd",
-           "parallax_attn_bwd_workspace_size", "parallax_attn_decode", "parallax_attn_fwd",
+           "parallax_attn_bwd_workspace_size", "parallax_attn_decode",
+           "parallax_attn_decode_paged", "parallax_attn_fwd",
            "parallax_attn_fwd_train", "parallax_attn_fwd_workspace_size",
            "parallax_status_string"]

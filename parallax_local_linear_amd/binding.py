@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
 # Every symbol include/parallax.h declares.
 EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_train",
             "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
-            "parallax_status_string")
+            "parallax_attn_decode_paged", "parallax_status_string")
 
 
 class parallax_strides(ctypes.Structure):
@@ -73,6 +73,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.parallax_attn_decode.restype = ctypes.c_int
     lib.parallax_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, S, S,
                                          f, i, vp]
+    lib.parallax_attn_decode_paged.restype = ctypes.c_int
+    lib.parallax_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, vp,
+                                               i, i, i, i, S, S, f, i, i, i, vp]
     lib.parallax_status_string.restype = ctypes.c_char_p
     lib.parallax_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -275,6 +278,60 @@ def parallax_attn_decode(q, r, k_cache, v_cache, seqlens=None, *, softmax_scale=
         q.data_ptr(), r.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         seqlens.data_ptr() if seqlens is not None else None, out.data_ptr(), lse.data_ptr(),
         B, H, Lmax, d, _strides(k_cache), _strides(v_cache), float(softmax_scale),
+        int(num_splits), _stream_handle(q.device, stream))
+    _check(st)
+    return out, lse
+
+
+def parallax_attn_decode_paged(q, r, k_cache, v_cache, block_table=None, seqlens=None, *,
+                               softmax_scale=None, window=0, n_sink=0, num_splits=16,
+                               out=None, lse=None, stream=None):
+    """General decode step.  q, r: bf16 [B,Hq,d].
+
+    Paged (block_table: int32 [B, max_pages]): k_cache, v_cache are page pools
+    [num_pages, page_size, Hkv, d] (any strides, d contiguous).  Contiguous
+    (block_table None): caches [B, Lmax, Hkv, d]; pass cache.permute(0, 2, 1, 3)
+    for a [B, Hkv, Lmax, d] tensor.  seqlens: int32 [B] or None.
+    Returns (o fp32 [B,Hq,d], lse fp32 [B,Hq]).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(r, "r", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, Hq, d = q.shape
+    P, page_size, Hkv, dk = k_cache.shape
+    if v_cache.shape != k_cache.shape or r.shape != q.shape or dk != d:
+        raise ValueError("decode shapes disagree")
+    if not (q.is_contiguous() and r.is_contiguous()):
+        raise ValueError("q and r must be contiguous")
+    if k_cache.stride(-1) != 1 or v_cache.stride(-1) != 1:
+        raise ValueError("the feature dimension must be contiguous (stride 1)")
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32, 2)
+        if block_table.shape[0] != B or not block_table.is_contiguous():
+            raise ValueError("block_table must be a contiguous int32 [B, max_pages] tensor")
+        max_pages = block_table.shape[1]
+    else:
+        if P != B:
+            raise ValueError("a contiguous cache has one page per sequence")
+        max_pages = 1
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, 1)
+        if seqlens.shape[0] != B or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be a contiguous int32 [B] tensor")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ks = parallax_strides(k_cache.stride(0), k_cache.stride(2), k_cache.stride(1))
+    vs = parallax_strides(v_cache.stride(0), v_cache.stride(2), v_cache.stride(1))
+    st = load_library().parallax_attn_decode_paged(
+        q.data_ptr(), r.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_table.data_ptr() if block_table is not None else None, P, page_size, max_pages,
+        seqlens.data_ptr() if seqlens is not None else None, out.data_ptr(), lse.data_ptr(),
+        B, Hq, Hkv, d, ks, vs, float(softmax_scale), int(window), int(n_sink),
         int(num_splits), _stream_handle(q.device, stream))
     _check(st)
     return out, lse

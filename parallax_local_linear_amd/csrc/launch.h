@@ -49,6 +49,24 @@ struct DecodeArgs {
     float scale_log2;
 };
 
+struct PagedDecodeArgs {
+    const uint16_t *q, *r;          // bf16 [B,Hq,d] contiguous
+    const uint16_t *k, *v;          // bf16 cache: element strides along page, kv head, row
+    const int32_t *block_table;     // device [B][max_pages] page indices, or nullptr
+    const int32_t *seqlens;         // device [B] or nullptr
+    float *o;                       // [B,Hq,d]
+    float *lse;                     // [B,Hq]
+    int64_t k_p, k_h, k_l;
+    int64_t v_p, v_h, v_l;
+    int B, Hq, Hkv;
+    int page_shift;                 // log2(page size) when paged
+    int max_pages;                  // block-table row length when paged
+    int num_pages;                  // pages in the pool (page indices are clamped into it)
+    int max_len;                    // longest sequence the cache holds
+    float scale_log2;
+    int window, n_sink;
+};
+
 struct BwdArgs {
     const uint16_t *q, *k, *v, *r, *dout;  // bf16 bits, [B,H,L,d] with the strides below
     const float *o, *lse, *sbar, *pv;      // from the forward, contiguous
@@ -107,5 +125,6 @@ constexpr int fwd_block_rows(int d) { return 16 * fwd_waves(d); }
 hipError_t launch_fwd(const FwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int d, int num_splits, hipStream_t stream);
+hipError_t launch_decode_paged(const PagedDecodeArgs &a, int d, int num_splits, hipStream_t stream);
 
 }  // namespace plx

@@ -278,4 +278,68 @@ parallax_status parallax_attn_decode(const void *q, const void *r, const void *k
     return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
 }
 
+parallax_status parallax_attn_decode_paged(const void *q, const void *r, const void *k_cache,
+                                           const void *v_cache, const int32_t *block_table,
+                                           int num_pages, int page_size, int max_pages,
+                                           const int32_t *seqlens, float *o, float *lse, int B,
+                                           int Hq, int Hkv, int d, parallax_strides sk,
+                                           parallax_strides sv, float softmax_scale, int window,
+                                           int n_sink, int num_splits, void *stream) {
+    if (B < 0 || Hq < 0 || Hkv < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (num_splits != 1 && num_splits != 2 && num_splits != 4 && num_splits != 8 &&
+        num_splits != 16)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!scale_ok(softmax_scale) || window < 0 || n_sink < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * Hq == 0)
+        return PARALLAX_OK;
+    if (Hkv <= 0 || Hq % Hkv != 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (page_size <= 0 || (block_table && ((page_size & (page_size - 1)) != 0 ||
+                                            num_pages <= 0 || max_pages <= 0)))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!q || !r || !o || !lse || !k_cache || !v_cache)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(r, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(o, 4) || !aligned(lse, 4) || !aligned(seqlens, 4) || !aligned(block_table, 4))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!bf16_strides_ok(sk) || !bf16_strides_ok(sv))
+        return PARALLAX_ERR_INVALID_ARG;
+    const int64_t max_len = block_table ? (int64_t)max_pages * page_size : page_size;
+    const int64_t g = Hq / Hkv;
+    if (max_len > INT_MAX || (((int64_t)B * Hkv + 7) / 8) * 8 * g > INT_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+
+    plx::PagedDecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.r = static_cast<const uint16_t *>(r);
+    a.k = static_cast<const uint16_t *>(k_cache);
+    a.v = static_cast<const uint16_t *>(v_cache);
+    a.block_table = block_table;
+    a.seqlens = seqlens;
+    a.o = o;
+    a.lse = lse;
+    a.k_p = sk.b; a.k_h = sk.h; a.k_l = sk.l;
+    a.v_p = sv.b; a.v_h = sv.h; a.v_l = sv.l;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    int shift = 0;
+    while (block_table && (1 << shift) < page_size)
+        ++shift;
+    a.page_shift = shift;
+    a.max_pages = block_table ? max_pages : 1;
+    a.num_pages = block_table ? num_pages : B;
+    a.max_len = (int)max_len;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.window = window;
+    a.n_sink = n_sink;
+    hipError_t e =
+        plx::launch_decode_paged(a, d, num_splits, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -233,6 +233,300 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_kernel(DecodeArgs a) 
         a.lse[bh] = lt > 0.f ? (M + log2f(lt)) * kLn2 : kNegInf;
 }
 
+// ---------------------------------------------------------------------------
+// General decode: a paged (or contiguous) cache, grouped kv heads, and a
+// sliding window with attention sinks at decode ("Sliding-window beats linear
+// attention" review, sec. 1 and sec. 3: windowed attention with sink tokens
+// keeps a fixed-size KV cache).  The same partial-state scheme as above;
+// what changes is which rows are read and where they live.
+//   * Query head h reads kv head h / (Hq / Hkv).  A workgroup serves GW
+//     query heads of one kv head with NS wavefronts each (wavefront w:
+//     head w % GW, key chunk w / GW), so the GW wavefronts of a chunk read
+//     the same cache rows on one CU.  Workgroups of one kv head get block
+//     indices with the same residue mod 8 (one XCD, one L2) when the group
+//     needs several of them.  Loads are cached when rows are shared and
+//     non-temporal when they are not (Hq = Hkv).
+//   * The query at position n-1 sees the sink keys [0, ns) and the window
+//     [lo, n) (all of [0, n) without a window); the NS wavefronts split the
+//     concatenation of the two segments evenly.
+//   * Paged: key j lives in page block_table[b][j >> page_shift] (clamped
+//     into the pool), row j & (page size - 1).  Contiguous: page b, row j.  A lane's key index
+//     is clamped into its segment before the address is formed, so every
+//     load reads a visible row of the sequence; the results of clamped
+//     lanes are masked.
+
+template <int D, int NS, int GW, bool PAGED, bool NT>
+__global__ __launch_bounds__(64 * NS * GW) void parallax_decode_paged_kernel(PagedDecodeArgs a) {
+    constexpr int LPK = D / 8;     // lanes per key
+    constexpr int KPS = 64 / LPK;  // keys per wave step
+    constexpr int U = 2;           // wave steps per iteration
+
+    __shared__ float s_m[GW][NS], s_l[GW][NS], s_s[GW][NS];
+    __shared__ float s_A[GW][NS][D], s_C[GW][NS][D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int head = wv % GW;     // query head of the workgroup's group
+    const int wave = wv / GW;     // key chunk
+    const int grp = lane / LPK;
+    const int sub = lane % LPK;
+
+    // Block -> (sequence, kv head, group of GW query heads).
+    const int g = a.Hq / a.Hkv;
+    const int ng = g / GW;        // workgroups per kv head
+    const int x = blockIdx.x;
+    const int slot = x >> 3;
+    const int pair = (slot / ng) * 8 + (x & 7);
+    if (pair >= a.B * a.Hkv)
+        return;
+    const int b = pair / a.Hkv;
+    const int hk = pair - b * a.Hkv;
+    const int hq = hk * g + (slot - (slot / ng) * ng) * GW + head;
+    const int64_t row_q = (int64_t)b * a.Hq + hq;
+    const float c = a.scale_log2;
+
+    int n = a.seqlens ? a.seqlens[b] : a.max_len;
+    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    int lo = 0, ns = 0;
+    if (a.window > 0) {
+        lo = max(0, n - a.window);
+        ns = min(a.n_sink, lo);
+    }
+    const int total = ns + (n - lo);
+    const int chunk = (total + NS - 1) / NS;
+    const int ts = min(wave * chunk, total);
+    const int te = min(ts + chunk, total);
+
+    float qv[8], rv[8];
+    {
+        const u32x4 qw = ldg16(a.q + row_q * D + 8 * sub);
+        const u32x4 rw = ldg16(a.r + row_q * D + 8 * sub);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            qv[2 * w] = bf16_lo(qw[w]);
+            qv[2 * w + 1] = bf16_hi(qw[w]);
+            rv[2 * w] = bf16_lo(rw[w]);
+            rv[2 * w + 1] = bf16_hi(rw[w]);
+        }
+    }
+    const uint16_t *kbase = a.k + (int64_t)hk * a.k_h + 8 * sub;
+    const uint16_t *vbase = a.v + (int64_t)hk * a.v_h + 8 * sub;
+    const int32_t *bt = PAGED ? a.block_table + (int64_t)b * a.max_pages : nullptr;
+    const int pmask = (1 << a.page_shift) - 1;
+
+    float m = kNegInf, ell = 0.f, ssum = 0.f;
+    float A[8], C[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        A[e] = 0.f;
+        C[e] = 0.f;
+    }
+
+    // Keys [j0, j1) of the sequence (j0 < j1).
+    auto process = [&](int j0, int j1) __attribute__((always_inline)) {
+        for (int j = j0; j < j1; j += KPS * U) {
+            u32x4 kw[U], vw[U];
+            bool valid[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int kj = j + u * KPS + grp;
+                valid[u] = kj < j1;
+                const int kc = valid[u] ? kj : j1 - 1;
+                int64_t page, row;
+                if constexpr (PAGED) {
+                    page = min(max(bt[kc >> a.page_shift], 0), a.num_pages - 1);
+                    row = kc & pmask;
+                } else {
+                    page = b;
+                    row = kc;
+                }
+                // One query head per kv head: the rows are read once
+                // (non-temporal loads); otherwise the other heads of the
+                // group read them too (cached loads).
+                const u32x4 *kp = reinterpret_cast<const u32x4 *>(kbase + page * a.k_p + row * a.k_l);
+                const u32x4 *vp = reinterpret_cast<const u32x4 *>(vbase + page * a.v_p + row * a.v_l);
+                if constexpr (NT) {
+                    kw[u] = __builtin_nontemporal_load(kp);
+                    vw[u] = __builtin_nontemporal_load(vp);
+                } else {
+                    kw[u] = *kp;
+                    vw[u] = *vp;
+                }
+            }
+            float xs[U], sr[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float dq = 0.f, dr = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float k0 = bf16_lo(kw[u][w]);
+                    const float k1 = bf16_hi(kw[u][w]);
+                    dq = fmaf(qv[2 * w], k0, dq);
+                    dq = fmaf(qv[2 * w + 1], k1, dq);
+                    dr = fmaf(rv[2 * w], k0, dr);
+                    dr = fmaf(rv[2 * w + 1], k1, dr);
+                }
+                dq = group_sum<LPK>(dq);
+                dr = group_sum<LPK>(dr);
+                xs[u] = valid[u] ? dq * c : kNegInf;
+                sr[u] = dr;
+            }
+            float mt = xs[0];
+#pragma unroll
+            for (int u = 1; u < U; ++u)
+                mt = fmaxf(mt, xs[u]);
+            const float m_new = fmaxf(m, mt);
+            const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m - m_new);
+            m = m_new;
+            const float msub = (m == kNegInf) ? 0.f : m;
+            ell *= alpha;
+            ssum *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                A[e] *= alpha;
+                C[e] *= alpha;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = exp2_fast(xs[u] - msub);
+                const float w = p * sr[u];
+                ell += p;
+                ssum += w;
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) {
+                    const float v0 = bf16_lo(vw[u][q2]);
+                    const float v1 = bf16_hi(vw[u][q2]);
+                    A[2 * q2] = fmaf(p, v0, A[2 * q2]);
+                    A[2 * q2 + 1] = fmaf(p, v1, A[2 * q2 + 1]);
+                    C[2 * q2] = fmaf(w, v0, C[2 * q2]);
+                    C[2 * q2 + 1] = fmaf(w, v1, C[2 * q2 + 1]);
+                }
+            }
+        }
+    };
+    // Segment 1: sink keys [ts, min(te, ns)); segment 2: window keys.
+    if (ts < ns)
+        process(ts, min(te, ns));
+    if (te > ns) {
+        const int v0 = max(ts, ns);
+        process(lo + (v0 - ns), lo + (te - ns));
+    }
+
+    // Merge the lane groups, then the wavefronts (as in the kernel above).
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) {
+        const float mo = __shfl_xor(m, off, 64);
+        const float lo2 = __shfl_xor(ell, off, 64);
+        const float so = __shfl_xor(ssum, off, 64);
+        const float M = fmaxf(m, mo);
+        const float f = (M == kNegInf) ? 0.f : exp2_fast(m - M);
+        const float fo = (M == kNegInf) ? 0.f : exp2_fast(mo - M);
+        ell = ell * f + lo2 * fo;
+        ssum = ssum * f + so * fo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            A[e] = A[e] * f + __shfl_xor(A[e], off, 64) * fo;
+            C[e] = C[e] * f + __shfl_xor(C[e], off, 64) * fo;
+        }
+        m = M;
+    }
+    if (lane < LPK) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s_A[head][wave][8 * sub + e] = A[e];
+            s_C[head][wave][8 * sub + e] = C[e];
+        }
+        if (lane == 0) {
+            s_m[head][wave] = m;
+            s_l[head][wave] = ell;
+            s_s[head][wave] = ssum;
+        }
+    }
+    __syncthreads();
+
+    // Merge the chunks of each head: index t covers feature t % D of head
+    // t / D of the group.
+    for (int t = tid; t < GW * D; t += 64 * NS * GW) {
+        const int hj = t / D;
+        const int nidx = t - hj * D;
+        float M = kNegInf;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            M = fmaxf(M, s_m[hj][s]);
+        float lt = 0.f, st = 0.f, at = 0.f, ct = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const float f = (M == kNegInf) ? 0.f : exp2_fast(s_m[hj][s] - M);
+            lt += f * s_l[hj][s];
+            st += f * s_s[hj][s];
+            at += f * s_A[hj][s][nidx];
+            ct += f * s_C[hj][s][nidx];
+        }
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float keep = 1.f - st * inv;
+        const int64_t row = row_q - head + hj;
+        a.o[row * D + nidx] = (at * keep + ct) * inv;
+        if (nidx == 0)
+            a.lse[row] = lt > 0.f ? (M + log2f(lt)) * kLn2 : kNegInf;
+    }
+}
+
+template <int D, int NS, int GW>
+hipError_t launch_decode_paged_t(const PagedDecodeArgs &a, hipStream_t stream) {
+    const int pairs = a.B * a.Hkv;
+    const int ng = a.Hq / a.Hkv / GW;
+    const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * ng));
+    const dim3 block(64 * NS * GW);
+    PagedDecodeArgs args = a;
+    void *params[] = {&args};
+    const void *fn;
+    if (a.Hq == a.Hkv)
+        fn = a.block_table
+                 ? reinterpret_cast<const void *>(&parallax_decode_paged_kernel<D, NS, GW, true, true>)
+                 : reinterpret_cast<const void *>(&parallax_decode_paged_kernel<D, NS, GW, false, true>);
+    else
+        fn = a.block_table
+                 ? reinterpret_cast<const void *>(&parallax_decode_paged_kernel<D, NS, GW, true, false>)
+                 : reinterpret_cast<const void *>(&parallax_decode_paged_kernel<D, NS, GW, false, false>);
+    return hipLaunchKernel(fn, grid, block, params, 0, stream);
+}
+
+// Heads per workgroup: the largest power of two dividing Hq/Hkv with at
+// most 16 wavefronts per workgroup (NS key chunks per head come first:
+// they keep enough workgroups in flight when B * Hkv is small).
+template <int D, int NS>
+hipError_t launch_decode_paged_g(const PagedDecodeArgs &a, hipStream_t stream) {
+    const int g = a.Hq / a.Hkv;
+    int gw = 1;
+    while (gw * 2 * NS <= 16 && g % (gw * 2) == 0)
+        gw *= 2;
+    if constexpr (NS <= 1) {
+        if (gw == 16) return launch_decode_paged_t<D, NS, 16>(a, stream);
+    }
+    if constexpr (NS <= 2) {
+        if (gw == 8) return launch_decode_paged_t<D, NS, 8>(a, stream);
+    }
+    if constexpr (NS <= 4) {
+        if (gw == 4) return launch_decode_paged_t<D, NS, 4>(a, stream);
+    }
+    if constexpr (NS <= 8) {
+        if (gw == 2) return launch_decode_paged_t<D, NS, 2>(a, stream);
+    }
+    return launch_decode_paged_t<D, NS, 1>(a, stream);
+}
+
+template <int D>
+hipError_t launch_decode_paged_d(const PagedDecodeArgs &a, int num_splits, hipStream_t stream) {
+    switch (num_splits) {
+    case 1: return launch_decode_paged_g<D, 1>(a, stream);
+    case 2: return launch_decode_paged_g<D, 2>(a, stream);
+    case 4: return launch_decode_paged_g<D, 4>(a, stream);
+    case 8: return launch_decode_paged_g<D, 8>(a, stream);
+    default: return launch_decode_paged_g<D, 16>(a, stream);
+    }
+}
+
 template <int D, int NS>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.B * a.H));
@@ -259,6 +553,12 @@ hipError_t launch_decode_d(const DecodeArgs &a, int num_splits, hipStream_t stre
 hipError_t launch_decode(const DecodeArgs &a, int d, int num_splits, hipStream_t stream) {
     return d == 64 ? launch_decode_d<64>(a, num_splits, stream)
                    : launch_decode_d<128>(a, num_splits, stream);
+}
+
+hipError_t launch_decode_paged(const PagedDecodeArgs &a, int d, int num_splits,
+                               hipStream_t stream) {
+    return d == 64 ? launch_decode_paged_d<64>(a, num_splits, stream)
+                   : launch_decode_paged_d<128>(a, num_splits, stream);
 }
 
 }  // namespace plx

@@ -228,6 +228,32 @@ def test_bwd_empty_is_a_no_op(lib):
     assert bwd(lib, H=0, q=None, dq=None, ws=None, ws_bytes=0) == OK
 
 
+def decp(lib, q=A16, r=A16, k=A16, v=A16, bt=A16, num_pages=64, page=16, max_pages=8,
+         seqlens=None, o=A16, lse=A16, B=2, Hq=4, Hkv=2, d=128, sk=CONTIG, sv=CONTIG,
+         scale=0.1, window=0, n_sink=0, splits=16):
+    return lib.parallax_attn_decode_paged(q, r, k, v, bt, num_pages, page, max_pages, seqlens, o,
+                                          lse, B, Hq, Hkv, d, sk, sv, scale, window, n_sink,
+                                          splits, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(splits=3), UNSUPPORTED), (dict(B=-1), INVALID),
+    (dict(Hkv=3), INVALID), (dict(Hkv=0), INVALID), (dict(page=24), INVALID),
+    (dict(page=0), INVALID), (dict(num_pages=0), INVALID), (dict(max_pages=0), INVALID),
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(o=None), INVALID),
+    (dict(q=A16 + 4), INVALID), (dict(bt=A16 + 2), INVALID), (dict(window=-1), INVALID),
+    (dict(n_sink=-1), INVALID), (dict(scale=0.0), INVALID), (dict(sk=S(8, 8, 4)), INVALID),
+])
+def test_decode_paged_rejects(lib, kw, status):
+    assert decp(lib, **kw) == status
+
+
+def test_decode_paged_empty_is_a_no_op(lib):
+    assert decp(lib, B=0, q=None, r=None, k=None, v=None, o=None, lse=None) == OK
+    # a contiguous cache (no block table) needs no power-of-two page size
+    assert decp(lib, Hq=0, bt=None, page=300) == OK
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
