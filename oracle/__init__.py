@@ -9,7 +9,9 @@ The oracle computes the Parallax forward from its definition (review page
 sec. 1 and sec. 3): softmax weights over the visible keys, the weighted key
 mean, the probe correction rho.(k_j - kbar) and the corrected weighted sum of
 values, all in fp64; and its backward (the gradients of a loss through o with
-respect to q, k, v and rho) by reverse-mode steps of the same definition.
+respect to q, k, v and rho) by reverse-mode steps of the same definition;
+exact Local Linear Attention (the probe by a conjugate-gradient solve) for
+comparison with it.
 Everything here converts arrays to contiguous float64
 and calls the C code; no arithmetic of the method lives in this file.
 """
@@ -65,6 +67,11 @@ class Oracle:
         lib.parallax_oracle_bwd.argtypes = [
             _D, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
             ctypes.c_int, ctypes.c_double, ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        lib.parallax_oracle_lla_rows.restype = ctypes.c_int
+        lib.parallax_oracle_lla_rows.argtypes = [
+            _D, _L, ctypes.c_long, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double,
+            ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+            _D, _D, _I, ctypes.c_int]
         lib.parallax_oracle_decode_ext.restype = ctypes.c_int
         lib.parallax_oracle_decode_ext.argtypes = [
             _D, _D, _D, _D, _I, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
@@ -162,6 +169,28 @@ class Oracle:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return o, lse
 
+
+    def lla_rows(self, q_rows, pos, k, v, scale, window=0, n_sink=0, max_iters=None, tol=1e-12,
+                 ridge=0.0, nthreads=None):
+        """Exact Local Linear Attention on selected rows of one (b, h) slice: the
+        p-weighted least-squares intercept, with the probe found by conjugate
+        gradients.  Returns (o [n, d], rho [n, d], CG iterations [n])."""
+        q_rows, k, v = (self._f64(x) for x in (q_rows, k, v))
+        pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+        n, d = q_rows.shape
+        if max_iters is None:
+            max_iters = 4 * d
+        o = np.zeros((n, d), dtype=np.float64)
+        rho = np.zeros((n, d), dtype=np.float64)
+        iters = np.zeros(n, dtype=np.int32)
+        rc = self.lib.parallax_oracle_lla_rows(
+            self._ptr(q_rows), pos.ctypes.data_as(_L), n, self._ptr(k), self._ptr(v),
+            k.shape[0], d, float(scale), int(window), int(n_sink), int(max_iters), float(tol),
+            float(ridge), self._ptr(o), self._ptr(rho), iters.ctypes.data_as(_I),
+            int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return o, rho, iters
 
     def decode_ext(self, q, r, k_cache, v_cache, seqlens=None, scale=None, window=0, n_sink=0,
                    nthreads=None):

@@ -537,3 +537,153 @@ int parallax_oracle_bwd(const double *q, const double *k, const double *v,
     free(work);
     return failed ? -2 : 0;
 }
+
+/*
+ * Exact Local Linear Attention (LLA), the estimator Parallax parameterises
+ * (review page "Parallax: Parameterized Local Linear Attention for Language
+ * Modeling", sec. 1-2: LLA fits a local linear model around each query and
+ * needs a per-token linear solve; tilnote note on Parallax, section on the
+ * starting point).  For query i with softmax weights p_j over its visible
+ * keys, the p-weighted least-squares fit v ~ a + B (k - q_i) has intercept
+ *
+ *     a_i = sum_j p_j (1 + rho_i . (k_j - kbar_i)) v_j,
+ *     rho_i solving  (Sigma_i + ridge I) rho_i = q_i - kbar_i,
+ *     Sigma_i = sum_j p_j (k_j - kbar_i)(k_j - kbar_i)^T,
+ *
+ * i.e. Parallax's form with the probe obtained by a solve instead of a
+ * learned projection.  The solve is done the way a kernel would do it, by
+ * conjugate gradients with matrix-free products
+ *     Sigma x = sum_j p_j (k_j - kbar) ((k_j - kbar) . x),
+ * each of which reads all visible keys again.  CG stops after max_iters
+ * iterations or once the residual norm falls below tol times the norm of
+ * q - kbar.  ridge >= 0 keeps the system definite for rows with fewer
+ * visible keys than d + 1 (the plain solve is singular there).
+ *
+ *   q_rows: [n_rows][d]; pos: [n_rows]; k, v: [n_ctx][d]
+ *   o_rows, rho_rows: [n_rows][d]; iters: [n_rows] CG iterations used
+ * Returns 0, -1 on an invalid argument, -2 when scratch memory is short.
+ */
+static void lla_row(const double *q_i, long i, const double *k, const double *v, long n_ctx,
+                    int d, double scale, long window, long n_sink, int max_iters, double tol,
+                    double ridge, double *o_i, double *rho, int *iters, double *work)
+{
+    double *p = work;                /* weights            [n_ctx] */
+    double *kbar = work + n_ctx;     /* [d] */
+    double *res = kbar + d;          /* CG residual        [d] */
+    double *dir = res + d;           /* CG direction       [d] */
+    double *Ad = dir + d;            /* Sigma dir          [d] */
+    double m = -INFINITY, ell = 0.0;
+    for (int t = 0; t < d; ++t)
+        o_i[t] = rho[t] = kbar[t] = 0.0;
+    *iters = 0;
+    for (long j = 0; j < n_ctx; ++j)
+        if (visible(i, j, window, n_sink)) {
+            p[j] = scale * dot(q_i, k + j * (long)d, d);
+            if (p[j] > m)
+                m = p[j];
+        }
+    if (m == -INFINITY)
+        return;
+    for (long j = 0; j < n_ctx; ++j)
+        if (visible(i, j, window, n_sink)) {
+            p[j] = exp(p[j] - m);
+            ell += p[j];
+        }
+    for (long j = 0; j < n_ctx; ++j)
+        if (visible(i, j, window, n_sink)) {
+            p[j] /= ell;
+            for (int t = 0; t < d; ++t)
+                kbar[t] += p[j] * k[j * (long)d + t];
+        }
+    /* CG on (Sigma + ridge I) rho = q - kbar, starting from rho = 0 */
+    double rr = 0.0;
+    for (int t = 0; t < d; ++t) {
+        res[t] = q_i[t] - kbar[t];
+        dir[t] = res[t];
+        rr += res[t] * res[t];
+    }
+    const double stop = tol * tol * rr;
+    for (int it = 0; it < max_iters && rr > stop && rr > 0.0; ++it) {
+        for (int t = 0; t < d; ++t)
+            Ad[t] = ridge * dir[t];
+        for (long j = 0; j < n_ctx; ++j) {
+            if (!visible(i, j, window, n_sink))
+                continue;
+            const double *kj = k + j * (long)d;
+            double c = 0.0;
+#if ORACLE_MUTANT == 18
+            /* planted mistake: covariance product not centred on kbar */
+            for (int t = 0; t < d; ++t)
+                c += kj[t] * dir[t];
+            c *= p[j];
+            for (int t = 0; t < d; ++t)
+                Ad[t] += c * kj[t];
+#else
+            for (int t = 0; t < d; ++t)
+                c += (kj[t] - kbar[t]) * dir[t];
+            c *= p[j];
+            for (int t = 0; t < d; ++t)
+                Ad[t] += c * (kj[t] - kbar[t]);
+#endif
+        }
+        const double dAd = dot(dir, Ad, d);
+        if (!(dAd > 0.0))
+            break;
+        const double alpha = rr / dAd;
+        double rr_new = 0.0;
+        for (int t = 0; t < d; ++t) {
+            rho[t] += alpha * dir[t];
+            res[t] -= alpha * Ad[t];
+            rr_new += res[t] * res[t];
+        }
+        for (int t = 0; t < d; ++t)
+            dir[t] = res[t] + (rr_new / rr) * dir[t];
+        rr = rr_new;
+        *iters = it + 1;
+    }
+    /* intercept: sum_j p_j (1 + rho . (k_j - kbar)) v_j */
+    for (long j = 0; j < n_ctx; ++j) {
+        if (!visible(i, j, window, n_sink))
+            continue;
+        const double *kj = k + j * (long)d;
+        double c = 0.0;
+        for (int t = 0; t < d; ++t)
+            c += rho[t] * (kj[t] - kbar[t]);
+        const double w = p[j] * (1.0 + c);
+        for (int t = 0; t < d; ++t)
+            o_i[t] += w * v[j * (long)d + t];
+    }
+}
+
+int parallax_oracle_lla_rows(const double *q_rows, const long *pos, long n_rows,
+                             const double *k, const double *v, long n_ctx, int d,
+                             double scale, long window, long n_sink, int max_iters, double tol,
+                             double ridge, double *o_rows, double *rho_rows, int *iters,
+                             int nthreads)
+{
+    if (n_rows < 0 || n_ctx < 0 || d <= 0 || n_sink < 0 || window < 0 || max_iters < 0 ||
+        !(tol >= 0.0) || !(ridge >= 0.0))
+        return -1;
+    for (long r = 0; r < n_rows; ++r)
+        if (pos[r] < -1 || pos[r] >= n_ctx)
+            return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *work = (double *)malloc(sizeof(double) * (size_t)(n_ctx + 4 * d + 1));
+        if (!work) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long r = 0; r < n_rows; ++r)
+                lla_row(q_rows + r * (long)d, pos[r], k, v, n_ctx, d, scale, window, n_sink,
+                        max_iters, tol, ridge, o_rows + r * (long)d, rho_rows + r * (long)d,
+                        iters + r, work);
+            free(work);
+        }
+    }
+    return failed ? -2 : 0;
+}

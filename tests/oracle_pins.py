@@ -256,6 +256,45 @@ def pin_decode_general(orc):
                 _close(lse[b, h], lse2[0, 0, n - 1], what="decode lse b=%d h=%d" % (b, h))
 
 
+def _weighted_fit_intercept(q, K, V, scale, vis, ridge=0.0):
+    """Intercept a of min sum_j p_j |v_j - a - B (k_j - q)|^2 + ridge |B|^2 (numpy lstsq)."""
+    p = _softmax_weights(q, K, scale, vis)
+    Kv, Vv = K[vis], V[vis]
+    X = np.concatenate([np.ones((len(p), 1)), Kv - q], axis=1) * np.sqrt(p)[:, None]
+    Y = Vv * np.sqrt(p)[:, None]
+    if ridge > 0:
+        d = K.shape[1]
+        X = np.concatenate([X, np.concatenate([np.zeros((d, 1)), np.sqrt(ridge) * np.eye(d)],
+                                              axis=1)])
+        Y = np.concatenate([Y, np.zeros((d, V.shape[1]))])
+    coef, *_ = np.linalg.lstsq(X, Y, rcond=None)
+    return coef[0]
+
+
+def pin_lla_conjugate_gradient(orc):
+    """Exact LLA by CG equals the weighted least-squares intercept (numpy lstsq),
+    with and without a ridge, and the Parallax form with the CG probe gives the
+    same output."""
+    L, d = 24, 4
+    rng_q, rng_k, rng_v = (_rand((L, d), 700 + t) for t in range(3))
+    scale = 0.5
+    for window, n_sink, ridge in ((0, 0, 0.0), (12, 2, 0.0), (0, 0, 0.3), (7, 1, 0.05)):
+        mask = visible_mask(L, window, n_sink)
+        rows = [i for i in range(L) if mask[i].sum() >= d + 2 or ridge > 0]
+        o, rho, iters = orc.lla_rows(rng_q[rows], rows, rng_k, rng_v, scale, window, n_sink,
+                                     ridge=ridge)
+        assert np.all(iters <= 4 * d)
+        for n, i in enumerate(rows):
+            ref = _weighted_fit_intercept(rng_q[i], rng_k, rng_v, scale, mask[i], ridge)
+            _close(o[n], ref, tol=1e-9, what="LLA CG intercept row %d W=%d S=%d ridge=%g"
+                   % (i, window, n_sink, ridge))
+        r_full = np.zeros((1, 1, L, d))
+        r_full[0, 0, rows] = rho
+        o_plx, _ = orc.fwd(rng_q[None, None], rng_k[None, None], rng_v[None, None], r_full,
+                           scale=scale, window=window, n_sink=n_sink)
+        _close(o_plx[0, 0, rows], o, tol=1e-10, what="Parallax with the LLA probe")
+
+
 # ---------------------------------------------------------------------------
 # Backward.  The loss is Lambda = sum dO . o (so dO is dLambda/do); lse takes
 # no part in it.  The pins below use the forward oracle (itself pinned above)
@@ -365,6 +404,6 @@ def pin_bwd_identities(orc):
 
 ALL_PINS = [pin_closed_form, pin_softmax_special_case, pin_local_linear_fit,
             pin_single_key, pin_key_translation, pin_value_affine, pin_rho_linearity,
-            pin_masks, pin_golden, pin_decode, pin_decode_general,
+            pin_masks, pin_golden, pin_decode, pin_decode_general, pin_lla_conjugate_gradient,
             pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_softmax_case,
             pin_bwd_identities]
