@@ -17,8 +17,10 @@ the fp64 CPU oracle on a bounded sample of the same prefill workload.
 
 After the timed steps, the general decode (parallax_attn_decode_paged) is
 timed on the decode workload's size in 64-token pages, with 16 and with 4 kv
-heads (GQA), reported under "decode_paged" (bytes: the cache read once); then
-the prefill backward (parallax_attn_bwd: dq, dk, dv,
+heads (GQA), reported under "decode_paged" (bytes: the cache read once); the
+fused input projections (parallax_qkvr_project, [Q|K|V|R] = X W^T for the
+1.7B-like layer: 2 x 8192 tokens, width 2048, 4 x 16 heads x 128) under
+"projection"; then the prefill backward (parallax_attn_bwd: dq, dk, dv,
 drho of the same prefill workload, with a seeded N(0,1) output gradient) is
 timed separately and reported under "backward" (algorithmic FLOP: 16d per
 visible pair); it is not part of a step.
@@ -240,6 +242,38 @@ def time_decode_paged(dcfg, steps, warmup, stream):
     return out
 
 
+def time_projection(pcfg, steps, warmup, stream):
+    """parallax_qkvr_project on the prefill workload's layer: M = B L tokens,
+    K = H d, N = 4 H d.  TFLOP/s at 2 M N K FLOP per call."""
+    import torch
+
+    from parallax_local_linear_amd import parallax_qkvr_project
+    dev = torch.device("cuda:0")
+    M, K, N = pcfg.B * pcfg.L, pcfg.H * pcfg.d, 4 * pcfg.H * pcfg.d
+    g = torch.Generator(device=dev).manual_seed(99)
+    x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn((N, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        parallax_qkvr_project(x, w, out=y, stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        parallax_qkvr_project(x, w, out=y, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2 * M * N * K
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"M": M, "N": N, "K": K, "ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4),
+                         "traffic": None, "algorithmic_flop_per_launch": flops,
+                         "kernel": "parallax_proj_kernel"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -375,6 +409,9 @@ def main():
     print("[bench] timing the general decode", file=sys.stderr, flush=True)
     res["decode_paged"] = time_decode_paged(dcfg, min(args.steps, 20),
                                             max(1, min(args.warmup, 3)), stream)
+    print("[bench] timing the projections", file=sys.stderr, flush=True)
+    res["projection"] = time_projection(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
+                                        stream)
     if not args.no_backward:
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         res["backward"] = time_backward(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),

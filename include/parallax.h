@@ -272,6 +272,28 @@ parallax_status parallax_attn_decode_paged(const void *q, const void *r,
                                            float softmax_scale, int window, int n_sink,
                                            int num_splits, void *stream);
 
+/*
+ * Fused input projections: Y = X W^T with W the row-wise stack of W_Q, W_K,
+ * W_V and the probe projection W_R (review page "Parallax: Parameterized
+ * Local Linear Attention for Language Modeling", sec. 1 and sec. 3: the
+ * probe is a learned projection of the layer input, rho_i = x_i W_R).  Row
+ * i of Y is then [q_i | k_i | v_i | rho_i]; with H heads of d features each
+ * part is H*d wide, and the prefill and decode entry points take the parts
+ * as strided [B, H, L, d] views of Y (strides b = L*ldy, h = d, l = ldy,
+ * base Y + part*H*d for tokens ordered (b, l)), without copies.
+ *
+ *   x : bf16 [M, K], row stride ldx (M tokens, K model width);
+ *   w : bf16 [N, K], row stride ldw (N = 4*H*d output features);
+ *   y : bf16 [M, N], row stride ldy; written in full, fp32 accumulation
+ *       rounded to nearest even.
+ * K must be a positive multiple of 32 and N a multiple of 8; strides
+ * multiples of 8 elements, at least the row width, below 2^24; pointers
+ * 16-byte aligned; y must not alias x or w.  M or N of 0: OK, no work.
+ */
+parallax_status parallax_qkvr_project(const void *x, const void *w, void *y, int M, int N,
+                                      int K, int64_t ldx, int64_t ldw, int64_t ldy,
+                                      void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *parallax_status_string(parallax_status s);
 

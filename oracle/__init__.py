@@ -11,7 +11,7 @@ mean, the probe correction rho.(k_j - kbar) and the corrected weighted sum of
 values, all in fp64; and its backward (the gradients of a loss through o with
 respect to q, k, v and rho) by reverse-mode steps of the same definition;
 exact Local Linear Attention (the probe by a conjugate-gradient solve) for
-comparison with it.
+comparison with it; and the fused input projections x [W_Q; W_K; W_V; W_R]^T.
 Everything here converts arrays to contiguous float64
 and calls the C code; no arithmetic of the method lives in this file.
 """
@@ -67,6 +67,9 @@ class Oracle:
         lib.parallax_oracle_bwd.argtypes = [
             _D, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_long,
             ctypes.c_int, ctypes.c_double, ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        lib.parallax_oracle_project.restype = ctypes.c_int
+        lib.parallax_oracle_project.argtypes = [_D, _D, _D, ctypes.c_long, ctypes.c_long,
+                                                ctypes.c_long, ctypes.c_int]
         lib.parallax_oracle_lla_rows.restype = ctypes.c_int
         lib.parallax_oracle_lla_rows.argtypes = [
             _D, _L, ctypes.c_long, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double,
@@ -169,6 +172,20 @@ class Oracle:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return o, lse
 
+
+    def project(self, x, w, nthreads=None):
+        """Fused projections y = x w^T: x [M, K], w [N, K] -> y [M, N] (fp64)."""
+        x, w = self._f64(x), self._f64(w)
+        M, K = x.shape
+        N = w.shape[0]
+        if w.shape[1] != K:
+            raise ValueError("x and w disagree on K")
+        y = np.zeros((M, N), dtype=np.float64)
+        rc = self.lib.parallax_oracle_project(self._ptr(x), self._ptr(w), self._ptr(y), M, N, K,
+                                              int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return y
 
     def lla_rows(self, q_rows, pos, k, v, scale, window=0, n_sink=0, max_iters=None, tol=1e-12,
                  ridge=0.0, nthreads=None):

@@ -687,3 +687,34 @@ int parallax_oracle_lla_rows(const double *q_rows, const long *pos, long n_rows,
     }
     return failed ? -2 : 0;
 }
+
+/*
+ * Fused input projections: y = x w^T with w the row-wise stack of W_Q,
+ * W_K, W_V and the probe projection W_R, so that row i of y is
+ * [q_i | k_i | v_i | rho_i] (review page "Parallax: Parameterized Local
+ * Linear Attention for Language Modeling", sec. 1 and sec. 3: the probe is
+ * a learned projection of the layer input).  Plain triple loop.
+ *   x: [M][K]; w: [N][K]; y: [M][N].  Returns 0 or -1.
+ */
+int parallax_oracle_project(const double *x, const double *w, double *y, long M, long N,
+                            long K, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (long i = 0; i < M; ++i)
+        for (long n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (long t = 0; t < K; ++t)
+#if ORACLE_MUTANT == 19
+                /* planted mistake: the weight read transposed */
+                s += x[i * K + t] * w[(t % N) * K + (n % K)];
+#else
+                s += x[i * K + t] * w[n * K + t];
+#endif
+            y[i * N + n] = s;
+        }
+    return 0;
+}

@@ -8,10 +8,10 @@ from .binding import (EXPORTED, LIBRARY, ParallaxError, load_library, parallax_a
                       parallax_attn_bwd_workspace_size, parallax_attn_decode,
                       parallax_attn_decode_paged, parallax_attn_fwd,
                       parallax_attn_fwd_train, parallax_attn_fwd_workspace_size,
-                      parallax_status_string)
+                      parallax_qkvr_project, parallax_status_string, split_qkvr)
 
 __all__ = ["EXPORTED", "LIBRARY", "ParallaxError", "load_library", "parallax_attn_bwd",
            "parallax_attn_bwd_workspace_size", "parallax_attn_decode",
            "parallax_attn_decode_paged", "parallax_attn_fwd",
            "parallax_attn_fwd_train", "parallax_attn_fwd_workspace_size",
-           "parallax_status_string"]
+           "parallax_qkvr_project", "parallax_status_string", "split_qkvr"]

@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
 # Every symbol include/parallax.h declares.
 EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_train",
             "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
-            "parallax_attn_decode_paged", "parallax_status_string")
+            "parallax_attn_decode_paged", "parallax_qkvr_project", "parallax_status_string")
 
 
 class parallax_strides(ctypes.Structure):
@@ -76,6 +76,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.parallax_attn_decode_paged.restype = ctypes.c_int
     lib.parallax_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, vp,
                                                i, i, i, i, S, S, f, i, i, i, vp]
+    lib.parallax_qkvr_project.restype = ctypes.c_int
+    lib.parallax_qkvr_project.argtypes = [vp, vp, vp, i, i, i, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, vp]
     lib.parallax_status_string.restype = ctypes.c_char_p
     lib.parallax_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -335,3 +338,36 @@ def parallax_attn_decode_paged(q, r, k_cache, v_cache, block_table=None, seqlens
         int(num_splits), _stream_handle(q.device, stream))
     _check(st)
     return out, lse
+
+
+def parallax_qkvr_project(x, w, *, out=None, stream=None):
+    """Fused projections Y = X W^T.  x: bf16 [M, K]; w: bf16 [N, K] (the stacked
+    W_Q, W_K, W_V, W_R rows).  Returns bf16 [M, N] (row i = [q_i | k_i | v_i | rho_i])."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 2)
+    M, K = x.shape
+    N, Kw = w.shape
+    if Kw != K:
+        raise ValueError("x and w disagree on K")
+    if x.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("x and w must have contiguous rows")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError("out must be a [M, N] bf16 tensor with contiguous rows")
+    st = load_library().parallax_qkvr_project(
+        x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K, x.stride(0), w.stride(0),
+        out.stride(0), _stream_handle(x.device, stream))
+    _check(st)
+    return out
+
+
+def split_qkvr(y, B, L, H, d):
+    """The four parts of a parallax_qkvr_project output [B*L, 4*H*d] as strided
+    [B, H, L, d] views (no copies): (q, k, v, rho)."""
+    if y.shape[1] != 4 * H * d or y.shape[0] != B * L:
+        raise ValueError("y must be [B*L, 4*H*d]")
+    ld = y.stride(0)
+    return tuple(torch.as_strided(y, (B, H, L, d), (L * ld, d, ld, 1), y.storage_offset() + p * H * d)
+                 for p in range(4))

@@ -49,6 +49,14 @@ struct DecodeArgs {
     float scale_log2;
 };
 
+struct ProjArgs {
+    const uint16_t *x;   // bf16 [M, K] with row stride ldx
+    const uint16_t *w;   // bf16 [N, K] with row stride ldw
+    uint16_t *y;         // bf16 [M, N] with row stride ldy
+    int64_t ldx, ldw, ldy;
+    int M, N, K;
+};
+
 struct PagedDecodeArgs {
     const uint16_t *q, *r;          // bf16 [B,Hq,d] contiguous
     const uint16_t *k, *v;          // bf16 cache: element strides along page, kv head, row
@@ -124,6 +132,8 @@ constexpr int fwd_block_rows(int d) { return 16 * fwd_waves(d); }
 
 hipError_t launch_fwd(const FwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, int d, hipStream_t stream);
+hipError_t launch_proj(const ProjArgs &a, hipStream_t stream);
+size_t proj_tiles(int M, int N);
 hipError_t launch_decode(const DecodeArgs &a, int d, int num_splits, hipStream_t stream);
 hipError_t launch_decode_paged(const PagedDecodeArgs &a, int d, int num_splits, hipStream_t stream);
 

@@ -342,4 +342,34 @@ parallax_status parallax_attn_decode_paged(const void *q, const void *r, const v
     return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
 }
 
+parallax_status parallax_qkvr_project(const void *x, const void *w, void *y, int M, int N,
+                                      int K, int64_t ldx, int64_t ldw, int64_t ldy,
+                                      void *stream) {
+    if (M < 0 || N < 0 || K < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)M * N == 0)
+        return PARALLAX_OK;
+    if (K % 32 != 0 || N % 8 != 0)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!x || !w || !y || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (ldx < K || ldw < K || ldy < N || ldx % 8 || ldw % 8 || ldy % 8)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (K == 0 || ldx >= kMaxRowStride || ldw >= kMaxRowStride || ldy >= kMaxRowStride ||
+        plx::proj_tiles(M, N) > (size_t)INT_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+    plx::ProjArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = static_cast<const uint16_t *>(w);
+    a.y = static_cast<uint16_t *>(y);
+    a.ldx = ldx;
+    a.ldw = ldw;
+    a.ldy = ldy;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    hipError_t e = plx::launch_proj(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -295,6 +295,17 @@ def pin_lla_conjugate_gradient(orc):
         _close(o_plx[0, 0, rows], o, tol=1e-10, what="Parallax with the LLA probe")
 
 
+def pin_projection(orc):
+    """Fused projections equal numpy's matmul x @ w.T; an identity block of w
+    copies the matching columns of x."""
+    x = _rand((37, 64), 801)
+    w = _rand((40, 64), 802)
+    _close(orc.project(x, w), x @ w.T, tol=1e-12, what="projection vs numpy matmul")
+    eye = np.zeros((16, 64))
+    eye[:, 8:24] = np.eye(16)
+    _close(orc.project(x, eye), x[:, 8:24], tol=0.0, what="projection with an identity block")
+
+
 # ---------------------------------------------------------------------------
 # Backward.  The loss is Lambda = sum dO . o (so dO is dLambda/do); lse takes
 # no part in it.  The pins below use the forward oracle (itself pinned above)
@@ -405,5 +416,6 @@ def pin_bwd_identities(orc):
 ALL_PINS = [pin_closed_form, pin_softmax_special_case, pin_local_linear_fit,
             pin_single_key, pin_key_translation, pin_value_affine, pin_rho_linearity,
             pin_masks, pin_golden, pin_decode, pin_decode_general, pin_lla_conjugate_gradient,
+            pin_projection,
             pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_softmax_case,
             pin_bwd_identities]

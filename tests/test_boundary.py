@@ -254,6 +254,34 @@ def test_decode_paged_empty_is_a_no_op(lib):
     assert decp(lib, Hq=0, bt=None, page=300) == OK
 
 
+def proj(lib, x=A16, w=A16, y=A16, M=64, N=64, K=64, ldx=64, ldw=64, ldy=64):
+    return lib.parallax_qkvr_project(x, w, y, M, N, K, ldx, ldw, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INVALID), (dict(K=-32), INVALID), (dict(K=48), UNSUPPORTED),
+    (dict(N=60), UNSUPPORTED), (dict(x=None), INVALID), (dict(y=A16 + 8), INVALID),
+    (dict(ldx=32), INVALID), (dict(ldy=60), INVALID), (dict(ldw=66), INVALID),
+    (dict(K=0, ldx=8, ldw=8), UNSUPPORTED),
+])
+def test_projection_rejects(lib, kw, status):
+    assert proj(lib, **kw) == status
+
+
+def test_projection_empty_is_a_no_op(lib):
+    assert proj(lib, M=0, x=None, y=None) == OK
+
+
+def test_split_qkvr_views_share_storage():
+    import torch
+    y = torch.arange(2 * 5 * 4 * 3 * 8, dtype=torch.float32).view(2 * 5, 4 * 3 * 8)
+    q, k, v, r = binding.split_qkvr(y, B=2, L=5, H=3, d=8)
+    assert q.shape == (2, 3, 5, 8) and q.data_ptr() == y.data_ptr()
+    # token (b, l) = row b*L + l; head h of part p = columns p*H*d + h*d .. +d
+    assert torch.equal(r[1, 2, 4], y[1 * 5 + 4, 3 * 24 + 2 * 8: 3 * 24 + 3 * 8])
+    assert torch.equal(k[0, 1, 3], y[3, 24 + 8: 24 + 16])
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
