@@ -90,11 +90,20 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
     const int wm = wave / 4;  // wavefront row (tokens)
     const int wn = wave % 4;  // wavefront column (features)
 
-    // Tile order: consecutive blocks walk N fastest within groups of 8 M
-    // tiles, so that concurrent workgroups share X and W tiles in L2.
+    // Tile order.  Workgroups are dealt to the 8 XCDs round-robin
+    // (blockIdx % 8), each XCD with its own L2, so the block index is first
+    // renumbered to give every XCD one contiguous run of tiles; within the
+    // run, tiles walk M fastest inside groups of GROUP M tiles, so that the
+    // workgroups running together on one XCD share their X and W tiles in
+    // that XCD's L2.
     const int n_tm = (a.M + TM - 1) / TM;
     const int n_tn = (a.N + TN - 1) / TN;
-    const int bid = blockIdx.x;
+    const int n_tiles = n_tm * n_tn;
+    const int xcd = blockIdx.x % 8;
+    const int slot = blockIdx.x / 8;
+    const int per = n_tiles / 8, extra = n_tiles % 8;
+    const int bid = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) +
+                    slot;
     constexpr int GROUP = 8;
     const int group = bid / (GROUP * n_tn);
     const int first_m = group * GROUP;
