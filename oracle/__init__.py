@@ -11,7 +11,9 @@ mean, the probe correction rho.(k_j - kbar) and the corrected weighted sum of
 values, all in fp64; and its backward (the gradients of a loss through o with
 respect to q, k, v and rho) by reverse-mode steps of the same definition;
 exact Local Linear Attention (the probe by a conjugate-gradient solve) for
-comparison with it; and the fused input projections x [W_Q; W_K; W_V; W_R]^T.
+comparison with it; the fused input projections x [W_Q; W_K; W_V; W_R]^T;
+the Walsh-Hadamard output projection alpha * (Y H / sqrt(n)) + beta; and
+Based linear attention with the second-order Taylor kernel 1 + x + x^2/2.
 Everything here converts arrays to contiguous float64
 and calls the C code; no arithmetic of the method lives in this file.
 """
@@ -70,6 +72,13 @@ class Oracle:
         lib.parallax_oracle_project.restype = ctypes.c_int
         lib.parallax_oracle_project.argtypes = [_D, _D, _D, ctypes.c_long, ctypes.c_long,
                                                 ctypes.c_long, ctypes.c_int]
+        lib.parallax_oracle_hadamard.restype = ctypes.c_int
+        lib.parallax_oracle_hadamard.argtypes = [_D, _D, _D, _D, ctypes.c_long, ctypes.c_long,
+                                                 ctypes.c_int]
+        lib.parallax_oracle_based.restype = ctypes.c_int
+        lib.parallax_oracle_based.argtypes = [_D, _D, _D, _D, ctypes.c_long, ctypes.c_long,
+                                              ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                              ctypes.c_double, ctypes.c_int]
         lib.parallax_oracle_lla_rows.restype = ctypes.c_int
         lib.parallax_oracle_lla_rows.argtypes = [
             _D, _L, ctypes.c_long, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double,
@@ -186,6 +195,41 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return y
+
+    def hadamard(self, y, alpha=None, beta=None, nthreads=None):
+        """Walsh-Hadamard output projection alpha * (y H_n / sqrt(n)) + beta with H_n
+        the Sylvester Hadamard matrix: y [M, n] (n a power of two) -> [M, n] (fp64)."""
+        y = self._f64(y)
+        M, n = y.shape
+        a = None if alpha is None else self._f64(np.broadcast_to(alpha, (n,)))
+        b = None if beta is None else self._f64(np.broadcast_to(beta, (n,)))
+        out = np.zeros((M, n), dtype=np.float64)
+        rc = self.lib.parallax_oracle_hadamard(self._ptr(y), self._ptr(a) if a is not None else None,
+                                               self._ptr(b) if b is not None else None,
+                                               self._ptr(out), M, n,
+                                               int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return out
+
+    def based(self, q, k, v, scale=None, nthreads=None):
+        """Based linear attention, causal, weights 1 + x + x^2/2 with x = scale q.k:
+        q, k [B, H, L, dk], v [B, H, L, dv] -> o [B, H, L, dv] (fp64).  scale
+        defaults to 1/sqrt(dk)."""
+        q, k, v = (self._f64(x) for x in (q, k, v))
+        B, H, L, dk = q.shape
+        dv = v.shape[-1]
+        if k.shape != q.shape or v.shape[:3] != (B, H, L):
+            raise ValueError("q, k, v shapes disagree")
+        if scale is None:
+            scale = dk ** -0.5
+        o = np.zeros((B, H, L, dv), dtype=np.float64)
+        rc = self.lib.parallax_oracle_based(self._ptr(q), self._ptr(k), self._ptr(v),
+                                            self._ptr(o), B, H, L, dk, dv, float(scale),
+                                            int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return o
 
     def lla_rows(self, q_rows, pos, k, v, scale, window=0, n_sink=0, max_iters=None, tol=1e-12,
                  ridge=0.0, nthreads=None):

@@ -1,6 +1,8 @@
 /*
  * Plain fp64 CPU oracle for the Parallax attention forward (prefill rows and
- * decode rows) and for the prefill backward.
+ * decode rows) and for the prefill backward; at the end of the file, the
+ * exact Local Linear Attention solve, the fused input projections, the
+ * Walsh-Hadamard output projection and Based linear attention.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
  * GPU kernels are compared against.  Only the tests, the smoke check and the
@@ -716,5 +718,159 @@ int parallax_oracle_project(const double *x, const double *w, double *y, long M,
 #endif
             y[i * N + n] = s;
         }
+    return 0;
+}
+
+/*
+ * Walsh-Hadamard output projection (review page "Rethinking Attention
+ * Output Projection: Structured Hadamard Transforms for Efficient
+ * Transformers", sec. 2 "Methodology"): the dense output projection of
+ * multi-head attention is replaced by a fixed Walsh-Hadamard transform of
+ * the concatenated head outputs followed by a learned per-feature affine
+ * map,  out = alpha (.) (Y H) + beta.
+ *
+ * Readings: H is the Sylvester-ordered Hadamard matrix of order n (n a power
+ * of two) scaled by 1/sqrt(n), so that it is orthogonal and preserves the
+ * l2 norm of each row, as the page states; alpha and beta are length-n
+ * vectors indexed by the output feature.  NULL alpha means all ones, NULL
+ * beta all zeros.
+ *
+ * Steps: (1) build H_n by Sylvester's doubling, H_1 = [1],
+ * H_2m = [[H_m, H_m], [H_m, -H_m]]; (2) the plain product Y H_n / sqrt(n);
+ * (3) the affine map.
+ *   y: [M][n]; out: [M][n].  Returns 0, or -1 for bad sizes.
+ */
+int parallax_oracle_hadamard(const double *y, const double *alpha, const double *beta,
+                             double *out, long M, long n, int nthreads)
+{
+    if (M < 0 || n < 1 || (n & (n - 1)) != 0)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    double *h = malloc(sizeof(double) * (size_t)n * (size_t)n);
+    if (!h)
+        return -1;
+    h[0] = 1.0;
+    for (long m = 1; m < n; m *= 2)
+        for (long i = 0; i < m; ++i)
+            for (long j = 0; j < m; ++j) {
+                const double e = h[i * n + j];
+                h[i * n + j + m] = e;
+#if ORACLE_MUTANT == 21
+                /* planted mistake: the sign of the lower-left block flipped */
+                h[(i + m) * n + j] = -e;
+                h[(i + m) * n + j + m] = e;
+#else
+                h[(i + m) * n + j] = e;
+                h[(i + m) * n + j + m] = -e;
+#endif
+            }
+#if ORACLE_MUTANT == 20
+    /* planted mistake: the normalisation dropped */
+    const double norm = 1.0;
+#else
+    const double norm = 1.0 / sqrt((double)n);
+#endif
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (long i = 0; i < M; ++i)
+        for (long c = 0; c < n; ++c) {
+            double s = 0.0;
+            for (long t = 0; t < n; ++t)
+#if ORACLE_MUTANT == 22
+                /* planted mistake: alpha applied to the input features */
+                s += y[i * n + t] * (alpha ? alpha[t] : 1.0) * h[t * n + c];
+#else
+                s += y[i * n + t] * h[t * n + c];
+#endif
+            s *= norm;
+#if ORACLE_MUTANT == 23
+            /* planted mistake: beta added before the scaling by alpha */
+            if (beta)
+                s += beta[c];
+#endif
+#if ORACLE_MUTANT != 22
+            if (alpha)
+                s *= alpha[c];
+#endif
+#if ORACLE_MUTANT != 23
+            if (beta)
+                s += beta[c];
+#endif
+            out[i * n + c] = s;
+        }
+    free(h);
+    return 0;
+}
+
+/*
+ * Based linear attention (review page "Simple linear attention language
+ * models balance the recall-throughput tradeoff", "Proposed method"): the
+ * linear-attention half of the Based hybrid, whose other half is softmax
+ * attention over a small sliding window.  Linear attention replaces
+ * exp(scale q.k) by a kernel phi(q).phi(k), so that the causal sum can be
+ * carried as a fixed-size state; the feature dimension of phi sets the state
+ * size.
+ *
+ * Reading (the page leaves phi open): phi is the feature map of the
+ * second-order Taylor expansion of exp, so that with x = scale * q_i . k_j
+ *
+ *     w_ij = phi(q_i) . phi(k_j) = 1 + x + x^2 / 2        (> 0 for every x)
+ *     o_i  = sum_{j <= i} w_ij v_j / sum_{j <= i} w_ij
+ *
+ * q and k have the feature dimension dk, v has dv; the sum is causal over
+ * all earlier positions (no window).  Written out pairwise, as defined.
+ *   q, k: [B][H][L][dk]; v, o: [B][H][L][dv].  Returns 0 or -1.
+ */
+int parallax_oracle_based(const double *q, const double *k, const double *v, double *o,
+                          long B, long H, long L, long dk, long dv, double scale,
+                          int nthreads)
+{
+    if (B < 0 || H < 0 || L < 0 || dk < 1 || dv < 1)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    const long rows = B * H * L;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        const long bh = r / L, i = r % L;
+        const double *qi = q + r * dk;
+        const double *kb = k + bh * L * dk;
+        const double *vb = v + bh * L * dv;
+        double *oi = o + r * dv;
+        for (long e = 0; e < dv; ++e)
+            oi[e] = 0.0;
+        double den = 0.0;
+#if ORACLE_MUTANT == 25
+        /* planted mistake: the query's own key left out */
+        for (long j = 0; j < i; ++j) {
+#else
+        for (long j = 0; j <= i; ++j) {
+#endif
+            double dot = 0.0;
+            for (long t = 0; t < dk; ++t)
+                dot += qi[t] * kb[j * dk + t];
+            const double x = scale * dot;
+#if ORACLE_MUTANT == 24
+            /* planted mistake: the second-order term dropped */
+            const double w = 1.0 + x;
+#elif ORACLE_MUTANT == 27
+            /* planted mistake: the square taken of the unscaled product */
+            const double w = 1.0 + x + 0.5 * dot * dot;
+#else
+            const double w = 1.0 + x + 0.5 * x * x;
+#endif
+#if ORACLE_MUTANT == 26
+            /* planted mistake: normalised by the number of keys */
+            den += 1.0;
+#else
+            den += w;
+#endif
+            for (long e = 0; e < dv; ++e)
+                oi[e] += w * vb[j * dv + e];
+        }
+        if (den > 0.0)
+            for (long e = 0; e < dv; ++e)
+                oi[e] /= den;
+    }
     return 0;
 }

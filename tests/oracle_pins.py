@@ -19,11 +19,22 @@ Facts used (none of them re-types the oracle's own two-pass algorithm):
   * a hand-worked example with exact rational results (tests/golden);
   * backward: central differences of the (pinned) forward, torch's autograd
     of softmax attention at rho = 0, and exact identities (key translation,
-    value shift, linearity in V, affinity in rho).
+    value shift, linearity in V, affinity in rho);
+  * Walsh-Hadamard output projection: scipy.linalg.hadamard and the
+    popcount closed form of the Sylvester matrix, orthogonality (norms kept,
+    the transform its own inverse), and the closed form of a constant row;
+  * Based linear attention: the state-space recurrence of the explicit
+    feature map, the weight as a function of x recovered from outputs (a
+    polynomial of degree two matching exp's value and first two derivatives
+    at 0), softmax attention as its small-x limit, and closed forms (equal
+    weights give prefix means, one key gives its value).
 Sources: review page "Parallax: Parameterized Local Linear Attention for
 Language Modeling", sec. 1-3; tilnote note on Parallax, section on Local
 Linear Attention as the starting point; "Sliding-window beats linear
-attention" review, sec. 1 (windows and sinks).
+attention" review, sec. 1 (windows and sinks); "Rethinking Attention Output
+Projection: Structured Hadamard Transforms for Efficient Transformers"
+review, sec. 2; "Simple linear attention language models balance the
+recall-throughput tradeoff" review, "Proposed method".
 """
 from __future__ import annotations
 
@@ -413,9 +424,137 @@ def pin_bwd_identities(orc):
                what="drho . rho" + tag)
 
 
+# ---------------------------------------------------------------------------
+# Walsh-Hadamard output projection and Based linear attention.
+
+def pin_hadamard_library(orc):
+    """sqrt(n) times the transform of the identity is scipy.linalg.hadamard(n);
+    entry (k, c) has the sign (-1)^popcount(k & c)."""
+    from scipy.linalg import hadamard
+    for n in (1, 2, 4, 8, 16, 64, 256, 512):
+        h = orc.hadamard(np.eye(n)) * np.sqrt(n)
+        _close(h, hadamard(n).astype(np.float64), tol=1e-12, what="H_%d vs scipy" % n)
+    n = 128
+    h = orc.hadamard(np.eye(n)) * np.sqrt(n)
+    kk, cc = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    sign = 1.0 - 2.0 * (np.vectorize(lambda a: bin(a).count("1"))(kk & cc) % 2)
+    _close(h, sign, tol=1e-12, what="H_128 vs popcount signs")
+
+
+def pin_hadamard_orthogonal(orc):
+    """Without the affine map the transform keeps every row's l2 norm and is its
+    own inverse (the normalised Sylvester matrix is symmetric and orthogonal)."""
+    y = _rand((6, 2048), 901)
+    t = orc.hadamard(y)
+    _close(np.linalg.norm(t, axis=1), np.linalg.norm(y, axis=1), tol=1e-12, what="norms kept")
+    _close(orc.hadamard(t), y, tol=1e-12, what="transform twice is the identity")
+
+
+def pin_hadamard_affine(orc):
+    """A constant row c maps to c sqrt(n) at feature 0 and 0 elsewhere, so the
+    output is alpha_0 c sqrt(n) + beta_0 at 0 and beta elsewhere; for any
+    input, alpha and beta act on the transformed features."""
+    n = 256
+    alpha, beta = _rand(n, 902) + 2.0, _rand(n, 903)
+    c = 0.75
+    out = orc.hadamard(np.full((1, n), c), alpha, beta)[0]
+    want = beta.copy()
+    want[0] += alpha[0] * c * np.sqrt(n)
+    _close(out, want, tol=1e-12, what="constant row")
+    y = _rand((5, n), 904)
+    _close(orc.hadamard(y, alpha, beta), alpha * orc.hadamard(y) + beta, tol=1e-12,
+           what="affine map after the transform")
+
+
+def _based_features(u, scale):
+    """phi(u) = [1, sqrt(scale) u, (scale / sqrt 2) vec(u u^T)], so that
+    phi(q) . phi(k) = 1 + x + x^2 / 2 with x = scale q . k."""
+    quad = np.einsum("...a,...b->...ab", u, u).reshape(u.shape[:-1] + (-1,))
+    one = np.ones(u.shape[:-1] + (1,))
+    return np.concatenate([one, np.sqrt(scale) * u, scale / np.sqrt(2.0) * quad], axis=-1)
+
+
+def pin_based_recurrence(orc):
+    """The causal sum equals linear attention's recurrence on the explicit
+    feature map: state S_i = S_{i-1} + phi(k_i) [v_i, 1]^T, o_i = phi(q_i) S_i
+    split into numerator and denominator."""
+    for (dk, dv, L, scale) in [(4, 3, 9, 0.5), (3, 5, 17, 0.9)]:
+        q, k, v = (_rand((1, 2, L, dd), 910 + dd + t) for t, dd in enumerate((dk, dk, dv)))
+        o = orc.based(q, k, v, scale=scale)
+        for h in range(2):
+            fq, fk = _based_features(q[0, h], scale), _based_features(k[0, h], scale)
+            vv = np.concatenate([v[0, h], np.ones((L, 1))], axis=1)
+            state = np.zeros((fq.shape[1], dv + 1))
+            for i in range(L):
+                state += np.outer(fk[i], vv[i])
+                num = fq[i] @ state
+                _close(o[0, h, i], num[:dv] / num[dv], tol=1e-12,
+                       what="recurrence dk=%d row %d" % (dk, i))
+
+
+def pin_based_taylor_weight(orc):
+    """The weight of a key as a function of x = scale q.k, read off outputs
+    (key 0 at x = 0 with value 0, key 1 at x with value 1: o_1 = w / (1 + w)),
+    is a polynomial of degree two with exp's value, slope and curvature at 0,
+    i.e. the second-order Taylor polynomial of exp."""
+    scale, h = 0.5, 0.25
+    xs = h * np.arange(-3, 4)
+    ws = []
+    for x in xs:
+        q = np.array([[[[1.0, 2.0], [1.0, 2.0]]]])
+        kx = x / (scale * 5.0)
+        k = np.array([[[[0.0, 0.0], [kx, 2.0 * kx]]]])
+        v = np.array([[[[0.0], [1.0]]]])
+        o = orc.based(q, k, v, scale=scale)[0, 0, 1, 0]
+        ws.append(o / (1.0 - o))
+    ws = np.array(ws)
+    c = 3  # index of x = 0
+    _close(ws[c], 1.0, tol=1e-12, what="w(0)")
+    _close((ws[c + 1] - ws[c - 1]) / (2 * h), 1.0, tol=1e-11, what="slope at 0")
+    _close((ws[c + 1] - 2 * ws[c] + ws[c - 1]) / h ** 2, 1.0, tol=1e-10, what="curvature at 0")
+    third = ws[3:] - 3 * ws[2:-1] + 3 * ws[1:-2] - ws[:-3]
+    _close(third, np.zeros_like(third), tol=1e-12, what="third differences vanish")
+
+
+def pin_based_closed_forms(orc):
+    """q = 0 gives equal weights, so o_i is the mean of v_0..v_i; row 0 sees
+    only its own key, so o_0 = v_0; o is affine in the values."""
+    B, H, L, dk, dv = 1, 2, 11, 4, 6
+    k, v = _rand((B, H, L, dk), 920), _rand((B, H, L, dv), 921)
+    o = orc.based(np.zeros((B, H, L, dk)), k, v)
+    means = np.cumsum(v, axis=2) / np.arange(1, L + 1)[None, None, :, None]
+    _close(o, means, tol=1e-12, what="prefix means")
+    q = _rand((B, H, L, dk), 922)
+    o = orc.based(q, k, v)
+    _close(o[:, :, 0], v[:, :, 0], tol=1e-12, what="row 0")
+    shift = _rand(dv, 923)
+    _close(orc.based(q, k, 2.5 * v + shift), 2.5 * o + shift, tol=1e-12, what="value affine")
+
+
+def pin_based_softmax_limit(orc):
+    """For small x the weight 1 + x + x^2/2 is exp(x) (1 - r) with
+    |r| <= |x|^3 e^|x| / 6, so the output stays within
+    2 max|r| / (1 - max|r|) * max|v - o| of softmax attention (the Parallax
+    oracle at rho = 0)."""
+    B, H, L, d = 1, 2, 40, 8
+    q, k = (_rand((B, H, L, d), 930 + t, scale=0.3) for t in range(2))
+    v = _rand((B, H, L, d), 932)
+    scale = d ** -0.5
+    o = orc.based(q, k, v, scale=scale)
+    o_sm, _ = orc.fwd(q, k, v, np.zeros_like(q), scale=scale)
+    xmax = float(np.max(np.abs(scale * np.einsum("bhid,bhjd->bhij", q, k))))
+    rmax = xmax ** 3 * np.exp(xmax) / 6.0
+    bound = 2.0 * rmax / (1.0 - rmax) * 2.0 * float(np.max(np.abs(v)))
+    err = float(np.max(np.abs(o - o_sm)))
+    assert err <= bound, "softmax limit: %.3e > %.3e" % (err, bound)
+
+
 ALL_PINS = [pin_closed_form, pin_softmax_special_case, pin_local_linear_fit,
             pin_single_key, pin_key_translation, pin_value_affine, pin_rho_linearity,
             pin_masks, pin_golden, pin_decode, pin_decode_general, pin_lla_conjugate_gradient,
             pin_projection,
             pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_softmax_case,
-            pin_bwd_identities]
+            pin_bwd_identities,
+            pin_hadamard_library, pin_hadamard_orthogonal, pin_hadamard_affine,
+            pin_based_recurrence, pin_based_taylor_weight, pin_based_closed_forms,
+            pin_based_softmax_limit]

@@ -8,7 +8,7 @@ import pytest
 import oracle
 from oracle_pins import ALL_PINS
 
-N_MUTANTS = 19
+N_MUTANTS = 27
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
