@@ -20,7 +20,11 @@ timed on the decode workload's size in 64-token pages, with 16 and with 4 kv
 heads (GQA), reported under "decode_paged" (bytes: the cache read once); the
 fused input projections (parallax_qkvr_project, [Q|K|V|R] = X W^T for the
 1.7B-like layer: 2 x 8192 tokens, width 2048, 4 x 16 heads x 128) under
-"projection"; then the prefill backward (parallax_attn_bwd: dq, dk, dv,
+"projection"; the Walsh-Hadamard output projection (parallax_hadamard_out on
+the prefill's fp32 output [2, 16, 8192, 128] -> bf16 [16384, 2048], with
+alpha and beta; bytes: the output read once and y written once) under
+"hadamard", with the time of a dense 2048 x 2048 output projection by the
+projection kernel beside it for context; then the prefill backward (parallax_attn_bwd: dq, dk, dv,
 drho of the same prefill workload, with a seeded N(0,1) output gradient) is
 timed separately and reported under "backward" (algorithmic FLOP: 16d per
 visible pair); it is not part of a step.
@@ -47,6 +51,8 @@ KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_fwd.hip"),
     "decode": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
     "backward": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_bwd.hip"),
+    "projection": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_proj.hip"),
+    "hadamard": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_hadamard.hip"),
 }
 
 
@@ -270,8 +276,57 @@ def time_projection(pcfg, steps, warmup, stream):
     return {"M": M, "N": N, "K": K, "ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_MFMA_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4),
-                         "traffic": None, "algorithmic_flop_per_launch": flops,
+                         "traffic": measured_traffic("projection"),
+                         "algorithmic_flop_per_launch": flops,
                          "kernel": "parallax_proj_kernel"}}
+
+
+def _time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_hadamard(pcfg, steps, warmup, stream):
+    """parallax_hadamard_out on the prefill workload's fp32 output: bytes =
+    4 B L H d read + 2 B L H d written + alpha and beta; and, for context, a
+    dense n x n output projection of the same tokens (bf16, projection kernel)."""
+    import torch
+
+    from parallax_local_linear_amd import parallax_hadamard_out, parallax_qkvr_project
+    dev = torch.device("cuda:0")
+    B, H, L, d = pcfg.B, pcfg.H, pcfg.L, pcfg.d
+    n, M = H * d, B * L
+    g = torch.Generator(device=dev).manual_seed(98)
+    o = torch.randn((B, H, L, d), generator=g, device=dev)
+    alpha = 1.0 + 0.1 * torch.randn((n,), generator=g, device=dev)
+    beta = 0.1 * torch.randn((n,), generator=g, device=dev)
+    y = torch.empty((B, L, n), dtype=torch.bfloat16, device=dev)
+    ms = _time_calls(lambda: parallax_hadamard_out(o, alpha, beta, out=y, stream=stream),
+                     steps, warmup, stream)
+    nbytes = M * n * 4 + M * n * 2 + 2 * n * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    x = torch.randn((M, n), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn((n, n), generator=g, device=dev) * n ** -0.5).to(torch.bfloat16)
+    yd = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+    ms_dense = _time_calls(lambda: parallax_qkvr_project(x, w, out=yd, stream=stream),
+                           steps, warmup, stream)
+    return {"B": B, "H": H, "L": L, "d": d, "ms": round(ms, 4), "value": round(gbs, 1),
+            "unit": "GB/s", "dense_output_projection_ms": round(ms_dense, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("hadamard"),
+                         "algorithmic_bytes_per_launch": nbytes,
+                         "kernel": "parallax_hadamard_kernel<11>"}}
 
 
 def main():
@@ -412,6 +467,9 @@ def main():
     print("[bench] timing the projections", file=sys.stderr, flush=True)
     res["projection"] = time_projection(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
                                         stream)
+    print("[bench] timing the Hadamard output projection", file=sys.stderr, flush=True)
+    res["hadamard"] = time_hadamard(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
+                                    stream)
     if not args.no_backward:
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         res["backward"] = time_backward(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),

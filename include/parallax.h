@@ -294,6 +294,34 @@ parallax_status parallax_qkvr_project(const void *x, const void *w, void *y, int
                                       int K, int64_t ldx, int64_t ldw, int64_t ldy,
                                       void *stream);
 
+/*
+ * Walsh-Hadamard output projection (review page "Rethinking Attention
+ * Output Projection: Structured Hadamard Transforms for Efficient
+ * Transformers", sec. 2 "Methodology"): in place of the dense output
+ * projection, the concatenated head outputs of each token are mixed by a
+ * fixed Walsh-Hadamard transform and rescaled per feature,
+ *
+ *     y_t = alpha (.) (O_t H_n / sqrt(n)) + beta,   n = H * d,
+ *
+ * where O_t = [o_t(head 0) | ... | o_t(head H-1)] and H_n is the Sylvester
+ * Hadamard matrix (entry (i, c) = (-1)^popcount(i & c)); with the 1/sqrt(n)
+ * factor the transform is orthogonal and keeps each row's l2 norm.
+ *
+ *   o     : fp32 [B, H, L, d] (an attention output), element strides so,
+ *           d contiguous; 16-byte aligned base, strides multiples of 4.
+ *           A plain row-major [M, n] matrix is B = M, L = 1, H = n / d with
+ *           strides (n, d, anything).
+ *   alpha, beta : fp32 [n], 16-byte aligned, or NULL (ones / zeros).
+ *   y     : bf16 [B * L, n], rows ordered (b, l), row stride ldy (a multiple
+ *           of 4, at least n); 8-byte aligned; fp32 arithmetic, rounded to
+ *           nearest even.  Must not alias o, alpha or beta.
+ * d is 64 or 128 and n = H * d a power of two in [256, 4096]
+ * (PARALLAX_ERR_UNSUPPORTED otherwise).  B * L == 0: OK, no work.
+ */
+parallax_status parallax_hadamard_out(const float *o, parallax_strides so, int B, int H, int L,
+                                      int d, const float *alpha, const float *beta, void *y,
+                                      int64_t ldy, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *parallax_status_string(parallax_status s);
 

@@ -1,4 +1,6 @@
-"""Parallax (parameterized Local Linear Attention) forward and backward on AMD MI355X.
+"""Parallax (parameterized Local Linear Attention) forward and backward on AMD MI355X,
+with the kernels around it: fused input projections, a Walsh-Hadamard output
+projection and Based linear attention.
 
 The compute path is the gfx950 HIP library ``libparallax.so`` (C ABI in
 ``include/parallax.h``); this package only builds it and marshals torch
@@ -8,10 +10,11 @@ from .binding import (EXPORTED, LIBRARY, ParallaxError, load_library, parallax_a
                       parallax_attn_bwd_workspace_size, parallax_attn_decode,
                       parallax_attn_decode_paged, parallax_attn_fwd,
                       parallax_attn_fwd_train, parallax_attn_fwd_workspace_size,
-                      parallax_qkvr_project, parallax_status_string, split_qkvr)
+                      parallax_hadamard_out, parallax_qkvr_project, parallax_status_string,
+                      split_qkvr)
 
 __all__ = ["EXPORTED", "LIBRARY", "ParallaxError", "load_library", "parallax_attn_bwd",
            "parallax_attn_bwd_workspace_size", "parallax_attn_decode",
            "parallax_attn_decode_paged", "parallax_attn_fwd",
            "parallax_attn_fwd_train", "parallax_attn_fwd_workspace_size",
-           "parallax_qkvr_project", "parallax_status_string", "split_qkvr"]
+           "parallax_hadamard_out", "parallax_qkvr_project", "parallax_status_string", "split_qkvr"]

@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
 # Every symbol include/parallax.h declares.
 EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_train",
             "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
-            "parallax_attn_decode_paged", "parallax_qkvr_project", "parallax_status_string")
+            "parallax_attn_decode_paged", "parallax_qkvr_project", "parallax_hadamard_out",
+            "parallax_status_string")
 
 
 class parallax_strides(ctypes.Structure):
@@ -79,6 +80,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.parallax_qkvr_project.restype = ctypes.c_int
     lib.parallax_qkvr_project.argtypes = [vp, vp, vp, i, i, i, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int64, vp]
+    lib.parallax_hadamard_out.restype = ctypes.c_int
+    lib.parallax_hadamard_out.argtypes = [vp, S, i, i, i, i, vp, vp, vp, ctypes.c_int64, vp]
     lib.parallax_status_string.restype = ctypes.c_char_p
     lib.parallax_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -359,6 +362,37 @@ def parallax_qkvr_project(x, w, *, out=None, stream=None):
     st = load_library().parallax_qkvr_project(
         x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K, x.stride(0), w.stride(0),
         out.stride(0), _stream_handle(x.device, stream))
+    _check(st)
+    return out
+
+
+def parallax_hadamard_out(o, alpha=None, beta=None, *, out=None, stream=None):
+    """Walsh-Hadamard output projection y = alpha * (O H_n / sqrt(n)) + beta.
+
+    o: fp32 [B, H, L, d] attention output (any strides, d contiguous); the
+    heads of each token are concatenated to n = H*d features.  alpha, beta:
+    fp32 [n] or None.  Returns bf16 [B, L, n] (or writes ``out``, a bf16
+    [B*L, n] or [B, L, n] tensor with contiguous rows)."""
+    _need(o, "o", torch.float32, 4)
+    B, H, L, d = o.shape
+    n = H * d
+    for t, name in ((alpha, "alpha"), (beta, "beta")):
+        if t is not None:
+            _need(t, name, torch.float32, 1)
+            if t.shape[0] != n or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous fp32 [%d] tensor" % (name, n))
+    if out is None:
+        out = torch.empty((B, L, n), dtype=torch.bfloat16, device=o.device)
+    if out.dtype != torch.bfloat16 or out.device.type != "cuda":
+        raise TypeError("out must be a bf16 device tensor")
+    rows = out.view(-1, n) if out.dim() == 3 and out.is_contiguous() else out
+    if rows.dim() != 2 or tuple(rows.shape) != (B * L, n) or rows.stride(1) != 1:
+        raise ValueError("out must be [B*L, n] (or contiguous [B, L, n]) with contiguous rows")
+    st = load_library().parallax_hadamard_out(
+        o.data_ptr(), _strides(o), B, H, L, d,
+        alpha.data_ptr() if alpha is not None else None,
+        beta.data_ptr() if beta is not None else None,
+        rows.data_ptr(), rows.stride(0), _stream_handle(o.device, stream))
     _check(st)
     return out
 

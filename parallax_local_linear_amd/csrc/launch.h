@@ -57,6 +57,17 @@ struct ProjArgs {
     int M, N, K;
 };
 
+struct HadArgs {
+    const float *o;                 // fp32 [B, H, L, d], element strides below, d contiguous
+    int64_t o_b, o_h, o_l;
+    const float *alpha, *beta;      // fp32 [n] or nullptr (ones / zeros)
+    uint16_t *y;                    // bf16 [B * L, n], row stride ldy; rows ordered (b, l)
+    int64_t ldy;
+    int M;                          // B * L (< 2^31)
+    int L;
+    int log2d;                      // feature index i reads head i >> log2d, feature i & (d - 1)
+};
+
 struct PagedDecodeArgs {
     const uint16_t *q, *r;          // bf16 [B,Hq,d] contiguous
     const uint16_t *k, *v;          // bf16 cache: element strides along page, kv head, row
@@ -133,6 +144,8 @@ constexpr int fwd_block_rows(int d) { return 16 * fwd_waves(d); }
 hipError_t launch_fwd(const FwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_proj(const ProjArgs &a, hipStream_t stream);
+hipError_t launch_hadamard(const HadArgs &a, int log2n, hipStream_t stream);
+int64_t hadamard_blocks(int64_t M, int log2n);
 size_t proj_tiles(int M, int N);
 hipError_t launch_decode(const DecodeArgs &a, int d, int num_splits, hipStream_t stream);
 hipError_t launch_decode_paged(const PagedDecodeArgs &a, int d, int num_splits, hipStream_t stream);

@@ -372,4 +372,41 @@ parallax_status parallax_qkvr_project(const void *x, const void *w, void *y, int
     return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
 }
 
+parallax_status parallax_hadamard_out(const float *o, parallax_strides so, int B, int H, int L,
+                                      int d, const float *alpha, const float *beta, void *y,
+                                      int64_t ldy, void *stream) {
+    if (B < 0 || H < 0 || L < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return PARALLAX_ERR_UNSUPPORTED;
+    const int64_t n = (int64_t)H * d;
+    if ((int64_t)B * L == 0)
+        return PARALLAX_OK;
+    if (n < 256 || n > 4096 || (n & (n - 1)) != 0)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!o || !y || !aligned(o, 16) || !aligned(y, 8) || !aligned(alpha, 16) ||
+        !aligned(beta, 16) || !f32_strides_ok(so) || ldy < n || ldy % 4 != 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    int log2n = 0;
+    while ((int64_t(1) << log2n) < n)
+        ++log2n;
+    const int64_t M = (int64_t)B * L;
+    if (M > (int64_t)INT_MAX - 256 || plx::hadamard_blocks(M, log2n) > (int64_t)INT_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+    plx::HadArgs a;
+    a.o = o;
+    a.o_b = so.b;
+    a.o_h = so.h;
+    a.o_l = so.l;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.y = static_cast<uint16_t *>(y);
+    a.ldy = ldy;
+    a.M = (int)M;
+    a.L = L;
+    a.log2d = d == 64 ? 6 : 7;
+    hipError_t e = plx::launch_hadamard(a, log2n, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -272,6 +272,29 @@ def test_projection_empty_is_a_no_op(lib):
     assert proj(lib, M=0, x=None, y=None) == OK
 
 
+def had(lib, o=A16, so=S(16 * 8 * 128, 8 * 128, 128), B=2, H=16, L=8, d=128, alpha=None,
+        beta=None, y=A16, ldy=2048):
+    return lib.parallax_hadamard_out(o, so, B, H, L, d, alpha, beta, y, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(L=-3), INVALID), (dict(H=-1), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(H=3, ldy=384), UNSUPPORTED),
+    (dict(H=1, ldy=128), UNSUPPORTED), (dict(H=64, ldy=8192), UNSUPPORTED),
+    (dict(o=None), INVALID), (dict(y=None), INVALID), (dict(o=A16 + 4), INVALID),
+    (dict(y=A16 + 2), INVALID), (dict(alpha=A16 + 4), INVALID), (dict(beta=A16 + 8), INVALID),
+    (dict(ldy=2044), INVALID), (dict(ldy=2050), INVALID),
+    (dict(so=S(16 * 8 * 128, 8 * 128, 130)), INVALID), (dict(so=S(-4, 1024, 128)), INVALID),
+])
+def test_hadamard_rejects(lib, kw, status):
+    assert had(lib, **kw) == status
+
+
+def test_hadamard_empty_is_a_no_op(lib):
+    assert had(lib, B=0, o=None, y=None) == OK
+    assert had(lib, L=0, o=None, y=None) == OK
+
+
 def test_split_qkvr_views_share_storage():
     import torch
     y = torch.arange(2 * 5 * 4 * 3 * 8, dtype=torch.float32).view(2 * 5, 4 * 3 * 8)
