@@ -24,7 +24,11 @@ fused input projections (parallax_qkvr_project, [Q|K|V|R] = X W^T for the
 the prefill's fp32 output [2, 16, 8192, 128] -> bf16 [16384, 2048], with
 alpha and beta; bytes: the output read once and y written once) under
 "hadamard", with the time of a dense 2048 x 2048 output projection by the
-projection kernel beside it for context; then the prefill backward (parallax_attn_bwd: dq, dk, dv,
+projection kernel beside it for context; Based linear attention
+(parallax_based_fwd on 2 x 16 heads x 8192 tokens, 16 query/key and 128
+value features; bytes: q, k, v read once and the fp32 output written once;
+and one parallax_based_decode step for 64 x 16 heads, bytes: the fp32 state
+read and written) under "based"; then the prefill backward (parallax_attn_bwd: dq, dk, dv,
 drho of the same prefill workload, with a seeded N(0,1) output gradient) is
 timed separately and reported under "backward" (algorithmic FLOP: 16d per
 visible pair); it is not part of a step.
@@ -53,6 +57,7 @@ KERNEL_SOURCES = {
     "backward": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_bwd.hip"),
     "projection": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_proj.hip"),
     "hadamard": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_hadamard.hip"),
+    "based": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_based.hip"),
 }
 
 
@@ -329,6 +334,53 @@ def time_hadamard(pcfg, steps, warmup, stream):
                          "kernel": "parallax_hadamard_kernel<11>"}}
 
 
+def time_based(steps, warmup, stream):
+    """parallax_based_fwd on the Based workload, and one decode step per
+    (batch, head) for 64 sequences x 16 heads on the state a prefill returns."""
+    import torch
+
+    from parallax_local_linear_amd import (parallax_based_decode, parallax_based_fwd,
+                                           parallax_based_workspace_size, workloads)
+    cfg = workloads.BASED
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.based_inputs(cfg, device=dev)
+    o = torch.empty((cfg.B, cfg.H, cfg.L, cfg.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(parallax_based_workspace_size(cfg.B, cfg.H, cfg.L, cfg.dk, cfg.dv),
+                     dtype=torch.uint8, device=dev)
+    ms = _time_calls(lambda: parallax_based_fwd(q, k, v, scale=cfg.scale, out=o, workspace=ws,
+                                                stream=stream), steps, warmup, stream)
+    tokens = cfg.B * cfg.H * cfg.L
+    nbytes = tokens * (2 * cfg.dk * 2 + cfg.dv * 2 + cfg.dv * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # decode: 64 sequences x 16 heads, state of a 4096-token prefill
+    Bd = 64
+    g = torch.Generator(device=dev).manual_seed(97)
+    qd, kd = (torch.randn((Bd, cfg.H, cfg.dk), generator=g, device=dev).to(torch.bfloat16)
+              for _ in range(2))
+    vd = torch.randn((Bd, cfg.H, cfg.dv), generator=g, device=dev).to(torch.bfloat16)
+    kp = torch.randn((Bd, cfg.H, 512, cfg.dk), generator=g, device=dev).to(torch.bfloat16)
+    vp = torch.randn((Bd, cfg.H, 512, cfg.dv), generator=g, device=dev).to(torch.bfloat16)
+    _, state = parallax_based_fwd(kp, kp, vp, scale=cfg.scale, return_state=True, stream=stream)
+    od = torch.empty((Bd, cfg.H, cfg.dv), dtype=torch.float32, device=dev)
+    ms_d = _time_calls(lambda: parallax_based_decode(qd, kd, vd, state, scale=cfg.scale, out=od,
+                                                     stream=stream), steps, warmup, stream)
+    dbytes = Bd * cfg.H * (2 * state[0, 0].numel() * 4 + 2 * cfg.dk * 2 + cfg.dv * 6)
+    dgbs = dbytes / (ms_d * 1e-3) / 1e9
+    return {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "L": cfg.L, "dk": cfg.dk,
+            "dv": cfg.dv, "ms": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("based"),
+                         "algorithmic_bytes_per_launch": nbytes,
+                         "kernel": "parallax_based_fwd call = parallax_based_state_kernel<128> + "
+                                   "parallax_based_scan_kernel<128> + "
+                                   "parallax_based_out_kernel<128>"},
+            "decode": {"B": Bd, "H": cfg.H, "ms": round(ms_d, 4), "value": round(dgbs, 1),
+                       "unit": "GB/s", "frac": round(dgbs / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes_per_launch": dbytes,
+                       "kernel": "parallax_based_decode_kernel<128>"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -470,6 +522,8 @@ def main():
     print("[bench] timing the Hadamard output projection", file=sys.stderr, flush=True)
     res["hadamard"] = time_hadamard(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
                                     stream)
+    print("[bench] timing Based linear attention", file=sys.stderr, flush=True)
+    res["based"] = time_based(min(args.steps, 20), max(1, min(args.warmup, 3)), stream)
     if not args.no_backward:
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         res["backward"] = time_backward(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),

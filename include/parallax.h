@@ -322,6 +322,78 @@ parallax_status parallax_hadamard_out(const float *o, parallax_strides so, int B
                                       int d, const float *alpha, const float *beta, void *y,
                                       int64_t ldy, void *stream);
 
+/*
+ * Based linear attention (review page "Simple linear attention language
+ * models balance the recall-throughput tradeoff", "Proposed method"): the
+ * linear-attention half of the Based hybrid, whose other half is softmax
+ * attention over a small sliding window (parallax_attn_fwd with rho = 0,
+ * a window of 64 or 128 keys and, optionally, sinks).  Linear attention
+ * replaces exp(scale q.k) by a kernel phi(q).phi(k), so the causal sum is
+ * carried as a state whose size the feature dimension sets.  Here phi is
+ * the feature map of the second-order Taylor expansion of exp: with
+ * x = scale * q_i . k_j,
+ *
+ *     w_ij = phi(q_i) . phi(k_j) = 1 + x + x^2 / 2      (always > 0)
+ *     o_i  = sum_{j <= i} w_ij v_j / sum_{j <= i} w_ij
+ *
+ * The query/key feature dimension dk must be 16 (phi then has 153
+ * features: 1, 16 linear, 136 distinct quadratic products); dv is 64 or
+ * 128.  PARALLAX_ERR_UNSUPPORTED otherwise.
+ *
+ * State (decoding): fp32 [B, H, 160, NC] with NC = 16 * (dv / 16 + 1),
+ * contiguous; parallax_based_state_floats(dk, dv) = 160 * NC floats per
+ * (batch, head).  Entry [f][c] is sum_j phi_f(k_j) v_jc for c < dv and
+ * sum_j phi_f(k_j) for every c >= dv, with the feature order
+ *     f = 16 d + a (f < 128): k_a k_{(a+d) mod 16} * (scale/sqrt2 if d == 0
+ *                             else scale);
+ *     f = 128 + a (a < 8): scale k_a k_{a+8};  f = 136 + a: sqrt(scale) k_a;
+ *     f = 152: 1;  f = 153..159: 0.
+ *
+ * Numerics: the prefill feeds phi(k) and v to the matrix cores as float16
+ * (|v| <= 65504, |k_a k_b| * scale <= 65504) and the prefix state and
+ * phi(q) as bfloat16, with fp32 sums; the decode works in fp32.
+ */
+size_t parallax_based_state_floats(int dk, int dv);
+
+/*
+ * Bytes of device workspace parallax_based_fwd needs: per (batch, head) and
+ * per 512-token segment, the segment's state in fp32 plus the prefix state
+ * as bf16 fragments, i.e. B * H * ceil(L / 512) * 160 * NC * 6 bytes.  0 for
+ * sizes parallax_based_fwd would reject.
+ */
+size_t parallax_based_workspace_size(int B, int H, int L, int dk, int dv);
+
+/*
+ * Causal Based linear-attention prefill.
+ *   q, k : bf16 [B, H, L, 16]; v: bf16 [B, H, L, dv]; element strides
+ *          sq, sk, sv (last dimension contiguous, strides multiples of 8,
+ *          16-byte aligned bases).
+ *   o    : fp32 [B, H, L, dv], strides so (multiples of 4), 16-byte aligned.
+ *   state: NULL, or fp32 [B, H, 160, NC] (16-byte aligned): receives the
+ *          state after the last token, for parallax_based_decode.
+ *   scale: > 0 and finite (x = scale * q.k; 1/4 is 1/sqrt(dk)).
+ *   workspace: device memory of parallax_based_workspace_size bytes,
+ *          16-byte aligned; scratch once the call's work has finished.
+ * B * H * L == 0: OK, no work.
+ */
+parallax_status parallax_based_fwd(const void *q, const void *k, const void *v, float *o,
+                                   float *state, int B, int H, int L, int dk, int dv,
+                                   parallax_strides sq, parallax_strides sk, parallax_strides sv,
+                                   parallax_strides so, float scale, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
+ * One Based decode step per (batch, head): adds phi(k)[v | 1]^T to the
+ * state (in place) and writes o = phi(q).S[:, :dv] / phi(q).S[:, dv], the
+ * output of the new token over every token so far (the state's and its
+ * own).  q, k: bf16 [B, H, 16]; v: bf16 [B, H, dv]; state: fp32
+ * [B, H, 160, NC]; o: fp32 [B, H, dv]; all contiguous.  A zero state starts
+ * a new sequence.  B * H == 0: OK, no work.
+ */
+parallax_status parallax_based_decode(const void *q, const void *k, const void *v, float *state,
+                                      float *o, int B, int H, int dk, int dv, float scale,
+                                      void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *parallax_status_string(parallax_status s);
 

@@ -6,14 +6,18 @@ The compute path is the gfx950 HIP library ``libparallax.so`` (C ABI in
 ``include/parallax.h``); this package only builds it and marshals torch
 tensors into it.
 """
-from .binding import (EXPORTED, LIBRARY, ParallaxError, load_library, parallax_attn_bwd,
+from .binding import (EXPORTED, LIBRARY, ParallaxError, based_state_shape, load_library,
+                      parallax_attn_bwd, parallax_based_decode, parallax_based_fwd,
+                      parallax_based_state_floats, parallax_based_workspace_size,
                       parallax_attn_bwd_workspace_size, parallax_attn_decode,
                       parallax_attn_decode_paged, parallax_attn_fwd,
                       parallax_attn_fwd_train, parallax_attn_fwd_workspace_size,
                       parallax_hadamard_out, parallax_qkvr_project, parallax_status_string,
                       split_qkvr)
 
-__all__ = ["EXPORTED", "LIBRARY", "ParallaxError", "load_library", "parallax_attn_bwd",
+__all__ = ["EXPORTED", "LIBRARY", "ParallaxError", "based_state_shape", "load_library",
+           "parallax_attn_bwd", "parallax_based_decode", "parallax_based_fwd",
+           "parallax_based_state_floats", "parallax_based_workspace_size",
            "parallax_attn_bwd_workspace_size", "parallax_attn_decode",
            "parallax_attn_decode_paged", "parallax_attn_fwd",
            "parallax_attn_fwd_train", "parallax_attn_fwd_workspace_size",

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
 EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_train",
             "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
             "parallax_attn_decode_paged", "parallax_qkvr_project", "parallax_hadamard_out",
-            "parallax_status_string")
+            "parallax_based_state_floats", "parallax_based_workspace_size", "parallax_based_fwd",
+            "parallax_based_decode", "parallax_status_string")
 
 
 class parallax_strides(ctypes.Structure):
@@ -82,6 +83,15 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                           ctypes.c_int64, vp]
     lib.parallax_hadamard_out.restype = ctypes.c_int
     lib.parallax_hadamard_out.argtypes = [vp, S, i, i, i, i, vp, vp, vp, ctypes.c_int64, vp]
+    lib.parallax_based_state_floats.restype = ctypes.c_size_t
+    lib.parallax_based_state_floats.argtypes = [i, i]
+    lib.parallax_based_workspace_size.restype = ctypes.c_size_t
+    lib.parallax_based_workspace_size.argtypes = [i, i, i, i, i]
+    lib.parallax_based_fwd.restype = ctypes.c_int
+    lib.parallax_based_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, S, S, S, S, f, vp,
+                                       ctypes.c_size_t, vp]
+    lib.parallax_based_decode.restype = ctypes.c_int
+    lib.parallax_based_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp]
     lib.parallax_status_string.restype = ctypes.c_char_p
     lib.parallax_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -393,6 +403,90 @@ def parallax_hadamard_out(o, alpha=None, beta=None, *, out=None, stream=None):
         alpha.data_ptr() if alpha is not None else None,
         beta.data_ptr() if beta is not None else None,
         rows.data_ptr(), rows.stride(0), _stream_handle(o.device, stream))
+    _check(st)
+    return out
+
+
+BASED_FEATURES = 160
+
+
+def parallax_based_state_floats(dk: int, dv: int) -> int:
+    """fp32 values of one (batch, head) Based state: 160 x 16 (dv / 16 + 1)."""
+    return int(load_library().parallax_based_state_floats(int(dk), int(dv)))
+
+
+def parallax_based_workspace_size(B: int, H: int, L: int, dk: int, dv: int) -> int:
+    return int(load_library().parallax_based_workspace_size(int(B), int(H), int(L), int(dk),
+                                                             int(dv)))
+
+
+def based_state_shape(dv: int):
+    """Shape of one (batch, head) state: (160 features, 16 (dv/16 + 1) columns)."""
+    return (BASED_FEATURES, 16 * (dv // 16 + 1))
+
+
+def parallax_based_fwd(q, k, v, *, scale=None, return_state=False, out=None, workspace=None,
+                       stream=None):
+    """Causal Based linear attention (Taylor kernel 1 + x + x^2/2, x = scale q.k).
+
+    q, k: bf16 [B, H, L, 16]; v: bf16 [B, H, L, dv] (dv 64 or 128).  Returns
+    o fp32 [B, H, L, dv], and with ``return_state`` also the state after the
+    last token (fp32 [B, H, 160, 16 (dv/16 + 1)]) for parallax_based_decode."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, H, L, dk = q.shape
+    dv = v.shape[3]
+    if tuple(k.shape) != (B, H, L, dk) or tuple(v.shape[:3]) != (B, H, L):
+        raise ValueError("q, k, v shapes disagree")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 4)
+    if tuple(out.shape) != (B, H, L, dv):
+        raise ValueError("out has the wrong shape")
+    state = None
+    if return_state:
+        state = torch.zeros((B, H) + based_state_shape(dv), dtype=torch.float32, device=q.device)
+    nbytes = parallax_based_workspace_size(B, H, L, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = load_library().parallax_based_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        state.data_ptr() if state is not None else None, B, H, L, dk, dv, _strides(q),
+        _strides(k), _strides(v), _strides(out), float(scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(q.device, stream))
+    _check(st)
+    return (out, state) if return_state else out
+
+
+def parallax_based_decode(q, k, v, state, *, scale=None, out=None, stream=None):
+    """One Based decode step: q, k bf16 [B, H, 16], v bf16 [B, H, dv]; ``state``
+    fp32 [B, H, 160, 16 (dv/16 + 1)] is updated in place.  Returns o fp32 [B, H, dv]."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(state, "state", torch.float32, 4)
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
+        raise ValueError("q, k, v shapes disagree")
+    if tuple(state.shape) != (B, H) + based_state_shape(dv) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 [B, H, 160, 16 (dv/16 + 1)] tensor")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3)
+    if tuple(out.shape) != (B, H, dv) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [B, H, dv] tensor")
+    st = load_library().parallax_based_decode(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), state.data_ptr(), out.data_ptr(), B, H, dk, dv,
+        float(scale), _stream_handle(q.device, stream))
     _check(st)
     return out
 

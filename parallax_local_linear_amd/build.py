@@ -18,7 +18,7 @@ LIBRARY = os.path.join(PKG, "libparallax.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["parallax_api.hip", "parallax_fwd.hip", "parallax_bwd.hip", "parallax_decode.hip",
-           "parallax_proj.hip", "parallax_hadamard.hip"]
+           "parallax_proj.hip", "parallax_hadamard.hip", "parallax_based.hip"]
 # Kernel sources: no NaN ever reaches a max or compare (masking uses -inf and
 # non-finite inputs are outside the contract), so max chains need no NaN
 # canonicalisation.  The host API keeps IEEE NaN semantics for its argument
@@ -29,6 +29,7 @@ KERNEL_FLAGS = {
     "parallax_decode.hip": ["-fno-honor-nans"],
     "parallax_proj.hip": ["-fno-honor-nans"],
     "parallax_hadamard.hip": ["-fno-honor-nans"],
+    "parallax_based.hip": ["-fno-honor-nans"],
 }
 ARCH = "gfx950"
 

@@ -68,6 +68,25 @@ struct HadArgs {
     int log2d;                      // feature index i reads head i >> log2d, feature i & (d - 1)
 };
 
+// Based linear attention (second-order Taylor kernel, 16 query/key
+// features): prefill in 512-token segments, decode on a fixed-size state.
+constexpr int kBasedSegment = 512;
+struct BasedArgs {
+    const uint16_t *q, *k, *v;      // bf16 [B,H,L,16], [B,H,L,16], [B,H,L,dv]; strides below
+    float *o;                       // fp32 [B,H,L,dv]
+    int64_t q_b, q_h, q_l;
+    int64_t k_b, k_h, k_l;
+    int64_t v_b, v_h, v_l;
+    int64_t o_b, o_h, o_l;
+    int B, H, L;
+    int n_seg;                      // ceil(L / kBasedSegment)
+    int n_qt;                       // ceil(L / 256): output workgroups per (batch, head)
+    float scale;                    // x = scale * q.k
+    float *dstate;                  // workspace: fp32 [B*H][n_seg][160][16 (dv/16 + 1)]
+    uint16_t *sfrag;                // workspace: bf16 prefix-state fragments per segment
+    float *state;                   // optional: fp32 [B*H][160][16 (dv/16 + 1)] final state
+};
+
 struct PagedDecodeArgs {
     const uint16_t *q, *r;          // bf16 [B,Hq,d] contiguous
     const uint16_t *k, *v;          // bf16 cache: element strides along page, kv head, row
@@ -145,6 +164,10 @@ hipError_t launch_fwd(const FwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_proj(const ProjArgs &a, hipStream_t stream);
 hipError_t launch_hadamard(const HadArgs &a, int log2n, hipStream_t stream);
+hipError_t launch_based_fwd(const BasedArgs &a, int dv, hipStream_t stream);
+hipError_t launch_based_decode(const BasedArgs &a, int dv, hipStream_t stream);
+size_t based_workspace_bytes(int64_t B, int64_t H, int64_t L, int dv);
+size_t based_state_floats(int dv);
 int64_t hadamard_blocks(int64_t M, int log2n);
 size_t proj_tiles(int M, int N);
 hipError_t launch_decode(const DecodeArgs &a, int d, int num_splits, hipStream_t stream);

@@ -409,4 +409,97 @@ parallax_status parallax_hadamard_out(const float *o, parallax_strides so, int B
     return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
 }
 
+size_t parallax_based_state_floats(int dk, int dv) {
+    if (dk != 16 || (dv != 64 && dv != 128))
+        return 0;
+    return plx::based_state_floats(dv);
+}
+
+size_t parallax_based_workspace_size(int B, int H, int L, int dk, int dv) {
+    if (B < 0 || H < 0 || L < 0 || dk != 16 || (dv != 64 && dv != 128))
+        return 0;
+    return plx::based_workspace_bytes(B, H, L, dv);
+}
+
+parallax_status parallax_based_fwd(const void *q, const void *k, const void *v, float *o,
+                                   float *state, int B, int H, int L, int dk, int dv,
+                                   parallax_strides sq, parallax_strides sk, parallax_strides sv,
+                                   parallax_strides so, float scale, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    if (B < 0 || H < 0 || L < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (dk != 16 || (dv != 64 && dv != 128))
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!scale_ok(scale))
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * H * L == 0)
+        return PARALLAX_OK;
+    if (!q || !k || !v || !o || !workspace)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(state, 16) || !aligned(workspace, 16))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!bf16_strides_ok(sq) || !bf16_strides_ok(sk) || !bf16_strides_ok(sv) ||
+        !f32_strides_ok(so))
+        return PARALLAX_ERR_INVALID_ARG;
+    if (workspace_bytes < plx::based_workspace_bytes(B, H, L, dv))
+        return PARALLAX_ERR_INVALID_ARG;
+    const int64_t n_seg = ((int64_t)L + plx::kBasedSegment - 1) / plx::kBasedSegment;
+    const int64_t n_qt = ((int64_t)L + 255) / 256;
+    if ((int64_t)B * H * n_qt > INT_MAX || (int64_t)B * H * n_seg * 64 * 9 * 5 > INT_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+    plx::BasedArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = o;
+    a.q_b = sq.b, a.q_h = sq.h, a.q_l = sq.l;
+    a.k_b = sk.b, a.k_h = sk.h, a.k_l = sk.l;
+    a.v_b = sv.b, a.v_h = sv.h, a.v_l = sv.l;
+    a.o_b = so.b, a.o_h = so.h, a.o_l = so.l;
+    a.B = B;
+    a.H = H;
+    a.L = L;
+    a.n_seg = (int)n_seg;
+    a.n_qt = (int)n_qt;
+    a.scale = scale;
+    a.dstate = static_cast<float *>(workspace);
+    a.sfrag = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
+                                           (size_t)B * H * n_seg *
+                                               plx::based_state_floats(dv) * 4);
+    a.state = state;
+    hipError_t e = plx::launch_based_fwd(a, dv, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
+parallax_status parallax_based_decode(const void *q, const void *k, const void *v, float *state,
+                                      float *o, int B, int H, int dk, int dv, float scale,
+                                      void *stream) {
+    if (B < 0 || H < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (dk != 16 || (dv != 64 && dv != 128))
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!scale_ok(scale))
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * H == 0)
+        return PARALLAX_OK;
+    if (!q || !k || !v || !state || !o || !aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) ||
+        !aligned(state, 4) || !aligned(o, 4))
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * H > INT_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+    plx::BasedArgs a = {};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = o;
+    a.B = B;
+    a.H = H;
+    a.L = 1;
+    a.scale = scale;
+    a.state = state;
+    hipError_t e = plx::launch_based_decode(a, dv, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
 }  // extern "C"

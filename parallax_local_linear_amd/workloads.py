@@ -47,11 +47,28 @@ class Decode:
     num_splits: int = 16
 
 
+@dataclasses.dataclass(frozen=True)
+class Based:
+    """Based linear attention layer: dk query/key features, dv value features."""
+    name: str
+    seed: int
+    B: int
+    H: int
+    L: int
+    dk: int
+    dv: int
+    scale: float
+
+
 TINY = Prefill("tiny", 1, 1, 2, 256, 64)
 PREFILL_06B = Prefill("prefill_0.6b", 2, 4, 16, 2048, 64, scale_inputs=64 ** -0.25)
 PREFILL_17B = Prefill("prefill_1.7b_long", 3, 2, 16, 8192, 128)
 LOCAL = Prefill("local_swa128_sink4", 4, 1, 16, 16384, 64, window=128, n_sink=4)
 DECODE = Decode("decode_4k", 5, 64, 16, 4096, 128, num_splits=16)
+
+# The 1.7B-like layer shape (16 heads, 8192 tokens, 128 value features) with
+# Based's 16 query/key features; x = q.k / sqrt(16).
+BASED = Based("based_1.7b_long", 6, 2, 16, 8192, 16, 128, 0.25)
 
 PREFILLS = (TINY, PREFILL_06B, PREFILL_17B, LOCAL)
 
@@ -91,6 +108,15 @@ def decode_inputs(cfg: Decode, device="cpu", dtype=torch.bfloat16):
     v = torch.randn((cfg.B, cfg.H, cfg.Lmax, cfg.d), generator=g, device=device).to(dtype)
     r = torch.randn((cfg.B, cfg.H, cfg.d), generator=g, device=device).to(dtype)
     return q, k, v, r
+
+
+def based_inputs(cfg: Based, device="cpu", dtype=torch.bfloat16):
+    """(q [B,H,L,dk], k [B,H,L,dk], v [B,H,L,dv]), N(0,1), drawn in that order."""
+    g = _gen(device, cfg.seed)
+    q = torch.randn((cfg.B, cfg.H, cfg.L, cfg.dk), generator=g, device=device).to(dtype)
+    k = torch.randn((cfg.B, cfg.H, cfg.L, cfg.dk), generator=g, device=device).to(dtype)
+    v = torch.randn((cfg.B, cfg.H, cfg.L, cfg.dv), generator=g, device=device).to(dtype)
+    return q, k, v
 
 
 def random_tensor(shape, seed: int, device="cpu", scale: float = 1.0, dtype=torch.bfloat16):

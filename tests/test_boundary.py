@@ -295,6 +295,57 @@ def test_hadamard_empty_is_a_no_op(lib):
     assert had(lib, L=0, o=None, y=None) == OK
 
 
+QK16 = S(2 * 300 * 16, 300 * 16, 16)
+V128 = S(2 * 300 * 128, 300 * 128, 128)
+
+
+def based(lib, q=A16, k=A16, v=A16, o=A16, state=None, B=1, H=2, L=300, dk=16, dv=128,
+          sq=QK16, sk=QK16, sv=V128, so=V128, scale=0.25, ws=A16, ws_bytes=1 << 40):
+    return lib.parallax_based_fwd(q, k, v, o, state, B, H, L, dk, dv, sq, sk, sv, so, scale, ws,
+                                  ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(L=-1), INVALID), (dict(dk=32), UNSUPPORTED),
+    (dict(dv=96), UNSUPPORTED), (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(ws=None), INVALID), (dict(q=A16 + 8), INVALID), (dict(o=A16 + 4), INVALID),
+    (dict(state=A16 + 4), INVALID), (dict(ws=A16 + 8), INVALID), (dict(ws_bytes=0), INVALID),
+    (dict(sk=S(2 * 300 * 16, 300 * 16, 12)), INVALID), (dict(so=S(-4, 128, 128)), INVALID),
+])
+def test_based_rejects(lib, kw, status):
+    assert based(lib, **kw) == status
+
+
+def test_based_empty_is_a_no_op(lib):
+    assert based(lib, L=0, q=None, k=None, v=None, o=None, ws=None) == OK
+
+
+def test_based_sizes(lib):
+    nc = 16 * (128 // 16 + 1)
+    assert binding.parallax_based_state_floats(16, 128) == 160 * nc
+    assert binding.parallax_based_state_floats(16, 64) == 160 * 80
+    assert binding.parallax_based_state_floats(8, 128) == 0
+    # B * H * ceil(L / 512) * 160 * NC * 6 bytes
+    assert binding.parallax_based_workspace_size(2, 16, 8192, 16, 128) == 2 * 16 * 16 * 160 * nc * 6
+    assert binding.parallax_based_workspace_size(1, 1, 513, 16, 64) == 2 * 160 * 80 * 6
+    assert binding.parallax_based_workspace_size(1, 1, 64, 16, 96) == 0
+
+
+def test_based_decode_rejects(lib):
+    dec_b = lambda **kw: lib.parallax_based_decode(
+        kw.get("q", A16), kw.get("k", A16), kw.get("v", A16), kw.get("state", A16),
+        kw.get("o", A16), kw.get("B", 2), kw.get("H", 2), kw.get("dk", 16), kw.get("dv", 128),
+        kw.get("scale", 0.25), None)
+    assert dec_b(dk=8) == UNSUPPORTED
+    assert dec_b(dv=32) == UNSUPPORTED
+    assert dec_b(B=-1) == INVALID
+    assert dec_b(state=None) == INVALID
+    assert dec_b(scale=-1.0) == INVALID
+    assert dec_b(state=A16 + 2) == INVALID
+    assert dec_b(B=0, q=None, state=None) == OK
+
+
 def test_split_qkvr_views_share_storage():
     import torch
     y = torch.arange(2 * 5 * 4 * 3 * 8, dtype=torch.float32).view(2 * 5, 4 * 3 * 8)
