@@ -19,7 +19,9 @@
 //     f = 153 .. 159             :  0
 //
 // Prefill, three kernels (one pass over q, k, v; the state never leaves
-// the chip inside a segment):
+// the chip inside a segment).  Keys and values stream through LDS in
+// super-stages of 128 tokens: one round of loads and barriers per four
+// 32-token MFMA stages, loads of the next super-stage in flight meanwhile.
 //   1. parallax_based_state_kernel: per (batch, head, 512-token segment),
 //      dS = Phi(K)^T [V | 1] on the matrix cores (f16 operands, fp32 sums).
 //      Each 32-token stage puts K^T in LDS, builds the Phi(K) fragments
@@ -48,11 +50,14 @@ constexpr int BK = 16;     // query/key features
 constexpr int NF = 160;    // expanded features (153 used)
 constexpr int NFC = 5;     // 32-feature chunks
 constexpr int TS = kBasedSegment;  // tokens per segment
-constexpr int BS = 32;     // tokens per stage
+constexpr int BS = 32;     // tokens per MFMA stage
+constexpr int SUB = 4;     // stages per super-stage (one round of loads and barriers)
+constexpr int SST = SUB * BS;
+constexpr int KTS = BS + 4;  // padded K^T row (floats): conflict-free 16-byte reads
 constexpr int QT = 256;    // queries per output workgroup
 constexpr int QW = 32;     // queries per output wavefront
 constexpr int OW = QT / QW;
-static_assert(TS % QT == 0 && TS % BS == 0, "segment tiling");
+static_assert(TS % QT == 0 && TS % SST == 0, "segment tiling");
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -75,15 +80,16 @@ __device__ __forceinline__ int pos_tok(int p) {
     return ((p >> 2) & 1) * 16 + (p >> 3) * 4 + (p & 3);
 }
 
-// 16-byte slot of chunk g (positions 8g .. 8g+7) of row r in a [rows][32]
-// f16 stage: rows 4 apart share banks, so the chunk index is rotated.
-__device__ __forceinline__ int vslot(int r, int g) { return 4 * r + (g ^ ((r >> 2) & 3)); }
+// V^T stages in LDS: row r (a value column) holds the stage's 32 positions
+// as f16, padded to VTS halves (80 bytes), so the 16-byte fragment reads of
+// 16 consecutive rows fall on distinct banks and a thread's 8 column writes
+// are one base address plus constant offsets.
+constexpr int VTS = BS + 8;
 
-// Feature f of a 16-vector given by two of its components (u_a, u_b are
-// the components the feature reads: see feat_ab).
+// Feature f as coef * u_a * u_b, where u_16 is 1 (0 for tokens past the
+// sequence end, which zeroes every feature of such tokens).
 struct FeatAB {
-    int a, b;     // component indices (b unused for linear, both unused for constants)
-    int kind;     // 0 product, 1 linear, 2 one, 3 zero
+    int a, b;
     float coef;
 };
 __device__ __forceinline__ FeatAB feat_ab(int f, float scale) {
@@ -92,26 +98,20 @@ __device__ __forceinline__ FeatAB feat_ab(int f, float scale) {
         const int delta = f >> 4;
         r.a = f & 15;
         r.b = (r.a + delta) & 15;
-        r.kind = 0;
         r.coef = delta == 0 ? scale * 0.70710678118654752f : scale;
     } else if (f < 136) {
         r.a = f - 128;
         r.b = r.a + 8;
-        r.kind = 0;
         r.coef = scale;
     } else if (f < 152) {
-        r.a = r.b = f - 136;
-        r.kind = 1;
+        r.a = f - 136;
+        r.b = BK;
         r.coef = __builtin_sqrtf(scale);
     } else {
-        r.a = r.b = 0;
-        r.kind = f == 152 ? 2 : 3;
-        r.coef = 0.f;
+        r.a = r.b = BK;
+        r.coef = f == 152 ? 1.f : 0.f;
     }
     return r;
-}
-__device__ __forceinline__ float feat_val(const FeatAB &fa, float ua, float ub) {
-    return fa.kind == 0 ? fa.coef * ua * ub : fa.kind == 1 ? fa.coef * ua : fa.kind == 2 ? 1.f : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -119,15 +119,75 @@ __device__ __forceinline__ float feat_val(const FeatAB &fa, float ua, float ub) 
 
 template <int DV>
 struct StateLds {
-    float kt[BK][BS];                       // K^T of the stage, positions in MFMA order
-    uint16_t vt[DV * BS];                   // V^T of the stage, f16, vslot layout
-    u32x4 phi[NF / 16][64];                 // Phi(K) B fragments of the stage
+    float kt[SUB][BK + 1][KTS];             // K^T per stage (+ the ones row), MFMA order
+    uint16_t vt[SUB][DV * VTS + 32];        // V^T per stage, f16, padded rows and stages
+    u32x4 phi[SUB][NF / 16][64];            // Phi(K) B fragments per stage
+};
+
+// Loads of one super-stage (128 tokens) into registers and their stores
+// into LDS, shared by the state and output kernels.
+//   V: task t < VT (G = t % 4, stage = t / 4 % 4, column chunk m = t / 16)
+//      loads the 8 tokens at reduction positions 8G .. 8G+7 of the stage,
+//      8 columns each, and writes them transposed as 8 rows of 16 bytes;
+//      lanes of a 16-lane phase differ in G and stage, which the 64-byte
+//      stage padding puts on distinct banks.
+//   K: chunk c < 256 (token c / 2, features 8 (c % 2) ..) by thread c.
+// Tokens past L read zeros.
+template <int DV>
+struct StageIO {
+    static constexpr int VT = SUB * 4 * (DV / 8);
+    static constexpr int VSTAGE = DV * VTS + 32;
+    u32x4 v[8];
+    u32x4 k;
+
+    __device__ __forceinline__ void load(const uint16_t *kb, const uint16_t *vb, int64_t k_l,
+                                         int64_t v_l, int t0, int L, int tid) {
+        if (tid < VT) {
+            const int G = tid & 3, sub = (tid >> 2) & 3, m = tid >> 4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = t0 + sub * BS + pos_tok(8 * G + e);
+                v[e] = t < L ? *reinterpret_cast<const u32x4 *>(vb + (int64_t)t * v_l + 8 * m)
+                             : (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+        if (tid < 2 * SST) {
+            const int t = t0 + (tid >> 1);
+            k = t < L ? *reinterpret_cast<const u32x4 *>(kb + (int64_t)t * k_l + 8 * (tid & 1))
+                      : (u32x4){0u, 0u, 0u, 0u};
+        }
+    }
+
+    // V^T of stage s at vt[s * VSTAGE + col * VTS + pos], f16.
+    __device__ __forceinline__ void store_v(uint16_t *vt, int tid) const {
+        if (tid >= VT)
+            return;
+        const int G = tid & 3, sub = (tid >> 2) & 3, m = tid >> 4;
+        uint32_t h[8][4];  // [token e][column pair]: f16x2
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                h[e][w] = __builtin_bit_cast(uint32_t, cvt_f16x2(bf16_lo(v[e][w]), bf16_hi(v[e][w])));
+        uint16_t *dst = vt + sub * VSTAGE + 8 * m * VTS + 8 * G;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            u32x4 out;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const uint32_t lo = h[2 * pp][i / 2], hi = h[2 * pp + 1][i / 2];
+                out[pp] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            *reinterpret_cast<u32x4 *>(dst + i * VTS) = out;
+        }
+    }
 };
 
 template <int DV>
 __global__ __launch_bounds__(64 * BCfg<DV>::CB) void parallax_based_state_kernel(BasedArgs a) {
     using C = BCfg<DV>;
     constexpr int NT = 64 * C::CB;
+    using IO = StageIO<DV>;
     __shared__ StateLds<DV> s;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -139,59 +199,9 @@ __global__ __launch_bounds__(64 * BCfg<DV>::CB) void parallax_based_state_kernel
     const uint16_t *kb = a.k + (int64_t)b * a.k_b + (int64_t)h * a.k_h;
     const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h;
     const int t_begin = seg * TS;
-    const int n_st = (min(a.L - t_begin, TS) + BS - 1) / BS;
+    const int n_sst = (min(a.L - t_begin, TS) + SST - 1) / SST;
 
-    // Loads of one stage into registers: K by threads 0..63 (8 features of
-    // one token each), V by all threads (8 columns of one token each).
-    constexpr int VCH = DV / 8;             // 16-byte chunks per V row
-    constexpr int VLOADS = (BS * VCH + NT - 1) / NT;
-    u32x4 kreg = {0u, 0u, 0u, 0u};
-    u32x4 vreg[VLOADS];
-    auto load_stage = [&](int st) __attribute__((always_inline)) {
-        const int t0 = t_begin + st * BS;
-        if (tid < 2 * BS) {
-            const int j = tid >> 1, t = t0 + j;
-            kreg = t < a.L ? *reinterpret_cast<const u32x4 *>(kb + (int64_t)t * a.k_l + 8 * (tid & 1))
-                           : (u32x4){0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < VLOADS; ++u) {
-            const int idx = tid + u * NT;
-            vreg[u] = (u32x4){0u, 0u, 0u, 0u};
-            if (idx < BS * VCH) {
-                const int j = idx / VCH, t = t0 + j;
-                if (t < a.L)
-                    vreg[u] = *reinterpret_cast<const u32x4 *>(vb + (int64_t)t * a.v_l +
-                                                               8 * (idx % VCH));
-            }
-        }
-    };
-    auto store_stage = [&]() __attribute__((always_inline)) {
-        if (tid < 2 * BS) {
-            const int j = tid >> 1, p = tok_pos(j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s.kt[8 * (tid & 1) + 2 * e][p] = bf16_lo(kreg[e]);
-                s.kt[8 * (tid & 1) + 2 * e + 1][p] = bf16_hi(kreg[e]);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < VLOADS; ++u) {
-            const int idx = tid + u * NT;
-            if (idx < BS * VCH) {
-                const int j = idx / VCH, c0 = 8 * (idx % VCH), p = tok_pos(j);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const f16x2 hv = cvt_f16x2(bf16_lo(vreg[u][e]), bf16_hi(vreg[u][e]));
-                    s.vt[vslot(c0 + 2 * e, p >> 3) * 8 + (p & 7)] =
-                        __builtin_bit_cast(uint32_t, hv) & 0xffffu;
-                    s.vt[vslot(c0 + 2 * e + 1, p >> 3) * 8 + (p & 7)] =
-                        __builtin_bit_cast(uint32_t, hv) >> 16;
-                }
-            }
-        }
-    };
-
+    IO io;
     f32x4 acc[NF / 16];
 #pragma unroll
     for (int fb = 0; fb < NF / 16; ++fb)
@@ -199,51 +209,67 @@ __global__ __launch_bounds__(64 * BCfg<DV>::CB) void parallax_based_state_kernel
     const _Float16 one = (_Float16)1.0f;
     const f16x8 ones = {one, one, one, one, one, one, one, one};
 
-    load_stage(0);
-    for (int st = 0; st < n_st; ++st) {
-        __syncthreads();  // the previous stage's fragments have been read
-        store_stage();
-        __syncthreads();
-        if (st + 1 < n_st)
-            load_stage(st + 1);
-        // Phi(K) fragments: fragment-lane (fb, l) holds feature 16 fb + l%16
-        // at positions 8 (l/16) .. +7; tokens past L get zeros.
-        const int t0 = t_begin + st * BS;
-        for (int fl = tid; fl < (NF / 16) * 64; fl += NT) {
-            const int fb = fl >> 6, fl16 = fl & 15, fG = (fl >> 4) & 3;
-            const FeatAB fa = feat_ab(16 * fb + fl16, a.scale);
-            const f32x4 ua0 = *reinterpret_cast<const f32x4 *>(&s.kt[fa.a][8 * fG]);
-            const f32x4 ua1 = *reinterpret_cast<const f32x4 *>(&s.kt[fa.a][8 * fG + 4]);
-            const f32x4 ub0 = *reinterpret_cast<const f32x4 *>(&s.kt[fa.b][8 * fG]);
-            const f32x4 ub1 = *reinterpret_cast<const f32x4 *>(&s.kt[fa.b][8 * fG + 4]);
-            f16x8 out;
+    io.load(kb, vb, a.k_l, a.v_l, t_begin, a.L, tid);
+    for (int ss = 0; ss < n_sst; ++ss) {
+        const int t0 = t_begin + ss * SST;
+        __syncthreads();  // the previous super-stage has been read
+        io.store_v(&s.vt[0][0], tid);
+        if (tid < 2 * SST) {
+            const int j = tid >> 1, p = tok_pos(j & (BS - 1));
+            float *col = &s.kt[j / BS][8 * (tid & 1)][p];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ua = e < 4 ? ua0[e] : ua1[e - 4];
-                const float ub = e < 4 ? ub0[e] : ub1[e - 4];
-                const bool live = t0 + pos_tok(8 * fG + e) < a.L;
-                out[e] = (_Float16)(live ? feat_val(fa, ua, ub) : 0.f);
+            for (int e = 0; e < 4; ++e) {
+                col[(2 * e) * KTS] = bf16_lo(io.k[e]);
+                col[(2 * e + 1) * KTS] = bf16_hi(io.k[e]);
             }
-            s.phi[fb][fl & 63] = __builtin_bit_cast(u32x4, out);
+            if (!(tid & 1))
+                s.kt[j / BS][BK][p] = t0 + j < a.L ? 1.f : 0.f;
         }
         __syncthreads();
-        // This wavefront's 16 columns of [V | 1]^T times Phi(K).
-        const f16x8 va = wave < C::VB
-                             ? __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-                                                              &s.vt[vslot(16 * wave + l16, G) * 8]))
+        if (ss + 1 < n_sst)
+            io.load(kb, vb, a.k_l, a.v_l, t0 + SST, a.L, tid);
+        // Phi(K) fragments: fragment-lane (stage, fb, l) holds feature
+        // 16 fb + l%16 at positions 8 (l/16) .. +7.
+        for (int fl = tid; fl < SUB * (NF / 16) * 64; fl += NT) {
+            const int sub = fl / ((NF / 16) * 64);
+            const int fb = (fl >> 6) % (NF / 16), fl16 = fl & 15, fG = (fl >> 4) & 3;
+            const FeatAB fa = feat_ab(16 * fb + fl16, a.scale);
+            const float *ra = &s.kt[sub][fa.a][8 * fG];
+            const float *rb = &s.kt[sub][fa.b][8 * fG];
+            const f32x4 ua0 = *reinterpret_cast<const f32x4 *>(ra);
+            const f32x4 ua1 = *reinterpret_cast<const f32x4 *>(ra + 4);
+            const f32x4 ub0 = *reinterpret_cast<const f32x4 *>(rb);
+            const f32x4 ub1 = *reinterpret_cast<const f32x4 *>(rb + 4);
+            f16x8 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                out[e] = (_Float16)(fa.coef * ua0[e] * ub0[e]);
+                out[4 + e] = (_Float16)(fa.coef * ua1[e] * ub1[e]);
+            }
+            s.phi[sub][fb][fl & 63] = __builtin_bit_cast(u32x4, out);
+        }
+        __syncthreads();
+        // Phi(K)^T times this wavefront's 16 columns of [V | 1], per stage:
+        // rows are features, columns value columns.
+#pragma unroll
+        for (int sub = 0; sub < SUB; ++sub) {
+            const f16x8 vb16 =
+                wave < C::VB ? __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
+                                                             &s.vt[sub][(16 * wave + l16) * VTS + 8 * G]))
                              : ones;
 #pragma unroll
-        for (int fb = 0; fb < NF / 16; ++fb)
-            acc[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                va, __builtin_bit_cast(f16x8, s.phi[fb][lane]), acc[fb], 0, 0, 0);
+            for (int fb = 0; fb < NF / 16; ++fb)
+                acc[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(f16x8, s.phi[sub][fb][lane]), vb16, acc[fb], 0, 0, 0);
+        }
     }
 
-    // dS [feature][column], fp32: lane holds columns 16 wave + 4G .. +3 of
-    // feature 16 fb + l16.
+    // dS [column][feature], fp32: lane holds features 16 fb + 4G .. +3 of
+    // column 16 wave + l16.
     float *dst = a.dstate + ((int64_t)bh * a.n_seg + seg) * (NF * C::NC);
 #pragma unroll
     for (int fb = 0; fb < NF / 16; ++fb)
-        *reinterpret_cast<f32x4 *>(dst + (16 * fb + l16) * C::NC + 16 * wave + 4 * G) = acc[fb];
+        *reinterpret_cast<f32x4 *>(dst + (16 * wave + l16) * NF + 16 * fb + 4 * G) = acc[fb];
 }
 
 // ---------------------------------------------------------------------------
@@ -264,18 +290,38 @@ __global__ __launch_bounds__(256) void parallax_based_scan_kernel(BasedArgs a) {
     const int col = 16 * cb + (lane & 15);
     const int f0 = 32 * kc + 8 * (lane >> 4);
     float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int seg = 0; seg < a.n_seg; ++seg) {
-        const int64_t sidx = (int64_t)bh * a.n_seg + seg;
-        bf16x8 frag;
+    // Four segments' loads in flight at a time.
+    for (int seg0 = 0; seg0 < a.n_seg; seg0 += 4) {
+        float val[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            frag[e] = (__bf16)run[e];
-        *reinterpret_cast<bf16x8 *>(a.sfrag + ((sidx * C::CB + cb) * NFC + kc) * 512 + lane * 8) =
-            frag;
-        const float *ds = a.dstate + sidx * (NF * C::NC);
+        for (int u = 0; u < 4; ++u) {
+            const int seg = seg0 + u;
+            const float *ds = a.dstate + ((int64_t)bh * a.n_seg + min(seg, a.n_seg - 1)) * (NF * C::NC) +
+                              col * NF + f0;
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(ds);
+            const f32x4 hi = *reinterpret_cast<const f32x4 *>(ds + 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            run[e] += ds[(f0 + e) * C::NC + col];
+            for (int e = 0; e < 4; ++e) {
+                val[u][e] = lo[e];
+                val[u][4 + e] = hi[e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int seg = seg0 + u;
+            if (seg >= a.n_seg)
+                break;
+            const int64_t sidx = (int64_t)bh * a.n_seg + seg;
+            bf16x8 frag;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                frag[e] = (__bf16)run[e];
+            *reinterpret_cast<bf16x8 *>(a.sfrag + ((sidx * C::CB + cb) * NFC + kc) * 512 +
+                                        lane * 8) = frag;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                run[e] += val[u][e];
+        }
     }
     if (a.state) {
         float *st = a.state + (int64_t)bh * (NF * C::NC);
@@ -291,8 +337,8 @@ __global__ __launch_bounds__(256) void parallax_based_scan_kernel(BasedArgs a) {
 template <int DV>
 struct OutLds {
     u32x4 sfrag[BCfg<DV>::CB][NFC][64];     // S^T fragments (bf16) of the segment's prefix
-    uint16_t k[BS][BK];                     // K of the stage, bf16, row-major
-    uint16_t vt[DV * BS];                   // V^T of the stage, f16, vslot layout
+    uint16_t k[SST][BK];                    // K of the super-stage, bf16, row-major
+    uint16_t vt[SUB][DV * VTS + 32];        // V^T per stage, f16, padded rows and stages
 };
 
 // Phi(q)^T B fragment kc for the query whose 16 features are u[]: lane
@@ -373,26 +419,6 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
 
     // This wavefront's queries: 16 g + l16 of rows q0 + 32 wave .. +31.
     const int wq0 = q0 + QW * wave;
-    float u[2][BK];
-    bf16x4 qfrag[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int row = min(wq0 + 16 * g + l16, a.L - 1);
-        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(qb + (int64_t)row * a.q_l);
-        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(qb + (int64_t)row * a.q_l + 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            u[g][2 * e] = bf16_lo(x0[e]);
-            u[g][2 * e + 1] = bf16_hi(x0[e]);
-            u[g][8 + 2 * e] = bf16_lo(x1[e]);
-            u[g][8 + 2 * e + 1] = bf16_hi(x1[e]);
-        }
-        // Score B fragment: features 4G .. 4G+3 of the query.
-        const uint32_t w0 = (G < 2 ? x0 : x1)[2 * (G & 1)];
-        const uint32_t w1 = (G < 2 ? x0 : x1)[2 * (G & 1) + 1];
-        qfrag[g] = __builtin_bit_cast(bf16x4, (u32x2){w0, w1});
-    }
-
     f32x4 acc[C::CB][2];
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
@@ -402,11 +428,27 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
 
     __syncthreads();  // state fragments in LDS
 
-    // State term: O^T += S^T Phi(Q)^T (bf16 operands).
+    // State term: O^T += S^T Phi(Q)^T (bf16 operands); also the score B
+    // fragments (features 4G .. 4G+3 of each query).
+    bf16x4 qfrag[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
+        const int row = min(wq0 + 16 * g + l16, a.L - 1);
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(qb + (int64_t)row * a.q_l);
+        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(qb + (int64_t)row * a.q_l + 8);
+        float u[BK];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[2 * e] = bf16_lo(x0[e]);
+            u[2 * e + 1] = bf16_hi(x0[e]);
+            u[8 + 2 * e] = bf16_lo(x1[e]);
+            u[8 + 2 * e + 1] = bf16_hi(x1[e]);
+        }
+        const uint32_t w0 = (G < 2 ? x0 : x1)[2 * (G & 1)];
+        const uint32_t w1 = (G < 2 ? x0 : x1)[2 * (G & 1) + 1];
+        qfrag[g] = __builtin_bit_cast(bf16x4, (u32x2){w0, w1});
         PhiQ p;
-        phi_setup(p, u[g], G);
+        phi_setup(p, u, G);
 #pragma unroll
         for (int kc = 0; kc < NFC; ++kc) {
             const bf16x8 pf = phi_frag(p, kc, G, a.scale);
@@ -414,105 +456,74 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
             for (int cb = 0; cb < C::CB; ++cb)
                 acc[cb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, s.sfrag[cb][kc][lane]), pf, acc[cb][g], 0, 0, 0);
+            // Keeps one chunk's fragment reads in flight at a time (registers).
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // Causal sum over the segment's keys up to this workgroup's last query.
-    constexpr int VCH = DV / 8;
-    constexpr int VLOADS = (BS * VCH + NT - 1) / NT;
-    u32x4 kreg = {0u, 0u, 0u, 0u};
-    u32x4 vreg[VLOADS];
-    auto load_stage = [&](int st) __attribute__((always_inline)) {
-        const int t0 = seg_begin + st * BS;
-        if (tid < 2 * BS) {
-            const int t = t0 + (tid >> 1);
-            kreg = t < a.L ? *reinterpret_cast<const u32x4 *>(kb + (int64_t)t * a.k_l + 8 * (tid & 1))
-                           : (u32x4){0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int w = 0; w < VLOADS; ++w) {
-            const int idx = tid + w * NT;
-            vreg[w] = (u32x4){0u, 0u, 0u, 0u};
-            if (idx < BS * VCH) {
-                const int t = t0 + idx / VCH;
-                if (t < a.L)
-                    vreg[w] = *reinterpret_cast<const u32x4 *>(vb + (int64_t)t * a.v_l +
-                                                               8 * (idx % VCH));
-            }
-        }
-    };
-    auto store_stage = [&]() __attribute__((always_inline)) {
-        if (tid < 2 * BS)
-            *reinterpret_cast<u32x4 *>(&s.k[tid >> 1][8 * (tid & 1)]) = kreg;
-#pragma unroll
-        for (int w = 0; w < VLOADS; ++w) {
-            const int idx = tid + w * NT;
-            if (idx < BS * VCH) {
-                const int j = idx / VCH, c0 = 8 * (idx % VCH), p = tok_pos(j);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const f16x2 hv = cvt_f16x2(bf16_lo(vreg[w][e]), bf16_hi(vreg[w][e]));
-                    s.vt[vslot(c0 + 2 * e, p >> 3) * 8 + (p & 7)] =
-                        __builtin_bit_cast(uint32_t, hv) & 0xffffu;
-                    s.vt[vslot(c0 + 2 * e + 1, p >> 3) * 8 + (p & 7)] =
-                        __builtin_bit_cast(uint32_t, hv) >> 16;
-                }
-            }
-        }
-    };
-
+    // Causal sum over the segment's keys up to this workgroup's last query,
+    // in super-stages of 128 keys (4 MFMA stages of 32).
+    using IO = StageIO<DV>;
+    IO io;
     const int q_last = min(q0 + QT, a.L) - 1;           // last query of the workgroup
-    const int n_st = (q_last - seg_begin) / BS + 1;
+    const int n_sst = (q_last - seg_begin) / SST + 1;
     const int w_last = min(wq0 + QW, a.L) - 1;          // last query of the wavefront
     const _Float16 one = (_Float16)1.0f;
     const f16x8 ones = {one, one, one, one, one, one, one, one};
     const float xs = a.scale;
 
-    load_stage(0);
-    for (int st = 0; st < n_st; ++st) {
-        __syncthreads();  // the previous stage has been read
-        store_stage();
+    io.load(kb, vb, a.k_l, a.v_l, seg_begin, a.L, tid);
+    for (int ss = 0; ss < n_sst; ++ss) {
+        __syncthreads();  // the previous super-stage has been read
+        io.store_v(&s.vt[0][0], tid);
+        if (tid < 2 * SST)
+            *reinterpret_cast<u32x4 *>(&s.k[tid >> 1][8 * (tid & 1)]) = io.k;
         __syncthreads();
-        if (st + 1 < n_st)
-            load_stage(st + 1);
-        const int t0 = seg_begin + st * BS;
-        if (t0 > w_last)
-            continue;  // every key of this stage is after this wavefront's queries
-        bf16x4 kf[2];
+        if (ss + 1 < n_sst)
+            io.load(kb, vb, a.k_l, a.v_l, seg_begin + (ss + 1) * SST, a.L, tid);
+        // Not unrolled: one stage's fragments live at a time.
+#pragma unroll 1
+        for (int sub = 0; sub < SUB; ++sub) {
+            const int t0 = seg_begin + ss * SST + sub * BS;
+            if (t0 > w_last)
+                break;  // every later key follows this wavefront's queries
+            bf16x4 kf[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-            kf[kt] = *reinterpret_cast<const bf16x4 *>(&s.k[16 * kt + l16][4 * G]);
-        f16x8 vf[C::VB];
-#pragma unroll
-        for (int cb = 0; cb < C::VB; ++cb)
-            vf[cb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
-                                                   &s.vt[vslot(16 * cb + l16, G) * 8]));
-        const bool diag = t0 + BS - 1 > wq0;  // some key may follow some query
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            // S^T tile kt: lane holds keys t0 + 16 kt + 4G + e of query
-            // wq0 + 16 g + l16.
-            const int qrow = wq0 + 16 * g + l16;
-            f16x8 w;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const f32x4 sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    __builtin_bit_cast(s16x4, kf[kt]), __builtin_bit_cast(s16x4, qfrag[g]),
-                    (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = xs * sc[e];
-                    float wt = __builtin_fmaf(0.5f * x, x, x + 1.f);
-                    if (diag && t0 + 16 * kt + 4 * G + e > qrow)
-                        wt = 0.f;
-                    w[4 * kt + e] = (_Float16)wt;
-                }
-            }
+            for (int kt = 0; kt < 2; ++kt)
+                kf[kt] = *reinterpret_cast<const bf16x4 *>(&s.k[sub * BS + 16 * kt + l16][4 * G]);
+            f16x8 vf[C::VB];
 #pragma unroll
             for (int cb = 0; cb < C::VB; ++cb)
-                acc[cb][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[cb], w, acc[cb][g], 0, 0, 0);
-            acc[C::VB][g] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, w, acc[C::VB][g], 0, 0, 0);
+                vf[cb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
+                                                       &s.vt[sub][(16 * cb + l16) * VTS + 8 * G]));
+            const bool diag = t0 + BS - 1 > wq0;  // some key may follow some query
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                // S^T tile kt: lane holds keys t0 + 16 kt + 4G + e of query
+                // wq0 + 16 g + l16.
+                const int qrow = wq0 + 16 * g + l16;
+                f16x8 w;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    const f32x4 sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        __builtin_bit_cast(s16x4, kf[kt]), __builtin_bit_cast(s16x4, qfrag[g]),
+                        (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = xs * sc[e];
+                        float wt = __builtin_fmaf(0.5f * x, x, x + 1.f);
+                        if (diag && t0 + 16 * kt + 4 * G + e > qrow)
+                            wt = 0.f;
+                        w[4 * kt + e] = (_Float16)wt;
+                    }
+                }
+#pragma unroll
+                for (int cb = 0; cb < C::VB; ++cb)
+                    acc[cb][g] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[cb], w, acc[cb][g], 0, 0, 0);
+                acc[C::VB][g] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, w, acc[C::VB][g], 0, 0, 0);
+            }
         }
     }
 
@@ -545,7 +556,7 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
 template <int DV>
 __global__ __launch_bounds__(4 * BCfg<DV>::NC) void parallax_based_decode_kernel(BasedArgs a) {
     using C = BCfg<DV>;
-    __shared__ float phq[NF], phk[NF], qv[BK], kv[BK], vv[DV];
+    __shared__ float phq[NF], phk[NF], qv[BK + 1], kv[BK + 1], vv[DV];
     __shared__ float part[4][C::NC];
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
@@ -555,16 +566,18 @@ __global__ __launch_bounds__(4 * BCfg<DV>::NC) void parallax_based_decode_kernel
     if (tid < BK) {
         qv[tid] = __uint_as_float((uint32_t)qr[tid] << 16);
         kv[tid] = __uint_as_float((uint32_t)kr[tid] << 16);
+    } else if (tid == BK) {
+        qv[BK] = kv[BK] = 1.f;
     }
     if (tid < DV)
         vv[tid] = __uint_as_float((uint32_t)vr[tid] << 16);
     __syncthreads();
     if (tid < NF) {
-        const FeatAB fa = feat_ab(tid, a.scale);
         // The prefill feeds bf16 / f16 features to the matrix cores; the
         // decode keeps them in fp32.
-        phq[tid] = feat_val(fa, qv[fa.a], qv[fa.b]);
-        phk[tid] = feat_val(fa, kv[fa.a], kv[fa.b]);
+        const FeatAB fa = feat_ab(tid, a.scale);
+        phq[tid] = fa.coef * qv[fa.a] * qv[fa.b];
+        phk[tid] = fa.coef * kv[fa.a] * kv[fa.b];
     }
     __syncthreads();
     const int fg = tid / C::NC, c = tid - fg * C::NC;
