@@ -156,3 +156,21 @@ def test_based_full_size(orc):
         ref = orc.based(Q[None, None], K[None, None], V[None, None], scale=cfg.scale)[0, 0]
         check_rows(f64(o[b, h])[rows], ref[rows], Q, K, V, rows, cfg.scale,
                    "based full size (%d,%d) sampled rows" % (b, h))
+
+
+@pytest.mark.parametrize("window,n_sink", [(64, 0), (128, 4)])
+def test_based_softmax_half(orc, window, n_sink):
+    """The other half of the Based hybrid, small-window softmax attention, is
+    the Parallax prefill at rho = 0 (the oracle's rho = 0 case is pinned to
+    torch's scaled_dot_product_attention): windows of 64 and 128 keys."""
+    from gpu_util import compare
+    from parallax_local_linear_amd import parallax_attn_fwd
+    B, H, L, d = 1, 2, 700, 64
+    say("[case] based softmax half W=%d S=%d" % (window, n_sink))
+    q, k, v = (workloads.random_tensor((B, H, L, d), 8400 + t) for t in range(3))
+    r = torch.zeros_like(q)
+    o, lse = parallax_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), r.to(DEV), window=window,
+                               n_sink=n_sink)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.fwd(f64(q), f64(k), f64(v), f64(r), window=window, n_sink=n_sink)
+    compare(f64(o), f64(lse), o_ref, lse_ref, "softmax half W=%d S=%d" % (window, n_sink))
