@@ -14,15 +14,19 @@
 //   Y: bf16 [M, N] row-major, fp32 accumulation, rounded to nearest even
 //
 // Mapping onto CDNA4:
-//   * A workgroup computes a 256 x 256 tile of Y with 8 wavefronts (2 x 4),
-//     each a 128 x 64 tile as 8 x 4 blocks of 16 x 16, with
-//     v_mfma_f32_16x16x32_bf16 over 32-wide k chunks.  The product is taken
-//     transposed (Y^T = W X^T): a lane's accumulator holds four consecutive
-//     output features of one token, stored as one 8-byte write.
+//   * A workgroup computes a 256 x 256 tile of Y with 4 wavefronts (2 x 2),
+//     one per SIMD, each a 128 x 128 tile as 8 x 8 blocks of 16 x 16 (256
+//     accumulator registers), with v_mfma_f32_16x16x32_bf16 over 32-wide k
+//     chunks.  The product is taken transposed (Y^T = W X^T): a lane's
+//     accumulator holds four consecutive output features of one token,
+//     stored as one 8-byte write.
 //   * Each k chunk of both operands is copied into LDS as 1 KiB blocks in
 //     fragment order (lane l holds row l % 16, k offsets 8 (l / 16) .. +7),
 //     directly from global memory, three chunks ahead of use in four stage
 //     buffers; fragment reads are one 16-byte LDS read per lane at l * 16.
+//   * The fragments of chunk k + 1 are read into a second register set
+//     while the 64 MFMAs of chunk k run, so LDS latency and the per-chunk
+//     barrier hide behind the matrix cores.
 //   * Blocks past the edges of X or W read zeros (buffer resources that end
 //     at the last row); rows and columns past M and N are not stored.
 #include "device_common.h"
@@ -36,16 +40,16 @@ namespace {
 constexpr int TM = 256;      // tokens per workgroup tile
 constexpr int TN = 256;      // output features per workgroup tile
 constexpr int TK = 32;       // k per stage
-constexpr int PW = 8;        // wavefronts per workgroup
+constexpr int PW = 4;        // wavefronts per workgroup
 constexpr int WM = 128;      // tokens per wavefront tile
-constexpr int WN = 64;       // features per wavefront tile
+constexpr int WN = 128;      // features per wavefront tile
 constexpr int NSTAGE = 4;
 constexpr int XBLK = TM / 16;  // X blocks per stage (16 rows x 32 k each)
 constexpr int WBLK = TN / 16;  // W blocks per stage
 constexpr int CPW = (XBLK + WBLK) / PW;  // copies per wave per stage
 
 static_assert((XBLK + WBLK) % PW == 0 && XBLK % PW == 0, "copy split");
-static_assert(TM == 2 * WM && TN == 4 * WN, "2 x 4 wavefronts");
+static_assert(TM == 2 * WM && TN == 2 * WN, "2 x 2 wavefronts");
 
 struct ProjStage {
     u32x4 x[XBLK][64];
@@ -87,8 +91,8 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int G = lane >> 4;
-    const int wm = wave / 4;  // wavefront row (tokens)
-    const int wn = wave % 4;  // wavefront column (features)
+    const int wm = wave / 2;  // wavefront row (tokens)
+    const int wn = wave % 2;  // wavefront column (features)
 
     // Tile order.  Workgroups are dealt to the 8 XCDs round-robin
     // (blockIdx % 8), each XCD with its own L2, so the block index is first
@@ -160,47 +164,56 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
         for (int j = 0; j < WM / 16; ++j)
             acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](auto buf) __attribute__((always_inline)) {
+    // Fragments of one chunk in registers.
+    struct Frags {
+        bf16x8 w[WN / 16], x[WM / 16];
+    };
+    auto read = [&](Frags &f, auto buf) __attribute__((always_inline)) {
         const ProjStage &S = sbuf(buf);
-        bf16x8 wf[WN / 16], xf[WM / 16];
 #pragma unroll
         for (int i = 0; i < WN / 16; ++i)
-            wf[i] = __builtin_bit_cast(bf16x8, S.w[wn * (WN / 16) + i][lane]);
+            f.w[i] = __builtin_bit_cast(bf16x8, S.w[wn * (WN / 16) + i][lane]);
 #pragma unroll
         for (int j = 0; j < WM / 16; ++j)
-            xf[j] = __builtin_bit_cast(bf16x8, S.x[wm * (WM / 16) + j][lane]);
+            f.x[j] = __builtin_bit_cast(bf16x8, S.x[wm * (WM / 16) + j][lane]);
+    };
+    auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < WN / 16; ++i)
 #pragma unroll
             for (int j = 0; j < WM / 16; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], xf[j], acc[i][j], 0,
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[i], f.x[j], acc[i][j], 0,
                                                                     0, 0);
     };
-
-    auto step = [&](int kk, auto buf) __attribute__((always_inline)) {
-        wait_copies<2 * CPW>();  // this wave's copies of chunk kk have landed
+    // Step kk (chunk kk in buffer kk % 4, its fragments already in `cur`):
+    // wait for this wave's copies of chunk kk + 1; the barrier then also
+    // means every wave is done with the buffer of chunk kk - 1, which the
+    // copy of chunk kk + 3 refills; read chunk kk + 1 into `nxt` and run
+    // the MFMAs of chunk kk.
+    auto step = [&](int kk, Frags &cur, Frags &nxt, auto buf) __attribute__((always_inline)) {
+        wait_copies<CPW>();
         stage_barrier();
         copy(kk + 3, SBuf<decltype(buf)::value + 3>{});
-        compute(buf);
+        read(nxt, SBuf<decltype(buf)::value + 1>{});
+        if (kk < nk)
+            mfmas(cur);
     };
 
+    Frags fa, fb;
     copy(0, SBuf<0>{});
     copy(1, SBuf<1>{});
     copy(2, SBuf<2>{});
-    int kk = 0;
-    for (; kk + 3 < nk; kk += 4) {
-        step(kk, SBuf<0>{});
-        step(kk + 1, SBuf<1>{});
-        step(kk + 2, SBuf<2>{});
-        step(kk + 3, SBuf<3>{});
-    }
-    if (kk < nk) {
-        step(kk, SBuf<0>{});
-        if (kk + 1 < nk) {
-            step(kk + 1, SBuf<1>{});
-            if (kk + 2 < nk)
-                step(kk + 2, SBuf<2>{});
-        }
+    wait_copies<2 * CPW>();  // chunk 0
+    stage_barrier();
+    read(fa, SBuf<0>{});
+    // Four steps per iteration keep the buffer numbers compile-time; the
+    // fragment sets alternate.  Steps past the last chunk copy and read
+    // the last chunk again (in bounds) and skip their MFMAs.
+    for (int kk = 0; kk < nk; kk += 4) {
+        step(kk, fa, fb, SBuf<0>{});
+        step(kk + 1, fb, fa, SBuf<1>{});
+        step(kk + 2, fa, fb, SBuf<2>{});
+        step(kk + 3, fb, fa, SBuf<3>{});
     }
     wait_copies<0>();
 
