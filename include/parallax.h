@@ -257,10 +257,16 @@ parallax_status parallax_attn_decode(const void *q, const void *r,
  *                reads kv head h / (Hq / Hkv).
  *   window, n_sink : as for the prefill (0 = no window).
  *   num_splits : 1, 2, 4, 8 or 16 key chunks per (sequence, query head),
- *                as for parallax_attn_decode.  A workgroup serves
- *                16 / num_splits query heads of one kv head when Hq/Hkv
- *                allows (the largest power of two dividing it), so that
- *                they share the rows they read.
+ *                as for parallax_attn_decode.  With Hq/Hkv < 4 a workgroup
+ *                serves 16 / num_splits query heads of one kv head when
+ *                Hq/Hkv allows (the largest power of two dividing it), so
+ *                that they share the rows they read.  With Hq/Hkv >= 4 the
+ *                query heads of a kv head (up to 16 per workgroup) are the
+ *                columns of matrix-core tiles and every row is read once
+ *                per workgroup; the keys are split min(num_splits, 8) ways.
+ *                That path feeds the weights and values to the matrix cores
+ *                as float16, like the prefill (|v| <= 65504, |rho.k| <
+ *                65504); the other path computes in fp32.
  */
 parallax_status parallax_attn_decode_paged(const void *q, const void *r,
                                            const void *k_cache, const void *v_cache,

@@ -472,6 +472,317 @@ __global__ __launch_bounds__(64 * NS * GW) void parallax_decode_paged_kernel(Pag
     }
 }
 
+// ---------------------------------------------------------------------------
+// General decode on the matrix cores for grouped heads (Hq / Hkv >= 4).  The
+// query heads that share a kv head become the columns of MFMA tiles, so a
+// workgroup reads every cache row once and the per-key products run on the
+// matrix cores instead of the VALU (with 16 lanes per key, the VALU kernel
+// above spends about 17 wavefront instructions per key and query head,
+// which bounds it once the rows are shared by several heads):
+//   * a workgroup serves (sequence, kv head, GQ query heads); its NS
+//     wavefronts split the visible keys (sink segment, then window) evenly;
+//   * per 32-key stage a wavefront loads K straight into the A fragments of
+//     S^T = K Q^T (16 keys x 32 features: one 16-byte load per lane), and V
+//     as 8 keys x 8 features per lane, transposed in registers into its own
+//     LDS stage as the V^T fragments of the value MFMAs;
+//   * S^T = K Q^T and K R^T (bf16, columns past the group's heads are zero),
+//     an online softmax per column, f16 weights p~ and p~ s, then O^T +=
+//     V^T P~^T and V^T (P~ o S)^T, with the sums of p~ and p~ s from an
+//     all-ones operand (f16 MFMAs, fp32 sums), as in the prefill;
+//   * the NS partial states of each head merge in LDS (the stage memory,
+//     reused after one barrier).
+// Each wavefront's stage count differs, so the loop synchronises within the
+// wavefront only.
+// 16-byte slot of chunk q (reduction positions 8q .. 8q+7) of V^T row r in a
+// [D][32] f16 stage: rows 4 apart share banks, so the chunk is rotated.
+__device__ __forceinline__ int gqa_slot(int r, int q) { return 4 * r + (q ^ ((r >> 2) & 3)); }
+
+template <int D, int NS, int GQ>
+struct GqaShape {
+    static constexpr int KC = D / 32;
+    static constexpr int DT = D / 16;
+    static constexpr int FCH = D / 8;                  // 16-byte feature chunks
+    static constexpr int VT_HALVES = D * 32;           // one wavefront's V^T stage
+    static constexpr int MERGE_FLOATS = NS * GQ * (2 * D + 3);
+    static constexpr int LDS_HALVES =
+        NS * VT_HALVES > 2 * MERGE_FLOATS ? NS * VT_HALVES : 2 * MERGE_FLOATS;
+};
+
+template <int D, int NS, int GQ, bool PAGED>
+__global__ __launch_bounds__(64 * NS) void parallax_decode_gqa_kernel(PagedDecodeArgs a) {
+    using S = GqaShape<D, NS, GQ>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_HALVES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int G = lane >> 4;
+
+    const int g = a.Hq / a.Hkv;
+    const int ngrp = (g + GQ - 1) / GQ;
+    const int pair = blockIdx.x / ngrp;
+    const int grp = blockIdx.x - pair * ngrp;
+    const int b = pair / a.Hkv;
+    const int hk = pair - b * a.Hkv;
+    const int q0 = hk * g + grp * GQ;            // first query head of the workgroup
+    const int ncol = min(GQ, g - grp * GQ);      // query heads it serves
+    const float c = a.scale_log2;
+
+    int n = a.seqlens ? a.seqlens[b] : a.max_len;
+    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    int lo = 0, ns = 0;
+    if (a.window > 0) {
+        lo = max(0, n - a.window);
+        ns = min(a.n_sink, lo);
+    }
+    const int total = ns + (n - lo);
+    const int chunk = (total + NS - 1) / NS;
+    const int ts = min(wave * chunk, total);
+    const int te = min(ts + chunk, total);
+
+    // Q^T and R^T B fragments: column l16 = query head q0 + l16, features
+    // 32 kc + 8G .. +7 (zeros past the group's heads).
+    bf16x8 qf[S::KC], rf[S::KC];
+#pragma unroll
+    for (int kc = 0; kc < S::KC; ++kc) {
+        u32x4 qw = {0u, 0u, 0u, 0u}, rw = {0u, 0u, 0u, 0u};
+        if (l16 < ncol) {
+            const int64_t row = (int64_t)b * a.Hq + q0 + l16;
+            qw = ldg16(a.q + row * D + 32 * kc + 8 * G);
+            rw = ldg16(a.r + row * D + 32 * kc + 8 * G);
+        }
+        qf[kc] = __builtin_bit_cast(bf16x8, qw);
+        rf[kc] = __builtin_bit_cast(bf16x8, rw);
+    }
+
+    const uint16_t *kbase = a.k + (int64_t)hk * a.k_h;
+    const uint16_t *vbase = a.v + (int64_t)hk * a.v_h;
+    const int32_t *bt = PAGED ? a.block_table + (int64_t)b * a.max_pages : nullptr;
+    const int pmask = (1 << a.page_shift) - 1;
+    // Offset (elements) of visible key li's row, li clamped into [ts, te).
+    auto row_of = [&](int li, const uint16_t *base, int64_t sp, int64_t sl) __attribute__((always_inline)) {
+        const int lc = min(li, te - 1);
+        const int kp = lc < ns ? lc : lo + (lc - ns);
+        int64_t page, r;
+        if constexpr (PAGED) {
+            page = min(max(bt[kp >> a.page_shift], 0), a.num_pages - 1);
+            r = kp & pmask;
+        } else {
+            page = b;
+            r = kp;
+        }
+        return base + page * sp + r * sl;
+    };
+
+    uint16_t *vt = lds + wave * S::VT_HALVES;  // this wavefront's V^T stage
+    f32x4 accA[S::DT], accC[S::DT], accL, accS;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+        accA[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        accC[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    accL = accS = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf;  // running offset of column l16 (scaled log2 units)
+    const _Float16 one = (_Float16)1.0f;
+    const f16x8 ones = {one, one, one, one, one, one, one, one};
+    // V loads: lane (vg = lane % 4, vm = lane / 4) holds features 8 vm .. +7
+    // of the keys at reduction positions 8 vg .. 8 vg + 7.
+    const int vg = lane & 3, vm = lane >> 2;
+
+    for (int s0 = ts; s0 < te; s0 += 32) {
+        bf16x8 kf[2][S::KC];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const uint16_t *kr = row_of(s0 + 16 * kt + l16, kbase, a.k_p, a.k_l);
+#pragma unroll
+            for (int kc = 0; kc < S::KC; ++kc)
+                kf[kt][kc] = __builtin_bit_cast(bf16x8, ldg16(kr + 32 * kc + 8 * G));
+        }
+        u32x4 vw[8];
+        if (vm < S::FCH) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 8 * vg + e;  // reduction position -> stage key
+                const int key = ((j >> 2) & 1) * 16 + (j >> 3) * 4 + (j & 3);
+                vw[e] = ldg16(row_of(s0 + key, vbase, a.v_p, a.v_l) + 8 * vm);
+            }
+        }
+        // Scores: S^T tiles (16 keys x 16 heads) for keys 0-15 and 16-31.
+        f32x4 sq[2], sr[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            sq[kt] = sr[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < S::KC; ++kc) {
+                sq[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][kc], qf[kc], sq[kt], 0, 0, 0);
+                sr[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][kc], rf[kc], sr[kt], 0, 0, 0);
+            }
+        }
+        // V^T into this wavefront's stage: 8 feature rows of 16 bytes.
+        if (vm < S::FCH) {
+            uint32_t h[8][4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    h[e][w] = __builtin_bit_cast(uint32_t, cvt_f16x2(bf16_lo(vw[e][w]), bf16_hi(vw[e][w])));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                u32x4 out;
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const uint32_t x0 = h[2 * pp][i / 2], x1 = h[2 * pp + 1][i / 2];
+                    out[pp] = (i & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+                }
+                *reinterpret_cast<u32x4 *>(vt + gqa_slot(8 * vm + i, vg) * 8) = out;
+            }
+        }
+        // Online softmax per column: the stage max over the lane's 8 keys
+        // and the 4 lanes of the column.
+        float x[8];
+        float mt = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool valid = s0 + 16 * kt + 4 * G + e < te;
+                x[4 * kt + e] = valid ? sq[kt][e] * c : kNegInf;
+                mt = fmaxf(mt, x[4 * kt + e]);
+            }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m, mt);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m - m_new);
+        m = m_new;
+        const float msub = (m == kNegInf) ? 0.f : m;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                accA[dt][e] *= alpha;
+                accC[dt][e] *= alpha;
+            }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            accL[e] *= alpha;
+            accS[e] *= alpha;
+        }
+        f16x8 wp, ws;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = exp2_fast(x[4 * kt + e] - msub);
+                wp[4 * kt + e] = (_Float16)p;
+                ws[4 * kt + e] = (_Float16)(p * sr[kt][e]);
+            }
+        // The stage's V^T writes are visible to the whole wavefront.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f16x8 vf[S::DT];
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+            vf[dt] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
+                                                   vt + gqa_slot(16 * dt + l16, G) * 8));
+        accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, wp, accL, 0, 0, 0);
+        accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, ws, accS, 0, 0, 0);
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) {
+            accA[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], wp, accA[dt], 0, 0, 0);
+            accC[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], ws, accC[dt], 0, 0, 0);
+        }
+        // The next stage rewrites the V^T stage: its reads are done first.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // Merge: wavefront w's state of column c at [w][c] (m, ell, S, A[D],
+    // C[D]) in the stage memory, once every wavefront is done with it.
+    __syncthreads();
+    float *mg = reinterpret_cast<float *>(lds);
+    auto rec = [&](int w, int col) { return mg + (w * GQ + col) * (2 * D + 3); };
+    if (l16 < GQ) {
+        float *r0 = rec(wave, l16);
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r0[3 + 16 * dt + 4 * G + e] = accA[dt][e];
+                r0[3 + D + 16 * dt + 4 * G + e] = accC[dt][e];
+            }
+        if (G == 0) {
+            r0[0] = m;
+            r0[1] = accL[0];
+            r0[2] = accS[0];
+        }
+    }
+    __syncthreads();
+    for (int t = tid; t < GQ * D; t += 64 * NS) {
+        const int col = t / D;
+        const int f = t - col * D;
+        if (col >= ncol)
+            continue;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < NS; ++w)
+            M = fmaxf(M, rec(w, col)[0]);
+        float lt = 0.f, st = 0.f, at = 0.f, ct = 0.f;
+#pragma unroll
+        for (int w = 0; w < NS; ++w) {
+            const float *r0 = rec(w, col);
+            const float fw = (M == kNegInf) ? 0.f : exp2_fast(r0[0] - M);
+            lt += fw * r0[1];
+            st += fw * r0[2];
+            at += fw * r0[3 + f];
+            ct += fw * r0[3 + D + f];
+        }
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float keep = 1.f - st * inv;
+        const int64_t row = (int64_t)b * a.Hq + q0 + col;
+        a.o[row * D + f] = (at * keep + ct) * inv;
+        if (f == 0)
+            a.lse[row] = lt > 0.f ? (M + log2f(lt)) * kLn2 : kNegInf;
+    }
+}
+
+template <int D, int NS, int GQ>
+hipError_t launch_decode_gqa_t(const PagedDecodeArgs &a, hipStream_t stream) {
+    const int g = a.Hq / a.Hkv;
+    const dim3 grid((unsigned)(a.B * a.Hkv * ((g + GQ - 1) / GQ)));
+    PagedDecodeArgs args = a;
+    void *params[] = {&args};
+    const void *fn = a.block_table
+                         ? reinterpret_cast<const void *>(&parallax_decode_gqa_kernel<D, NS, GQ, true>)
+                         : reinterpret_cast<const void *>(&parallax_decode_gqa_kernel<D, NS, GQ, false>);
+    return hipLaunchKernel(fn, grid, dim3(64 * NS), params, 0, stream);
+}
+
+// Columns per workgroup: 4, 8 or 16 (the group, rounded up, at most 16).
+// Wavefronts: the requested splits, at most 8 (up to 256 registers per lane;
+// with 16 columns also the LDS of the merge); two such workgroups share a
+// CU.
+template <int D>
+hipError_t launch_decode_gqa(const PagedDecodeArgs &a, int num_splits, hipStream_t stream) {
+    const int g = a.Hq / a.Hkv;
+    const int gq = g <= 4 ? 4 : (g <= 8 ? 8 : 16);
+    const int ns = min(num_splits, 8);
+#define PLX_GQA(NSV)                                                   \
+    if (ns == NSV) {                                                   \
+        if (gq == 4) return launch_decode_gqa_t<D, NSV, 4>(a, stream); \
+        if (gq == 8) return launch_decode_gqa_t<D, NSV, 8>(a, stream); \
+        return launch_decode_gqa_t<D, NSV, 16>(a, stream);             \
+    }
+    PLX_GQA(1)
+    PLX_GQA(2)
+    PLX_GQA(4)
+    PLX_GQA(8)
+#undef PLX_GQA
+    return hipErrorInvalidValue;
+}
+
 template <int D, int NS, int GW>
 hipError_t launch_decode_paged_t(const PagedDecodeArgs &a, hipStream_t stream) {
     const int pairs = a.B * a.Hkv;
@@ -518,6 +829,8 @@ hipError_t launch_decode_paged_g(const PagedDecodeArgs &a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_decode_paged_d(const PagedDecodeArgs &a, int num_splits, hipStream_t stream) {
+    if (a.Hq / a.Hkv >= 4)
+        return launch_decode_gqa<D>(a, num_splits, stream);
     switch (num_splits) {
     case 1: return launch_decode_paged_g<D, 1>(a, stream);
     case 2: return launch_decode_paged_g<D, 2>(a, stream);

@@ -4,7 +4,9 @@ sinks) against the fp64 oracle (MI355X only).
 The oracle computes each row on the logical contiguous cache
 [B, Hkv, Lmax, d]; the GPU reads the same values scattered over a page pool
 through a shuffled block table.  Tolerances as for the plain decode: O max
-abs error <= 2e-2, LSE <= 1e-3 (the decode runs in fp32)."""
+abs error <= 2e-2, LSE <= 1e-3 (the decode runs in fp32; with Hq / Hkv >= 4
+the weights and values reach the matrix cores as float16, as in the
+prefill)."""
 import numpy as np
 import pytest
 import torch
@@ -79,6 +81,12 @@ CASES = [
     (2, 4, 2, 257, 128, [257, 256], 600, 0, 128, 1),
     (3, 8, 8, 400, 128, [400, 399, 1], 64, 0, None, 16),
     (3, 8, 2, 400, 64, None, 100, 2, None, 4),
+    # matrix-core path (Hq / Hkv >= 4): 16 heads per kv head (MQA), a group
+    # of 6 (columns 6..7 of its tile unused), and 20 heads (16 + 4 columns
+    # in two workgroups per kv head)
+    (2, 16, 1, 300, 128, [300, 77], 0, 0, 32, 16),
+    (2, 12, 2, 300, 64, [300, 5], 50, 3, 16, 4),
+    (1, 20, 1, 700, 128, None, 0, 0, None, 8),
 ]
 
 
