@@ -71,6 +71,7 @@ struct HadArgs {
 // Based linear attention (second-order Taylor kernel, 16 query/key
 // features): prefill in 512-token segments, decode on a fixed-size state.
 constexpr int kBasedSegment = 512;
+constexpr int kBasedQueryTile = 256;  // queries per output workgroup
 struct BasedArgs {
     const uint16_t *q, *k, *v;      // bf16 [B,H,L,16], [B,H,L,16], [B,H,L,dv]; strides below
     float *o;                       // fp32 [B,H,L,dv]
@@ -80,7 +81,7 @@ struct BasedArgs {
     int64_t o_b, o_h, o_l;
     int B, H, L;
     int n_seg;                      // ceil(L / kBasedSegment)
-    int n_qt;                       // ceil(L / 256): output workgroups per (batch, head)
+    int n_qt;                       // ceil(L / kBasedQueryTile): output workgroups per (batch, head)
     float scale;                    // x = scale * q.k
     float *dstate;                  // workspace: fp32 [B*H][n_seg][160][16 (dv/16 + 1)]
     uint16_t *sfrag;                // workspace: bf16 prefix-state fragments per segment

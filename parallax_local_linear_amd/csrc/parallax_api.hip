@@ -445,7 +445,7 @@ parallax_status parallax_based_fwd(const void *q, const void *k, const void *v, 
     if (workspace_bytes < plx::based_workspace_bytes(B, H, L, dv))
         return PARALLAX_ERR_INVALID_ARG;
     const int64_t n_seg = ((int64_t)L + plx::kBasedSegment - 1) / plx::kBasedSegment;
-    const int64_t n_qt = ((int64_t)L + 255) / 256;
+    const int64_t n_qt = ((int64_t)L + plx::kBasedQueryTile - 1) / plx::kBasedQueryTile;
     if ((int64_t)B * H * n_qt > INT_MAX || (int64_t)B * H * n_seg * 64 * 9 * 5 > INT_MAX)
         return PARALLAX_ERR_UNSUPPORTED;
     plx::BasedArgs a;

@@ -54,7 +54,7 @@ constexpr int BS = 32;     // tokens per MFMA stage
 constexpr int SUB = 4;     // stages per super-stage (one round of loads and barriers)
 constexpr int SST = SUB * BS;
 constexpr int KTS = BS + 4;  // padded K^T row (floats): conflict-free 16-byte reads
-constexpr int QT = 256;    // queries per output workgroup
+constexpr int QT = kBasedQueryTile;  // queries per output workgroup
 constexpr int QW = 32;     // queries per output wavefront
 constexpr int OW = QT / QW;
 static_assert(TS % QT == 0 && TS % SST == 0, "segment tiling");
