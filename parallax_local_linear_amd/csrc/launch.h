@@ -135,20 +135,21 @@ struct BwdArgs {
 //   stats: float [4][32] -- lse*log2(e) (+inf for rows >= L), 1 - sbar,
 //          G = dout.pv, G - dout.o
 //   key-kernel record (the query side of the stage, as the key kernel's LDS
-//          stage holds it): 6 groups of 1 KiB operand blocks, each block 64
-//          lanes x 16 bytes in lane order --
+//          stage holds it): 1 KiB operand blocks, each block 64 lanes x 16
+//          bytes in lane order --
 //            row-major q, rho, dout: block (t, c) for rows 16t + (l % 16),
 //              features 32c + 8 (l / 16) .. +7          (2 * d/32 blocks each)
-//            transposed q, rho, dout: block u for feature 16u + (l % 16),
-//              rows 4g .. 4g+3 and 16+4g .. 16+4g+3, g = l / 16  (d/16 each)
+//          (the key kernel reads the transposed operands out of these
+//          blocks with LDS transpose reads)
 //   query-kernel record (the key side of the stage): row-major k, row-major
-//          v, transposed k, in the same block formats.
+//          v, and transposed k: block u for feature 16u + (l % 16), rows
+//          4g .. 4g+3 and 16+4g .. 16+4g+3, g = l / 16  (d/16 blocks).
 // Rows >= L are zeros.
 constexpr int kBwdChunk = 16;
 __host__ __device__ inline size_t bwd_stats_bytes(int64_t BH, int64_t n_st) {
     return (size_t)(BH * n_st * 128 * 4);
 }
-__host__ __device__ constexpr size_t bwd_kv_record_bytes(int d) { return (size_t)6 * kStageKeys * d * 2; }
+__host__ __device__ constexpr size_t bwd_kv_record_bytes(int d) { return (size_t)3 * kStageKeys * d * 2; }
 __host__ __device__ constexpr size_t bwd_q_record_bytes(int d) { return (size_t)3 * kStageKeys * d * 2; }
 inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     const int64_t n_st = (L + kStageKeys - 1) / kStageKeys;

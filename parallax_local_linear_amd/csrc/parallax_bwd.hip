@@ -19,9 +19,9 @@
 //   * stats: per row lse*log2(e), 1 - sbar, G and G - Y (sbar and pv are
 //     saved by the forward);
 //   * records: q, rho, dO, k and v rearranged per 32-row stage into
-//     matrix-core operand blocks (below), row-major and, for q, rho, dO and
-//     k, transposed, so that every LDS read is one 16-byte read per lane
-//     and every stage is copied into LDS as contiguous 1 KiB blocks;
+//     matrix-core operand blocks (below), row-major and, for k, also
+//     transposed, so that every stage is copied into LDS as contiguous
+//     1 KiB blocks;
 //   * key kernel: a workgroup owns 128 keys (16 per wavefront), streams the
 //     query rows that see them and accumulates dv and dk;
 //   * query kernel: a workgroup owns 128 query rows (16 per wavefront),
@@ -42,10 +42,13 @@
 //     rows {4g .. 4g+3, 16+4g .. 16+4g+3} (g = l / 16) of a 32-row stage,
 //     which it uses directly as the B operand of dv^T += dO^T (p t) over the
 //     stage's 32 rows, provided the A operand lists the rows in the same
-//     order: that is the transposed image.
+//     order.  The key kernel reads that A operand straight out of the
+//     row-major q, rho and dO blocks with two ds_read_b64_tr_b16 per
+//     fragment (LDS transpose reads), so the stage it copies holds each
+//     tensor once.
 //   * The query kernel computes C = K Q^T (a lane holds one query row and
-//     four consecutive keys), so with the k image the same holds for
-//     dq^T += K^T dZ^T.
+//     four consecutive keys), so with a transposed image of k, stored in
+//     that order by the record kernel, the same holds for dq^T += K^T dZ^T.
 //   * Row-major operands (q, rho, dO in the key kernel; k, v in the query
 //     kernel) are stored as one 16-byte fragment per lane as well, so each
 //     1 KiB block is read back at lane * 16.  All of a stage's blocks are
@@ -193,8 +196,8 @@ __global__ __launch_bounds__(256) void parallax_bwd_stats_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Stage records.  A thread reads 16 bytes (8 features) of the 8 rows that
 // lane group g of a stage holds: it stores each 16-byte chunk as it is into
-// the row-major blocks, and transposes the 8 x 8 block in registers for the
-// transposed blocks (8 lanes' operands).  blockIdx.y picks the tensor:
+// the row-major blocks and, for k, transposes the 8 x 8 block in registers
+// for the transposed blocks (8 lanes' operands).  blockIdx.y picks the tensor:
 // 0 q, 1 rho, 2 dO (key-kernel record), 3 k, 4 v (query-kernel record).
 
 template <int D>
@@ -229,8 +232,8 @@ __global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
     const size_t rec_elems = kv_side ? bwd_kv_record_bytes(D) / 2 : bwd_q_record_bytes(D) / 2;
     uint16_t *recs = kv_side ? a.kvrec : a.qrec;
     const int rm_block0 = x * 2 * KC;
-    const int tr_block0 = kv_side ? 3 * 2 * KC + x * DT : 2 * 2 * KC;
-    const bool has_tr = which != 4;
+    const int tr_block0 = 2 * 2 * KC;   // k's image in the query-kernel record
+    const bool has_tr = which == 3;     // the key kernel transposes q, rho, dO in LDS
     for (int bh = blockIdx.z; bh < BH; bh += gridDim.z) {
         const int b = bh / a.H;
         const int h = bh - b * a.H;
@@ -273,9 +276,34 @@ __global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
 template <int D>
 struct KvStage {
     u32x4 rm[3 * 2 * BCfg<D>::KC][64];  // row-major q, rho, dO: block (x, qt, kc)
-    u32x4 tr[3 * BCfg<D>::DT][64];      // images of q, rho, dO: block (x, dt)
     float st[4][BS];
 };
+
+// Transposed fragment of a row-major stage tensor from two LDS transpose
+// reads (ds_read_b64_tr_b16): the A operand of dv^T += dO^T (p t) and of
+// the dk^T products, feature row 16 dt + l16 and the stage rows
+// {4G .. 4G+3, 16+4G .. 16+4G+3} (the order of the weights' B operand).
+// Within each 16-lane group the read gives lane 4a + b element b of the
+// 8-byte pieces addressed by lanes a, a+4, a+8, a+12; lane s of the group
+// therefore addresses row 16h + 4G + s/4, features 16 dt + 4 (s % 4) .. +3,
+// whose place in the fragment-order row-major blocks is
+//   block (h, dt / 2), lane (4G + s/4) + 16 (2 (dt % 2) + (s % 4) / 2),
+//   byte 8 ((s % 4) % 2) of its 16.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+template <int KC>
+__device__ __forceinline__ bf16x8 lds_frag_t(const u32x4 (*blocks)[64], int dt, int lane) {
+    const int G = lane >> 4, s = lane & 15;
+    const int a4 = s & 3;
+    const int off = ((4 * G + (s >> 2)) + 16 * (2 * (dt & 1) + (a4 >> 1))) * 16 + 8 * (a4 & 1);
+    const char *b0 = reinterpret_cast<const char *>(&blocks[0 * KC + dt / 2][0]) + off;
+    const char *b1 = reinterpret_cast<const char *>(&blocks[1 * KC + dt / 2][0]) + off;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(b0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(b1));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+}
 
 template <int I>
 using BufI = std::integral_constant<int, I % NB>;
@@ -285,8 +313,7 @@ __global__ __launch_bounds__(NTHREADS) void parallax_bwd_kv_kernel(BwdArgs a) {
     using C = BCfg<D>;
     constexpr int KC = C::KC, DT = C::DT;
     constexpr int NRM = 3 * 2 * KC;      // row-major blocks per stage
-    constexpr int NTR = 3 * DT;          // image blocks per stage
-    constexpr int NCP = (NRM + NTR + NW - 1) / NW;  // block copies per wave per stage
+    constexpr int NCP = (NRM + NW - 1) / NW;  // block copies per wave per stage
     constexpr int COPIES = NCP + 1;      // + an eighth of the stage's statistics
     __shared__ KvStage<D> sb0, sb1, sb2;
     auto sbuf = [&](auto b) -> KvStage<D> & {
@@ -386,8 +413,8 @@ __global__ __launch_bounds__(NTHREADS) void parallax_bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < NCP; ++c) {
             int bi = NW * c + wave;
-            if (NW * (c + 1) > NRM + NTR && bi >= NRM + NTR)
-                bi -= NRM + NTR;
+            if (NW * (c + 1) > NRM && bi >= NRM)
+                bi -= NRM;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 r_rec, (lds_void *)(reinterpret_cast<char *>(&S) + bi * 1024), 16,
                 (int)(bi * 1024 + lane * 16), (int)(s * kRec), 0, 0);
@@ -470,9 +497,9 @@ __global__ __launch_bounds__(NTHREADS) void parallax_bwd_kv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 tq = lds_frag(S.tr[0 * DT + dt], lane);
-            const bf16x8 tr = lds_frag(S.tr[1 * DT + dt], lane);
-            const bf16x8 to = lds_frag(S.tr[2 * DT + dt], lane);
+            const bf16x8 tq = lds_frag_t<KC>(&S.rm[0 * 2 * KC], dt, lane);
+            const bf16x8 tr = lds_frag_t<KC>(&S.rm[1 * 2 * KC], dt, lane);
+            const bf16x8 to = lds_frag_t<KC>(&S.rm[2 * 2 * KC], dt, lane);
 #pragma unroll
             for (int kt = 0; kt < RT; ++kt) {
                 dv[dt][kt] = mfma(to, wb[kt], dv[dt][kt]);
