@@ -140,9 +140,9 @@ parallax_status parallax_attn_fwd_train(const void *q, const void *k, const void
 
 /*
  * Bytes of device workspace parallax_attn_bwd needs: per (b, h) and 32-row
- * stage, 512 bytes of row statistics plus six bf16 operand blocks of
- * 32 * d elements (q, r, dout, k and v row-major; k transposed), i.e.
- * B * H * ceil(L / 32) * (512 + 384 * d)
+ * stage, 512 bytes of row statistics plus five bf16 operand blocks of
+ * 32 * d elements (q, r, dout, k and v), i.e.
+ * B * H * ceil(L / 32) * (512 + 320 * d)
  * bytes (0 when B, H or L is 0, or for sizes parallax_attn_bwd would
  * reject).
  */

@@ -139,18 +139,17 @@ struct BwdArgs {
 //          bytes in lane order --
 //            row-major q, rho, dout: block (t, c) for rows 16t + (l % 16),
 //              features 32c + 8 (l / 16) .. +7          (2 * d/32 blocks each)
-//          (the key kernel reads the transposed operands out of these
-//          blocks with LDS transpose reads)
-//   query-kernel record (the key side of the stage): row-major k, row-major
-//          v, and transposed k: block u for feature 16u + (l % 16), rows
-//          4g .. 4g+3 and 16+4g .. 16+4g+3, g = l / 16  (d/16 blocks).
+//   query-kernel record (the key side of the stage): row-major k and v in
+//          the same block format.
+//   The kernels read the transposed operands they need out of these
+//   blocks with LDS transpose reads.
 // Rows >= L are zeros.
 constexpr int kBwdChunk = 16;
 __host__ __device__ inline size_t bwd_stats_bytes(int64_t BH, int64_t n_st) {
     return (size_t)(BH * n_st * 128 * 4);
 }
 __host__ __device__ constexpr size_t bwd_kv_record_bytes(int d) { return (size_t)3 * kStageKeys * d * 2; }
-__host__ __device__ constexpr size_t bwd_q_record_bytes(int d) { return (size_t)3 * kStageKeys * d * 2; }
+__host__ __device__ constexpr size_t bwd_q_record_bytes(int d) { return (size_t)2 * kStageKeys * d * 2; }
 inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     const int64_t n_st = (L + kStageKeys - 1) / kStageKeys;
     return bwd_stats_bytes(B * H, n_st) +

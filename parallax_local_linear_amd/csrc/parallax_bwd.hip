@@ -194,16 +194,14 @@ __global__ __launch_bounds__(256) void parallax_bwd_stats_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Stage records.  A thread reads 16 bytes (8 features) of the 8 rows that
-// lane group g of a stage holds: it stores each 16-byte chunk as it is into
-// the row-major blocks and, for k, transposes the 8 x 8 block in registers
-// for the transposed blocks (8 lanes' operands).  blockIdx.y picks the tensor:
-// 0 q, 1 rho, 2 dO (key-kernel record), 3 k, 4 v (query-kernel record).
+// Stage records.  A thread copies 16 bytes (8 features) of 8 of a stage's
+// rows into their places in the row-major operand blocks.  blockIdx.y picks
+// the tensor: 0 q, 1 rho, 2 dO (key-kernel record), 3 k, 4 v (query-kernel
+// record).
 
 template <int D>
 __global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
     constexpr int KC = D / 32;
-    constexpr int DT = D / 16;
     constexpr int FC = D / 8;        // 16-byte feature chunks per row
     constexpr int TPS = 4 * FC;      // threads per stage
     constexpr int SPB = 256 / TPS;   // stages per block
@@ -225,15 +223,12 @@ __global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
                      : which == 3 ? a.k_h : a.v_h;
     const int64_t sl = which == 0 ? a.q_l : which == 1 ? a.r_l : which == 2 ? a.do_l
                      : which == 3 ? a.k_l : a.v_l;
-    // Record of this tensor, and the positions of its row-major and
-    // transposed groups in it.
+    // Record of this tensor, and the position of its blocks in it.
     const bool kv_side = which < 3;
     const int x = kv_side ? which : which - 3;
     const size_t rec_elems = kv_side ? bwd_kv_record_bytes(D) / 2 : bwd_q_record_bytes(D) / 2;
     uint16_t *recs = kv_side ? a.kvrec : a.qrec;
     const int rm_block0 = x * 2 * KC;
-    const int tr_block0 = 2 * 2 * KC;   // k's image in the query-kernel record
-    const bool has_tr = which == 3;     // the key kernel transposes q, rho, dO in LDS
     for (int bh = blockIdx.z; bh < BH; bh += gridDim.z) {
         const int b = bh / a.H;
         const int h = bh - b * a.H;
@@ -243,29 +238,15 @@ __global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
         uint16_t *rec = recs + ((size_t)bh * a.n_st + s) * rec_elems;
         u32x4 in[8];
 #pragma unroll
+        for (int e = 0; e < 8; ++e)
+            in[e] = bufld16(rs, (uint32_t)((8 * G + e) * sl * 2 + fc * 16));
+#pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int row = e < 4 ? 4 * G + e : 16 + 4 * G + (e - 4);
-            in[e] = bufld16(rs, (uint32_t)(row * sl * 2 + fc * 16));
             // Row-major block (row / 16, fc / 4), lane row % 16 + 16 (fc % 4).
+            const int row = 8 * G + e;
             const int blk = rm_block0 + (row / 16) * KC + fc / 4;
             const int lane = (row % 16) + 16 * (fc % 4);
             *reinterpret_cast<u32x4 *>(rec + (size_t)blk * BLK + lane * 8) = in[e];
-        }
-        if (!has_tr)
-            continue;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            u32x4 out;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t lo = (in[2 * w][u / 2] >> (16 * (u & 1))) & 0xffffu;
-                const uint32_t hi = (in[2 * w + 1][u / 2] >> (16 * (u & 1))) & 0xffffu;
-                out[w] = lo | (hi << 16);
-            }
-            const int f = 8 * fc + u;
-            const int blk = tr_block0 + f / 16;
-            const int lane = (f % 16) + 16 * G;
-            *reinterpret_cast<u32x4 *>(rec + (size_t)blk * BLK + lane * 8) = out;
         }
     }
 }
@@ -561,7 +542,6 @@ __global__ __launch_bounds__(NTHREADS) void parallax_bwd_kv_kernel(BwdArgs a) {
 template <int D>
 struct QStage {
     u32x4 rm[2 * 2 * BCfg<D>::KC][64];  // row-major k, v: block (x, kt, kc)
-    u32x4 tr[BCfg<D>::DT][64];          // k image: block dt
 };
 
 template <int D>
@@ -569,7 +549,7 @@ __global__ __launch_bounds__(NTHREADS) void parallax_bwd_q_kernel(BwdArgs a) {
     using C = BCfg<D>;
     constexpr int KC = C::KC, DT = C::DT;
     constexpr int NRM = 2 * 2 * KC;
-    constexpr int NCP = (NRM + DT + NW - 1) / NW;
+    constexpr int NCP = (NRM + NW - 1) / NW;
     __shared__ QStage<D> sb0, sb1, sb2;
     auto sbuf = [&](auto b) -> QStage<D> & {
         constexpr int i = decltype(b)::value % NB;
@@ -661,8 +641,8 @@ __global__ __launch_bounds__(NTHREADS) void parallax_bwd_q_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < NCP; ++c) {
             int bi = NW * c + wave;
-            if (NW * (c + 1) > NRM + DT && bi >= NRM + DT)
-                bi -= NRM + DT;
+            if (NW * (c + 1) > NRM && bi >= NRM)
+                bi -= NRM;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 r_rec, (lds_void *)(reinterpret_cast<char *>(&S) + bi * 1024), 16,
                 (int)(bi * 1024 + lane * 16), (int)(s * kRec), 0, 0);
@@ -727,7 +707,7 @@ __global__ __launch_bounds__(NTHREADS) void parallax_bwd_q_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 tk = lds_frag(S.tr[dt], lane);
+            const bf16x8 tk = lds_frag_t<KC>(&S.rm[0], dt, lane);
 #pragma unroll
             for (int qt = 0; qt < RT; ++qt) {
                 dq[dt][qt] = mfma(tk, zb[qt], dq[dt][qt]);

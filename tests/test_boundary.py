@@ -182,8 +182,8 @@ def test_fwd_train_empty_is_a_no_op(lib):
 
 
 def expected_bwd_workspace(B, H, L, d):
-    """Per 32-row stage: 512 bytes of row statistics + six bf16 blocks of 32*d."""
-    return B * H * (-(-L // 32)) * (512 + 6 * 32 * d * 2)
+    """Per 32-row stage: 512 bytes of row statistics + five bf16 blocks of 32*d."""
+    return B * H * (-(-L // 32)) * (512 + 5 * 32 * d * 2)
 
 
 @pytest.mark.parametrize("B,H,L,d", [(1, 1, 1, 64), (2, 3, 32, 128), (2, 16, 8192, 128),
