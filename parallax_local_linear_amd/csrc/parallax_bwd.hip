@@ -19,9 +19,8 @@
 //   * stats: per row lse*log2(e), 1 - sbar, G and G - Y (sbar and pv are
 //     saved by the forward);
 //   * records: q, rho, dO, k and v rearranged per 32-row stage into
-//     matrix-core operand blocks (below), row-major and, for k, also
-//     transposed, so that every stage is copied into LDS as contiguous
-//     1 KiB blocks;
+//     row-major matrix-core operand blocks (below), so that every stage is
+//     copied into LDS as contiguous 1 KiB blocks;
 //   * key kernel: a workgroup owns 128 keys (16 per wavefront), streams the
 //     query rows that see them and accumulates dv and dk;
 //   * query kernel: a workgroup owns 128 query rows (16 per wavefront),
@@ -38,7 +37,8 @@
 // positions 8 (l / 16) .. +7 of A; column l % 16 and the same positions of
 // B; holds rows 4 (l / 16) .. +3 of column l % 16 of C):
 //   * The key kernel computes C = Q K^T per 16 x 16 tile: a lane holds one
-//     of the wavefront's 16 keys and four consecutive query rows.  Two query tiles give a lane the
+//     of the wavefront's 16 keys and four consecutive query rows.  Two
+//     query tiles give a lane the
 //     rows {4g .. 4g+3, 16+4g .. 16+4g+3} (g = l / 16) of a 32-row stage,
 //     which it uses directly as the B operand of dv^T += dO^T (p t) over the
 //     stage's 32 rows, provided the A operand lists the rows in the same
@@ -47,10 +47,10 @@
 //     fragment (LDS transpose reads), so the stage it copies holds each
 //     tensor once.
 //   * The query kernel computes C = K Q^T (a lane holds one query row and
-//     four consecutive keys), so with a transposed image of k, stored in
-//     that order by the record kernel, the same holds for dq^T += K^T dZ^T.
+//     four consecutive keys), and reads K^T for dq^T += K^T dZ^T out of the
+//     row-major k blocks the same way.
 //   * Row-major operands (q, rho, dO in the key kernel; k, v in the query
-//     kernel) are stored as one 16-byte fragment per lane as well, so each
+//     kernel) are stored as one 16-byte fragment per lane, so each
 //     1 KiB block is read back at lane * 16.  All of a stage's blocks are
 //     one contiguous record, copied with one buffer resource and a scalar
 //     offset per stage (no per-copy address arithmetic).
