@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
     __shared__ OutLds<DV> s;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, G = lane >> 4;
     const int bh = blockIdx.x / a.n_qt;
     const int qt = blockIdx.x - bh * a.n_qt;
@@ -408,17 +408,32 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
     const uint16_t *kb = a.k + (int64_t)b * a.k_b + (int64_t)h * a.k_h;
     const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h;
 
-    // The prefix state's fragments of this segment into LDS.
+    // The prefix state's fragments of this segment, 1 KiB blocks copied
+    // straight into LDS, all in flight at once with the query loads below.
+    // Wave w copies blocks w, w + OW, ...; a spare slot copies the last block
+    // again (the same bytes to the same place).
     {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(
-            a.sfrag + ((int64_t)bh * a.n_seg + seg) * (C::CB * NFC * 512));
-        u32x4 *dst = &s.sfrag[0][0][0];
-        for (int i = tid; i < C::CB * NFC * 64; i += NT)
-            dst[i] = src[i];
+        constexpr int NBLK = C::CB * NFC;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(a.sfrag + ((int64_t)bh * a.n_seg + seg) * (NBLK * 512), NBLK * 1024);
+#pragma unroll
+        for (int c = 0; c < (NBLK + OW - 1) / OW; ++c) {
+            const int blk = min(OW * c + wave, NBLK - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void *)(&s.sfrag[0][0][0] + blk * 64), 16,
+                lane * 16, blk * 1024, 0, 0);
+        }
     }
 
     // This wavefront's queries: 16 g + l16 of rows q0 + 32 wave .. +31.
     const int wq0 = q0 + QW * wave;
+    u32x4 xq[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int row = min(wq0 + 16 * g + l16, a.L - 1);
+        xq[g][0] = *reinterpret_cast<const u32x4 *>(qb + (int64_t)row * a.q_l);
+        xq[g][1] = *reinterpret_cast<const u32x4 *>(qb + (int64_t)row * a.q_l + 8);
+    }
     f32x4 acc[C::CB][2];
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
@@ -426,16 +441,20 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
         for (int g = 0; g < 2; ++g)
             acc[cb][g] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // state fragments in LDS
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+    __syncthreads();                     // and every other wave's
+
+    // The first key/value super-stage, in flight during the state term.
+    using IO = StageIO<DV>;
+    IO io;
+    io.load(kb, vb, a.k_l, a.v_l, seg_begin, a.L, tid);
 
     // State term: O^T += S^T Phi(Q)^T (bf16 operands); also the score B
     // fragments (features 4G .. 4G+3 of each query).
     bf16x4 qfrag[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-        const int row = min(wq0 + 16 * g + l16, a.L - 1);
-        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(qb + (int64_t)row * a.q_l);
-        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(qb + (int64_t)row * a.q_l + 8);
+        const u32x4 x0 = xq[g][0], x1 = xq[g][1];
         float u[BK];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -463,8 +482,6 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
 
     // Causal sum over the segment's keys up to this workgroup's last query,
     // in super-stages of 128 keys (4 MFMA stages of 32).
-    using IO = StageIO<DV>;
-    IO io;
     const int q_last = min(q0 + QT, a.L) - 1;           // last query of the workgroup
     const int n_sst = (q_last - seg_begin) / SST + 1;
     const int w_last = min(wq0 + QW, a.L) - 1;          // last query of the wavefront
@@ -472,7 +489,6 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
     const f16x8 ones = {one, one, one, one, one, one, one, one};
     const float xs = a.scale;
 
-    io.load(kb, vb, a.k_l, a.v_l, seg_begin, a.L, tid);
     for (int ss = 0; ss < n_sst; ++ss) {
         __syncthreads();  // the previous super-stage has been read
         io.store_v(&s.vt[0][0], tid);
