@@ -488,6 +488,7 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
     const _Float16 one = (_Float16)1.0f;
     const f16x8 ones = {one, one, one, one, one, one, one, one};
     const float xs = a.scale;
+    const float c2 = 0.5f * xs * xs;
 
     for (int ss = 0; ss < n_sst; ++ss) {
         __syncthreads();  // the previous super-stage has been read
@@ -512,7 +513,9 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
             for (int cb = 0; cb < C::VB; ++cb)
                 vf[cb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
                                                        &s.vt[sub][(16 * cb + l16) * VTS + 8 * G]));
-            const bool diag = t0 + BS - 1 > wq0;  // some key may follow some query
+            // Some key may follow some query only where the stage reaches
+            // the wavefront's first query; elsewhere the threshold keeps all.
+            const bool diag = t0 + BS - 1 > wq0;
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
                 // S^T tile kt: lane holds keys t0 + 16 kt + 4G + e of query
@@ -524,13 +527,13 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
                     const f32x4 sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                         __builtin_bit_cast(s16x4, kf[kt]), __builtin_bit_cast(s16x4, qfrag[g]),
                         (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    // key t0 + 16 kt + 4G + e is visible iff e <= lim
+                    const int lim = diag ? qrow - (t0 + 16 * kt + 4 * G) : 3;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float x = xs * sc[e];
-                        float wt = __builtin_fmaf(0.5f * x, x, x + 1.f);
-                        if (diag && t0 + 16 * kt + 4 * G + e > qrow)
-                            wt = 0.f;
-                        w[4 * kt + e] = (_Float16)wt;
+                        // 1 + x + x^2 / 2 at x = scale s, as (c2 s + scale) s + 1
+                        const float wt = __builtin_fmaf(__builtin_fmaf(c2, sc[e], xs), sc[e], 1.f);
+                        w[4 * kt + e] = (_Float16)(e <= lim ? wt : 0.f);
                     }
                 }
 #pragma unroll
