@@ -498,8 +498,8 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
         __syncthreads();
         if (ss + 1 < n_sst)
             io.load(kb, vb, a.k_l, a.v_l, seg_begin + (ss + 1) * SST, a.L, tid);
-        // Not unrolled: one stage's fragments live at a time.
-#pragma unroll 1
+        // Unrolled: the next stage's fragment reads can overlap this one's products.
+#pragma unroll
         for (int sub = 0; sub < SUB; ++sub) {
             const int t0 = seg_begin + ss * SST + sub * BS;
             if (t0 > w_last)
