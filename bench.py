@@ -54,6 +54,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_fwd.hip"),
     "decode": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
+    "decode_paged": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
+    "decode_gqa": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
+    "based_decode": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_based.hip"),
     "backward": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_bwd.hip"),
     "projection": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_proj.hip"),
     "hadamard": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_hadamard.hip"),
@@ -243,12 +246,16 @@ def time_decode_paged(dcfg, steps, warmup, stream):
         ms = e0.elapsed_time(e1) / steps
         nbytes = 2 * B * Hkv * Lmax * d * 2 + B * Hq * (2 * d * 2 + d * 4 + 4) + B * Lmax // page * 4
         gbs = nbytes / (ms * 1e-3) / 1e9
+        # Four or more query heads per kv head take the matrix-core kernel.
+        gqa = Hq // Hkv >= 4
         out.append({"Hq": Hq, "Hkv": Hkv, "page": page, "ms": round(ms, 4),
                     "value": round(gbs, 1), "unit": "GB/s",
                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                  "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                 "traffic": None, "algorithmic_bytes_per_launch": nbytes,
-                                 "kernel": "parallax_decode_paged_kernel<128,...>"}})
+                                 "traffic": measured_traffic("decode_gqa" if gqa else "decode_paged"),
+                                 "algorithmic_bytes_per_launch": nbytes,
+                                 "kernel": "parallax_decode_gqa_kernel<128,...>" if gqa
+                                           else "parallax_decode_paged_kernel<128,...>"}})
         del kp, vp
     return out
 
@@ -377,6 +384,7 @@ def time_based(steps, warmup, stream):
                                    "parallax_based_out_kernel<128>"},
             "decode": {"B": Bd, "H": cfg.H, "ms": round(ms_d, 4), "value": round(dgbs, 1),
                        "unit": "GB/s", "frac": round(dgbs / PEAK_HBM_GBS, 4),
+                       "traffic": measured_traffic("based_decode"),
                        "algorithmic_bytes_per_launch": dbytes,
                        "kernel": "parallax_based_decode_kernel<128>"}}
 
