@@ -39,6 +39,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -61,7 +62,20 @@ KERNEL_SOURCES = {
     "projection": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_proj.hip"),
     "hadamard": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_hadamard.hip"),
     "based": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_based.hip"),
+    "prefill_0.6b": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_fwd.hip"),
+    "local_swa128_sink4": os.path.join(ROOT, "parallax_local_linear_amd", "csrc",
+                                       "parallax_fwd.hip"),
 }
+# Kernels one prefill call launches, per workload.
+PREFILL_KERNELS = {
+    "prefill_1.7b_long": "parallax_attn_fwd call = parallax_vprep_kernel<128> + "
+                         "parallax_fwd_kernel<128, true, false>",
+    "prefill_0.6b": "parallax_attn_fwd call = parallax_vprep_kernel<64> + "
+                    "parallax_fwd_kernel<64, true, false>",
+    "local_swa128_sink4": "parallax_attn_fwd call = parallax_vprep_kernel<64> + "
+                          "parallax_fwd_kernel<64, true, false>",
+}
+FLUSH_BYTES = 512 << 20     # overwritten between timed calls: more than L2 + the 256 MB MALL
 
 
 def parse():
@@ -73,8 +87,9 @@ def parse():
                    help="skip timing the CPU oracle (profiling runs)")
     p.add_argument("--cpu-sample-heads", type=int, default=16,
                    help="(b,h) slices of the prefill workload the CPU oracle computes")
-    p.add_argument("--extra", action="store_true",
-                   help="also time the other prefill workloads (printed to stderr)")
+    p.add_argument("--cpu-single-heads", type=int, default=8,
+                   help="(b,h) slices of the 0.6B-like workload the single-thread oracle run "
+                        "computes")
     p.add_argument("--no-backward", action="store_true",
                    help="skip timing the prefill backward")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -101,8 +116,27 @@ def measured_traffic(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, n_heads: int):
-    """Time the fp64 oracle on all rows of the first n_heads (b, h) slices."""
+def host_cpu():
+    """The host's CPU model, its logical CPU count and the CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def time_oracle_slices(cfg, n_heads: int, nthreads: int):
+    """Seconds and algorithmic FLOP of the fp64 oracle on all rows of the first
+    n_heads (b, h) slices of a prefill workload, on nthreads host threads."""
     import numpy as np
     import torch
 
@@ -111,7 +145,6 @@ def cpu_baseline(cfg, n_heads: int):
 
     q, k, v, r = workloads.prefill_inputs(cfg, device="cpu")
     orc = oracle.default()
-    nthreads = oracle.default_threads()
     scale = 1.0 / np.sqrt(cfg.d)
     pos = np.arange(cfg.L)
     f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
@@ -122,38 +155,94 @@ def cpu_baseline(cfg, n_heads: int):
         orc.rows(Q, R, pos, K, V, scale, cfg.window, cfg.n_sink, nthreads=nthreads)
     dt = time.perf_counter() - t0
     flops = 8 * cfg.d * len(slices) * accounting.visible_pairs(cfg.L, cfg.window, cfg.n_sink)
+    return dt, flops, len(slices)
+
+
+def cpu_baseline(cfg, n_heads: int, single_cfg, single_heads: int):
+    """The fp64 oracle on the host: all rows of the first n_heads (b, h) slices
+    of the headline workload on the default thread count, and one
+    single-thread run on single_heads slices of single_cfg."""
+    import oracle
+
+    nthreads = oracle.default_threads()
+    dt, flops, n = time_oracle_slices(cfg, n_heads, nthreads)
+    dt1, flops1, n1 = time_oracle_slices(single_cfg, single_heads, 1)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
             "sample": "all %d rows of %d of the %d (b,h) slices of %s (%.3g GFLOP, %.1f s)"
-                      % (cfg.L, len(slices), cfg.B * cfg.H, cfg.name, flops / 1e9, dt)}
+                      % (cfg.L, n, cfg.B * cfg.H, cfg.name, flops / 1e9, dt),
+            "threads_used": nthreads,
+            "host": host_cpu(),
+            "single_thread": {
+                "value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                "sample": "all %d rows of %d of the %d (b,h) slices of %s (%.3g GFLOP, %.1f s)"
+                          % (single_cfg.L, n1, single_cfg.B * single_cfg.H, single_cfg.name,
+                             flops1 / 1e9, dt1)}}
 
 
-def time_prefill_only(cfg, steps, warmup, stream):
-    """Median-free mean kernel time (ms) of one prefill workload (for --extra)."""
+def time_each_call(fn, runs, warmup, stream, flush=None):
+    """Per-call times (ms) from HIP events recorded on `stream` around each
+    call; with `flush` (a device byte tensor), the tensor is overwritten on
+    the same stream before every call, outside the timed region, so that the
+    call starts with its inputs out of L2 and the MALL."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for i in range(runs):
+        if flush is not None:
+            with torch.cuda.stream(stream):
+                flush.fill_(i & 0xff)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return times
+
+
+def time_prefill_leg(cfg, bound, runs, warmup, stream, flush=None):
+    """One prefill workload timed call by call (median and min over `runs`),
+    with its roofline: the matrix-core peak for the compute-bound causal
+    workloads, HBM for the windowed one (8d FLOP per visible pair; bytes:
+    q, k, v, r read once, the fp32 output and lse written once)."""
+
     import torch
 
-    from parallax_local_linear_amd import accounting, parallax_attn_fwd, workloads
-    from parallax_local_linear_amd import parallax_attn_fwd_workspace_size
-    q, k, v, r = workloads.prefill_inputs(cfg, device="cuda:0")
-    o = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(parallax_attn_fwd_workspace_size(cfg.B, cfg.H, cfg.L, cfg.d),
-                     dtype=torch.uint8, device="cuda:0")
-    for _ in range(warmup):
-        parallax_attn_fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,
-                          workspace=ws, stream=stream)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        parallax_attn_fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,
-                          workspace=ws, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    return {"workload": cfg.name, "ms": ms,
-            "tflops": accounting.prefill_flops(cfg) / (ms * 1e-3) / 1e12,
-            "gbs": accounting.prefill_bytes(cfg) / (ms * 1e-3) / 1e9}
+    from parallax_local_linear_amd import (accounting, parallax_attn_fwd,
+                                           parallax_attn_fwd_workspace_size, workloads)
+    dev = torch.device("cuda:0")
+    q, k, v, r = workloads.prefill_inputs(cfg, device=dev)
+    o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, parallax_attn_fwd_workspace_size(cfg.B, cfg.H, cfg.L, cfg.d)),
+                     dtype=torch.uint8, device=dev)
+    times = time_each_call(
+        lambda: parallax_attn_fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o,
+                                  lse=lse, workspace=ws, stream=stream),
+        runs, warmup, stream, flush)
+    med = statistics.median(times)
+    flops = accounting.prefill_flops(cfg)
+    nbytes = accounting.prefill_bytes(cfg)
+    tflops = flops / (med * 1e-3) / 1e12
+    gbs = nbytes / (med * 1e-3) / 1e9
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": nbytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+                "algorithmic_flop_per_launch": flops}
+    roof["traffic"] = measured_traffic(cfg.name)
+    roof["kernel"] = PREFILL_KERNELS.get(cfg.name)
+    return {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "L": cfg.L, "d": cfg.d,
+            "window": cfg.window, "n_sink": cfg.n_sink,
+            "ms_median": round(med, 4), "ms_min": round(min(times), 4), "runs": runs,
+            "mall_flush": flush is not None,
+            "value": roof["achieved"], "unit": roof["unit"],
+            "tflops": round(tflops, 2), "gbs": round(gbs, 1), "roofline": roof}
 
 
 def time_backward(cfg, steps, warmup, stream):
@@ -494,6 +583,8 @@ def main():
             "precision": "bf16 inputs; bf16 score MFMA, f16 value MFMA, fp32 accumulate; fp32 O",
         },
         "prefill_ms": round(pre_avg, 4),
+        "prefill_ms_median": round(statistics.median(pre_ms), 4),
+        "prefill_ms_min": round(min(pre_ms), 4),
         "roofline": {
             "bound": "mfma",
             "achieved": round(p_tflops, 2),
@@ -509,6 +600,8 @@ def main():
             "value": round(d_gbs, 1),
             "unit": "GB/s",
             "ms": round(dec_avg, 4),
+            "ms_median": round(statistics.median(dec_ms), 4),
+            "ms_min": round(min(dec_ms), 4),
             "roofline": {
                 "bound": "hbm",
                 "achieved": round(d_gbs, 1),
@@ -536,12 +629,16 @@ def main():
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         res["backward"] = time_backward(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
                                         stream)
-    if args.extra:
-        for cfg in (workloads.PREFILL_06B, workloads.LOCAL, workloads.TINY):
-            print(json.dumps(time_prefill_only(cfg, 20, 3, stream)), file=sys.stderr, flush=True)
+    print("[bench] timing the 0.6B-like and windowed prefill workloads", file=sys.stderr,
+          flush=True)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    res["prefill_0.6b"] = time_prefill_leg(workloads.PREFILL_06B, "mfma", 20, 5, stream, flush)
+    res["local_swa128_sink4"] = time_prefill_leg(workloads.LOCAL, "hbm", 20, 5, stream, flush)
+    del flush
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(pcfg, args.cpu_sample_heads)
+        res["cpu_baseline"] = cpu_baseline(pcfg, args.cpu_sample_heads, workloads.PREFILL_06B,
+                                           args.cpu_single_heads)
     print(json.dumps(res), flush=True)
 
 

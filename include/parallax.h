@@ -199,7 +199,8 @@ parallax_status parallax_attn_bwd(const void *q, const void *k, const void *v, c
  *   q, r       : bf16 [B, H, d], contiguous, 16-byte aligned.
  *   k_cache,
  *   v_cache    : bf16 [B, H, Lmax, d] with strides sk, sv (16-byte aligned
- *                base, strides multiples of 8 elements).
+ *                base, strides multiples of 8 elements; row strides sk.l,
+ *                sv.l below 2^24 elements, else PARALLAX_ERR_UNSUPPORTED).
  *   seqlens    : DEVICE int32 [B] or NULL (= Lmax for every sequence).  The
  *                cache already holds the current token: the query sits at
  *                position seqlen-1 and sees keys 0 .. seqlen-1.  Values are

@@ -34,15 +34,14 @@ _L = ctypes.POINTER(ctypes.c_long)
 _I = ctypes.POINTER(ctypes.c_int)
 
 
-def build(out: str = LIBRARY, mutant: int = 0) -> str:
+def build(out: str = LIBRARY, source: str = SOURCE) -> str:
     """Compile the oracle with gcc (OpenMP, IEEE fp64; no fast-math).
 
-    ``mutant`` > 0 plants one deliberate mistake (see the C file); such
-    builds exist only for the tests that prove the pins catch mistakes.
+    ``source`` defaults to ``parallax_oracle.c``; the oracle's self-test
+    builds patched copies of it that each plant one deliberate mistake.
     """
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-           "-DORACLE_MUTANT=%d" % int(mutant), "-o", tmp, SOURCE, "-lm"]
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", tmp, source, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

@@ -49,9 +49,9 @@
  * values.  Two plain passes over the visible keys; no tiling, no online
  * rescaling.
  *
- * Build with -DORACLE_MUTANT=n (n >= 1) to plant one deliberate mistake; the
- * CPU tests use such builds to show that the pins catch each of them.  The
- * default build (ORACLE_MUTANT = 0) contains no planted mistake.
+ * The CPU tests plant deliberate mistakes in patched copies of this file
+ * (tests/oracle_mutants.py) to show that the pins catch each of them; this
+ * file itself contains none.
  */
 #include <math.h>
 #include <stdlib.h>
@@ -60,28 +60,13 @@
 #include <omp.h>
 #endif
 
-#ifndef ORACLE_MUTANT
-#define ORACLE_MUTANT 0
-#endif
-
 /* Is key j visible from query position i? */
 static int visible(long i, long j, long window, long n_sink)
 {
-#if ORACLE_MUTANT == 4
-    /* planted mistake: sink keys visible even ahead of the query */
-    if (j >= 0 && j < n_sink)
-        return 1;
-#endif
     if (j < 0 || j > i)
         return 0;
-#if ORACLE_MUTANT == 5
-    /* planted mistake: window boundary off by one (W+1 keys) */
-    if (window <= 0 || i - j <= window || j < n_sink)
-        return 1;
-#else
     if (window <= 0 || i - j < window || j < n_sink)
         return 1;
-#endif
     return 0;
 }
 
@@ -130,12 +115,7 @@ static void one_row(const double *q_i, const double *r_i, long i,
         z[j] = exp(z[j] - m);
         ell += z[j];
     }
-#if ORACLE_MUTANT == 6
-    /* planted mistake: log-sum-exp without the max */
-    *lse_i = log(ell);
-#else
     *lse_i = m + log(ell);
-#endif
     for (long j = 0; j <= last; ++j)
         if (visible(i, j, window, n_sink))
             z[j] /= ell;
@@ -146,12 +126,7 @@ static void one_row(const double *q_i, const double *r_i, long i,
     for (long j = 0; j <= last; ++j) {
         if (!visible(i, j, window, n_sink))
             continue;
-#if ORACLE_MUTANT == 7
-        /* planted mistake: key mean with unnormalised weights */
-        double w = z[j] * ell;
-#else
         double w = z[j];
-#endif
         for (int t = 0; t < d; ++t)
             kbar[t] += w * k[j * (long)d + t];
     }
@@ -163,20 +138,8 @@ static void one_row(const double *q_i, const double *r_i, long i,
         const double *kj = k + j * (long)d;
         double s = 0.0;
         for (int t = 0; t < d; ++t) {
-#if ORACLE_MUTANT == 2
-            /* planted mistake: correction not centred on kbar */
-            s += r_i[t] * kj[t];
-#elif ORACLE_MUTANT == 8
-            /* planted mistake: probe read against the values, not the keys */
-            s += r_i[t] * (v[j * (long)d + t] - kbar[t]);
-#else
             s += r_i[t] * (kj[t] - kbar[t]);
-#endif
         }
-#if ORACLE_MUTANT == 3
-        /* planted mistake: softmax scale also applied to the correction */
-        s *= scale;
-#endif
         c[j] = s;
     }
 
@@ -184,18 +147,7 @@ static void one_row(const double *q_i, const double *r_i, long i,
     for (long j = 0; j <= last; ++j) {
         if (!visible(i, j, window, n_sink))
             continue;
-#if ORACLE_MUTANT == 1
-        /* planted mistake: correction with the wrong sign */
-        double w = z[j] * (1.0 - c[j]);
-#elif ORACLE_MUTANT == 9
-        /* planted mistake: plain softmax term dropped */
-        double w = z[j] * c[j];
-#elif ORACLE_MUTANT == 10
-        /* planted mistake: weights taken from the previous key */
-        double w = (j > 0 ? z[j - 1] : z[j]) * (1.0 + c[j]);
-#else
         double w = z[j] * (1.0 + c[j]);
-#endif
         const double *vj = v + j * (long)d;
         for (int t = 0; t < d; ++t)
             o_i[t] += w * vj[t];
@@ -297,12 +249,7 @@ int parallax_oracle_decode_ext(const double *q, const double *r,
         if (n > Lmax)
             n = Lmax;
         for (long h = 0; h < Hq && rc == 0; ++h) {
-#if ORACLE_MUTANT == 17
-            /* planted mistake: query heads mapped to kv heads round-robin */
-            long hk = h % Hkv;
-#else
             long hk = h / g;
-#endif
             long bh = b * Hq + h;
             long p = n - 1;
             const double *kc = k_cache + (b * Hkv + hk) * Lmax * d;
@@ -413,12 +360,7 @@ static void one_row_bwd(const double *q_i, const double *r_i, const double *do_i
     for (long j = 0; j < n_ctx; ++j) {
         if (!visible(i, j, window, n_sink))
             continue;
-#if ORACLE_MUTANT == 14
-        /* planted mistake: value gradient without the probe correction */
-        double u = p[j];
-#else
         double u = p[j] * (1.0 + c[j]);
-#endif
         for (int t = 0; t < d; ++t)
             dv[j * (long)d + t] += u * do_i[t];
         double du = dot(do_i, v + j * (long)d, d);
@@ -433,33 +375,21 @@ static void one_row_bwd(const double *q_i, const double *r_i, const double *do_i
             continue;
         const double *kj = k + j * (long)d;
         for (int t = 0; t < d; ++t) {
-#if ORACLE_MUTANT == 15
-            /* planted mistake: probe gradient not centred on kbar */
-            dr_i[t] += dc[j] * kj[t];
-#else
             dr_i[t] += dc[j] * (kj[t] - kbar[t]);
-#endif
             dk[j * (long)d + t] += dc[j] * r_i[t];
         }
         sum_dc += dc[j];
     }
     for (int t = 0; t < d; ++t)
-#if ORACLE_MUTANT == 12
-        /* planted mistake: adjoint of the key mean with the wrong sign */
-        dkbar[t] = sum_dc * r_i[t];
-#else
         dkbar[t] = -sum_dc * r_i[t];
-#endif
 
     /* (3') */
     for (long j = 0; j < n_ctx; ++j) {
         if (!visible(i, j, window, n_sink))
             continue;
         dp[j] += dot(dkbar, k + j * (long)d, d);
-#if ORACLE_MUTANT != 16
         for (int t = 0; t < d; ++t)
             dk[j * (long)d + t] += p[j] * dkbar[t];
-#endif
     }
 
     /* (2') */
@@ -467,10 +397,6 @@ static void one_row_bwd(const double *q_i, const double *r_i, const double *do_i
     for (long j = 0; j < n_ctx; ++j)
         if (visible(i, j, window, n_sink))
             mean_dp += p[j] * dp[j];
-#if ORACLE_MUTANT == 11
-    /* planted mistake: softmax adjoint without its mean term */
-    mean_dp = 0.0;
-#endif
 
     /* (1'), with dz_j formed on the fly */
     for (long j = 0; j < n_ctx; ++j) {
@@ -479,12 +405,7 @@ static void one_row_bwd(const double *q_i, const double *r_i, const double *do_i
         double dz = p[j] * (dp[j] - mean_dp);
         const double *kj = k + j * (long)d;
         for (int t = 0; t < d; ++t) {
-#if ORACLE_MUTANT == 13
-            /* planted mistake: query gradient without the softmax scale */
-            dq_i[t] += dz * kj[t];
-#else
             dq_i[t] += scale * dz * kj[t];
-#endif
             dk[j * (long)d + t] += scale * dz * q_i[t];
         }
     }
@@ -613,20 +534,11 @@ static void lla_row(const double *q_i, long i, const double *k, const double *v,
                 continue;
             const double *kj = k + j * (long)d;
             double c = 0.0;
-#if ORACLE_MUTANT == 18
-            /* planted mistake: covariance product not centred on kbar */
-            for (int t = 0; t < d; ++t)
-                c += kj[t] * dir[t];
-            c *= p[j];
-            for (int t = 0; t < d; ++t)
-                Ad[t] += c * kj[t];
-#else
             for (int t = 0; t < d; ++t)
                 c += (kj[t] - kbar[t]) * dir[t];
             c *= p[j];
             for (int t = 0; t < d; ++t)
                 Ad[t] += c * (kj[t] - kbar[t]);
-#endif
         }
         const double dAd = dot(dir, Ad, d);
         if (!(dAd > 0.0))
@@ -710,12 +622,7 @@ int parallax_oracle_project(const double *x, const double *w, double *y, long M,
         for (long n = 0; n < N; ++n) {
             double s = 0.0;
             for (long t = 0; t < K; ++t)
-#if ORACLE_MUTANT == 19
-                /* planted mistake: the weight read transposed */
-                s += x[i * K + t] * w[(t % N) * K + (n % K)];
-#else
                 s += x[i * K + t] * w[n * K + t];
-#endif
             y[i * N + n] = s;
         }
     return 0;
@@ -756,46 +663,21 @@ int parallax_oracle_hadamard(const double *y, const double *alpha, const double 
             for (long j = 0; j < m; ++j) {
                 const double e = h[i * n + j];
                 h[i * n + j + m] = e;
-#if ORACLE_MUTANT == 21
-                /* planted mistake: the sign of the lower-left block flipped */
-                h[(i + m) * n + j] = -e;
-                h[(i + m) * n + j + m] = e;
-#else
                 h[(i + m) * n + j] = e;
                 h[(i + m) * n + j + m] = -e;
-#endif
             }
-#if ORACLE_MUTANT == 20
-    /* planted mistake: the normalisation dropped */
-    const double norm = 1.0;
-#else
     const double norm = 1.0 / sqrt((double)n);
-#endif
 #pragma omp parallel for num_threads(nthreads) schedule(static)
     for (long i = 0; i < M; ++i)
         for (long c = 0; c < n; ++c) {
             double s = 0.0;
             for (long t = 0; t < n; ++t)
-#if ORACLE_MUTANT == 22
-                /* planted mistake: alpha applied to the input features */
-                s += y[i * n + t] * (alpha ? alpha[t] : 1.0) * h[t * n + c];
-#else
                 s += y[i * n + t] * h[t * n + c];
-#endif
             s *= norm;
-#if ORACLE_MUTANT == 23
-            /* planted mistake: beta added before the scaling by alpha */
-            if (beta)
-                s += beta[c];
-#endif
-#if ORACLE_MUTANT != 22
             if (alpha)
                 s *= alpha[c];
-#endif
-#if ORACLE_MUTANT != 23
             if (beta)
                 s += beta[c];
-#endif
             out[i * n + c] = s;
         }
     free(h);
@@ -840,31 +722,13 @@ int parallax_oracle_based(const double *q, const double *k, const double *v, dou
         for (long e = 0; e < dv; ++e)
             oi[e] = 0.0;
         double den = 0.0;
-#if ORACLE_MUTANT == 25
-        /* planted mistake: the query's own key left out */
-        for (long j = 0; j < i; ++j) {
-#else
         for (long j = 0; j <= i; ++j) {
-#endif
             double dot = 0.0;
             for (long t = 0; t < dk; ++t)
                 dot += qi[t] * kb[j * dk + t];
             const double x = scale * dot;
-#if ORACLE_MUTANT == 24
-            /* planted mistake: the second-order term dropped */
-            const double w = 1.0 + x;
-#elif ORACLE_MUTANT == 27
-            /* planted mistake: the square taken of the unscaled product */
-            const double w = 1.0 + x + 0.5 * dot * dot;
-#else
             const double w = 1.0 + x + 0.5 * x * x;
-#endif
-#if ORACLE_MUTANT == 26
-            /* planted mistake: normalised by the number of keys */
-            den += 1.0;
-#else
             den += w;
-#endif
             for (long e = 0; e < dv; ++e)
                 oi[e] += w * vb[j * dv + e];
         }

@@ -12,7 +12,9 @@ valid in it.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import math
 import os
 
@@ -120,6 +122,29 @@ def _stream_handle(device: torch.device, stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on(device: torch.device, stream):
+    """Context for the binding's own allocations (outputs, workspaces, fills):
+    the stream the kernels are launched on.  The caching allocator then
+    orders the reuse of a buffer freed here (an internal workspace) after
+    those kernels; allocated on another stream it could be handed to new
+    work there while the kernels still read it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    return torch.cuda.stream(stream)
+
+
+def _stream_ordered(fn):
+    """Runs a binding with its allocations on the launch stream (see _on)."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        dev = args[0].device if args and isinstance(args[0], torch.Tensor) else None
+        with _on(dev, stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
+
+
 def _need(t: torch.Tensor, name: str, dtype, ndim: int):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -136,6 +161,7 @@ def parallax_attn_fwd_workspace_size(B: int, H: int, L: int, d: int) -> int:
     return int(load_library().parallax_attn_fwd_workspace_size(int(B), int(H), int(L), int(d)))
 
 
+@_stream_ordered
 def parallax_attn_fwd(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
                       out=None, lse=None, workspace=None, stream=None):
     """Causal Parallax prefill. q, k, v, r: bf16 [B,H,L,d] -> (o fp32 [B,H,L,d], lse fp32 [B,H,L]).
@@ -185,6 +211,7 @@ def _workspace(workspace, nbytes: int, device):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+@_stream_ordered
 def parallax_attn_fwd_train(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
                             workspace=None, stream=None):
     """Prefill forward that also saves what the backward needs.
@@ -220,6 +247,7 @@ def parallax_attn_bwd_workspace_size(B: int, H: int, L: int, d: int) -> int:
     return int(load_library().parallax_attn_bwd_workspace_size(int(B), int(H), int(L), int(d)))
 
 
+@_stream_ordered
 def parallax_attn_bwd(q, k, v, r, dout, o, lse, sbar, pv, *, softmax_scale=None, window=0,
                       n_sink=0, grads=None, workspace=None, stream=None):
     """Prefill backward.  q, k, v, r, dout: bf16 [B,H,L,d]; o, lse, sbar, pv from
@@ -258,6 +286,7 @@ def parallax_attn_bwd(q, k, v, r, dout, o, lse, sbar, pv, *, softmax_scale=None,
     return dq, dk, dv, dr
 
 
+@_stream_ordered
 def parallax_attn_decode(q, r, k_cache, v_cache, seqlens=None, *, softmax_scale=None,
                          num_splits=16, out=None, lse=None, stream=None):
     """Decode step. q, r: bf16 [B,H,d]; caches bf16 [B,H,Lmax,d]; seqlens int32 [B] or None.
@@ -299,6 +328,7 @@ def parallax_attn_decode(q, r, k_cache, v_cache, seqlens=None, *, softmax_scale=
     return out, lse
 
 
+@_stream_ordered
 def parallax_attn_decode_paged(q, r, k_cache, v_cache, block_table=None, seqlens=None, *,
                                softmax_scale=None, window=0, n_sink=0, num_splits=16,
                                out=None, lse=None, stream=None):
@@ -341,6 +371,12 @@ def parallax_attn_decode_paged(q, r, k_cache, v_cache, block_table=None, seqlens
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if not (out.is_contiguous() and lse.is_contiguous()):
+        raise ValueError("out and lse must be contiguous")
+    if tuple(out.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out / lse have the wrong shape")
     ks = parallax_strides(k_cache.stride(0), k_cache.stride(2), k_cache.stride(1))
     vs = parallax_strides(v_cache.stride(0), v_cache.stride(2), v_cache.stride(1))
     st = load_library().parallax_attn_decode_paged(
@@ -353,6 +389,7 @@ def parallax_attn_decode_paged(q, r, k_cache, v_cache, block_table=None, seqlens
     return out, lse
 
 
+@_stream_ordered
 def parallax_qkvr_project(x, w, *, out=None, stream=None):
     """Fused projections Y = X W^T.  x: bf16 [M, K]; w: bf16 [N, K] (the stacked
     W_Q, W_K, W_V, W_R rows).  Returns bf16 [M, N] (row i = [q_i | k_i | v_i | rho_i])."""
@@ -376,6 +413,7 @@ def parallax_qkvr_project(x, w, *, out=None, stream=None):
     return out
 
 
+@_stream_ordered
 def parallax_hadamard_out(o, alpha=None, beta=None, *, out=None, stream=None):
     """Walsh-Hadamard output projection y = alpha * (O H_n / sqrt(n)) + beta.
 
@@ -425,6 +463,7 @@ def based_state_shape(dv: int):
     return (BASED_FEATURES, 16 * (dv // 16 + 1))
 
 
+@_stream_ordered
 def parallax_based_fwd(q, k, v, *, scale=None, return_state=False, out=None, workspace=None,
                        stream=None):
     """Causal Based linear attention (Taylor kernel 1 + x + x^2/2, x = scale q.k).
@@ -461,6 +500,7 @@ def parallax_based_fwd(q, k, v, *, scale=None, return_state=False, out=None, wor
     return (out, state) if return_state else out
 
 
+@_stream_ordered
 def parallax_based_decode(q, k, v, state, *, scale=None, out=None, stream=None):
     """One Based decode step: q, k bf16 [B, H, 16], v bf16 [B, H, dv]; ``state``
     fp32 [B, H, 160, 16 (dv/16 + 1)] is updated in place.  Returns o fp32 [B, H, dv]."""

@@ -257,7 +257,8 @@ parallax_status parallax_attn_decode(const void *q, const void *r, const void *k
         return PARALLAX_ERR_INVALID_ARG;
     if (!bf16_strides_ok(sk) || !bf16_strides_ok(sv))
         return PARALLAX_ERR_INVALID_ARG;
-    if ((int64_t)B * H > INT_MAX)
+    // The kernel forms per-lane row offsets in 32 bits (a few rows apart).
+    if (!row_stride_ok(sk) || !row_stride_ok(sv) || (int64_t)B * H > INT_MAX)
         return PARALLAX_ERR_UNSUPPORTED;
 
     plx::DecodeArgs a;

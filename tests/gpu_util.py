@@ -43,14 +43,6 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, what: str, o_tol=O_TOL, lse_tol=LSE_
     return err_o, rel_l2, err_lse
 
 
-def sample_rows(L: int, rng: np.random.Generator, n_random: int = 16):
-    base = [0, 1, 2, 3, 4, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 255, 256,
-            L // 2, L // 2 + 1, L - 129, L - 128, L - 127, L - 65, L - 64, L - 63,
-            L - 33, L - 32, L - 31, L - 2, L - 1]
-    extra = rng.integers(0, L, size=n_random).tolist()
-    return sorted({i for i in base + extra if 0 <= i < L})
-
-
 def oracle_rows(orc, q, k, v, r, b, h, rows, scale, window=0, n_sink=0):
     """Oracle on selected rows of one (b, h) slice of device tensors [B,H,L,d]."""
     rows = np.asarray(rows, dtype=np.int64)

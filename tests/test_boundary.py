@@ -148,6 +148,8 @@ def test_fwd_empty_still_checks_d(lib):
     (dict(seqlens=A16 + 2), INVALID),
     (dict(scale=0.0), INVALID),
     (dict(sk=S(8, 8, 4)), INVALID),
+    (dict(sk=S(1 << 30, 1 << 26, 1 << 24)), UNSUPPORTED),
+    (dict(sv=S(1 << 30, 1 << 26, 1 << 24)), UNSUPPORTED),
 ])
 def test_decode_rejects(lib, kw, status):
     assert dec(lib, **kw) == status

@@ -155,3 +155,22 @@ def test_full_size_paged_gqa(orc, Hkv):
                                         f64(vb)[None])
         compare(f64(o[b:b + 1]), f64(lse[b:b + 1]), o_ref, lse_ref,
                 "full-size paged decode Hkv=%d b=%d n=%d" % (Hkv, b, n))
+
+
+@pytest.mark.parametrize("bad", ["dtype", "shape", "strided"])
+def test_paged_rejects_bad_outputs(bad):
+    """A caller-supplied out / lse is checked before the launch: the kernel
+    writes B*Hq*d and B*Hq fp32 values through their pointers."""
+    B, Hq, Hkv, L, d = 2, 4, 2, 64, 128
+    q, r = (rand((B, Hq, d), 7 + t).to(DEV) for t in range(2))
+    k, v = (rand((B, L, Hkv, d), 9 + t).to(DEV) for t in range(2))
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    if bad == "dtype":
+        out = out.to(torch.bfloat16)
+    elif bad == "shape":
+        lse = torch.empty((B, Hq - 1), dtype=torch.float32, device=DEV)
+    else:
+        out = torch.empty((B, Hq, 2 * d), dtype=torch.float32, device=DEV)[..., :d]
+    with pytest.raises((TypeError, ValueError)):
+        parallax_attn_decode_paged(q, r, k, v, out=out, lse=lse)

@@ -1,14 +1,14 @@
 """CPU tests of the fp64 oracle: every pin passes on the real oracle, and every
-planted mistake (a build with -DORACLE_MUTANT=n) fails at least one pin."""
+planted mistake (a patched copy of the oracle source, tests/oracle_mutants.py)
+fails at least one pin."""
 import os
 
 import numpy as np
 import pytest
 
 import oracle
+from oracle_mutants import MUTANTS, mutant_source
 from oracle_pins import ALL_PINS
-
-N_MUTANTS = 27
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -16,9 +16,11 @@ def test_pin(orc, pin):
     pin(orc)
 
 
-@pytest.mark.parametrize("mutant", range(1, N_MUTANTS + 1))
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, mutant):
-    path = oracle.build(str(tmp_path / ("liboracle_m%d.so" % mutant)), mutant=mutant)
+    src = tmp_path / ("oracle_m%d.c" % mutant)
+    src.write_text(mutant_source(mutant))
+    path = oracle.build(str(tmp_path / ("liboracle_m%d.so" % mutant)), source=str(src))
     bad = oracle.Oracle(path)
     failed = []
     for pin in ALL_PINS:
@@ -27,7 +29,7 @@ def test_planted_mistake_is_caught(tmp_path, mutant):
                 pin(bad)
         except AssertionError:
             failed.append(pin.__name__)
-    assert failed, "planted mistake %d passed every pin" % mutant
+    assert failed, "planted mistake %d (%s) passed every pin" % (mutant, MUTANTS[mutant][0])
 
 
 def test_rows_interface_matches_fwd(orc):
