@@ -69,11 +69,11 @@ KERNEL_SOURCES = {
 # Kernels one prefill call launches, per workload.
 PREFILL_KERNELS = {
     "prefill_1.7b_long": "parallax_attn_fwd call = parallax_vprep_kernel<128> + "
-                         "parallax_fwd_kernel<128, true, false>",
+                         "parallax_fwd_kernel<128, true, false, false>",
     "prefill_0.6b": "parallax_attn_fwd call = parallax_vprep_kernel<64> + "
-                    "parallax_fwd_kernel<64, true, false>",
+                    "parallax_fwd_kernel<64, true, false, false>",
     "local_swa128_sink4": "parallax_attn_fwd call = parallax_vprep_kernel<64> + "
-                          "parallax_fwd_kernel<64, true, false>",
+                          "parallax_fwd_kernel<64, true, false, false>",
 }
 FLUSH_BYTES = 512 << 20     # overwritten between timed calls: more than L2 + the 256 MB MALL
 
@@ -203,25 +203,27 @@ def time_each_call(fn, runs, warmup, stream, flush=None):
     return times
 
 
-def time_prefill_leg(cfg, bound, runs, warmup, stream, flush=None):
+def time_prefill_leg(cfg, bound, runs, warmup, stream, flush=None, precise=False):
     """One prefill workload timed call by call (median and min over `runs`),
     with its roofline: the matrix-core peak for the compute-bound causal
     workloads, HBM for the windowed one (8d FLOP per visible pair; bytes:
-    q, k, v, r read once, the fp32 output and lse written once)."""
-
+    q, k, v, r read once, the fp32 output and lse written once).  With
+    `precise`, the call is parallax_attn_fwd_precise (same FLOP count)."""
     import torch
 
     from parallax_local_linear_amd import (accounting, parallax_attn_fwd,
+                                           parallax_attn_fwd_precise,
                                            parallax_attn_fwd_workspace_size, workloads)
     dev = torch.device("cuda:0")
+    fwd = parallax_attn_fwd_precise if precise else parallax_attn_fwd
     q, k, v, r = workloads.prefill_inputs(cfg, device=dev)
     o = torch.empty(q.shape, dtype=torch.float32, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, parallax_attn_fwd_workspace_size(cfg.B, cfg.H, cfg.L, cfg.d)),
                      dtype=torch.uint8, device=dev)
     times = time_each_call(
-        lambda: parallax_attn_fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o,
-                                  lse=lse, workspace=ws, stream=stream),
+        lambda: fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,
+                    workspace=ws, stream=stream),
         runs, warmup, stream, flush)
     med = statistics.median(times)
     flops = accounting.prefill_flops(cfg)
@@ -235,8 +237,12 @@ def time_prefill_leg(cfg, bound, runs, warmup, stream, flush=None):
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
                 "algorithmic_flop_per_launch": flops}
-    roof["traffic"] = measured_traffic(cfg.name)
-    roof["kernel"] = PREFILL_KERNELS.get(cfg.name)
+    roof["traffic"] = None if precise else measured_traffic(cfg.name)
+    roof["kernel"] = PREFILL_KERNELS[cfg.name]
+    if precise:
+        roof["kernel"] = (roof["kernel"].replace("parallax_attn_fwd call",
+                                                 "parallax_attn_fwd_precise call")
+                          .replace("false, false>", "false, true>"))
     return {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "L": cfg.L, "d": cfg.d,
             "window": cfg.window, "n_sink": cfg.n_sink,
             "ms_median": round(med, 4), "ms_min": round(min(times), 4), "runs": runs,
@@ -593,8 +599,7 @@ def main():
             "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4),
             "traffic": measured_traffic("prefill"),
             "algorithmic_flop_per_launch": p_flops,
-            "kernel": "parallax_attn_fwd call = parallax_vprep_kernel<128> + "
-                      "parallax_fwd_kernel<128, true, false>",
+            "kernel": PREFILL_KERNELS[pcfg.name],
         },
         "decode": {
             "value": round(d_gbs, 1),
@@ -634,6 +639,8 @@ def main():
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     res["prefill_0.6b"] = time_prefill_leg(workloads.PREFILL_06B, "mfma", 20, 5, stream, flush)
     res["local_swa128_sink4"] = time_prefill_leg(workloads.LOCAL, "hbm", 20, 5, stream, flush)
+    print("[bench] timing the precise prefill", file=sys.stderr, flush=True)
+    res["precise"] = time_prefill_leg(pcfg, "mfma", 20, 3, stream, precise=True)
     del flush
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -39,11 +39,32 @@
  *     PARALLAX_ERR_LAUNCH reports a failed kernel launch.
  *   - Outputs must not alias inputs.  Non-finite inputs give undefined
  *     results.
- *   - Numerical range: the kernels feed the un-normalised softmax weights
- *     (at most 2^5 each), their products with rho_i . k_j and the values
- *     to float16 matrix-core operands, so |rho_i . k_j| must stay below
- *     2047 and |v| at or below 65504 (float16's largest finite value);
- *     beyond that results become infinite or NaN.
+ *   - Accuracy of the prefill.  Its value products take the values and two
+ *     weights per key as float16 matrix-core operands: the un-normalised
+ *     softmax weight p~ (at most 2^5) and p~ * rho_i.k_j, each rounded once
+ *     (relative error up to 2^-11).  A perturbation of the softmax weights
+ *     moves the probe correction in proportion to the probe scores, so the
+ *     O error of row i grows with R_i = max over j in V(i) of
+ *     |rho_i . k_j|.  Against the exact result on the same bf16 inputs,
+ *     parallax_attn_fwd and parallax_attn_fwd_train stay within
+ *         2e-2 * max(1, R_i / 24)
+ *     for values of unit scale (the bound scales with |v|); this is tested
+ *     at R = 24, 256 and 2000 with diffuse and with concentrated attention,
+ *     d = 64 and 128, causal and windowed with sinks.  The five reference
+ *     workloads (i.i.d. N(0,1) inputs, R up to about 70) stay within 2e-2.
+ *     parallax_attn_fwd_precise passes each weight as the sum of two
+ *     float16 values (its rounding and the rounded residual, about 22
+ *     significant bits), which doubles the matrix-core work of the value
+ *     products (the kernel's grows 1.5 times), and stays within
+ *         2e-2 * max(1, R_i / 256)
+ *     (tested at R = 256 and 2000, same cases).  What limits it is the fp32
+ *     rounding of the scores q.k themselves: where a row's weight is split
+ *     between keys whose probe scores differ by about R_i, one rounding
+ *     step of a score moves o_i by about R_i |v| times that step.
+ *   - Range.  float16 holds at most 65504, so |v| must stay at or below it
+ *     and, in the prefill, |rho_i . k_j| below 2047 (2^5 * 2047 < 65504);
+ *     beyond that the f16 weights overflow and the affected rows' outputs
+ *     are infinite or NaN (not finite and wrong).
  */
 #ifndef PARALLAX_H
 #define PARALLAX_H
@@ -116,6 +137,22 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
                                   float softmax_scale, int window, int n_sink,
                                   void *workspace, size_t workspace_bytes,
                                   void *stream);
+
+/*
+ * Causal prefill forward with two-part float16 weights: the same operation,
+ * arguments, workspace and errors as parallax_attn_fwd, accurate to 2e-2
+ * absolute for probe scores |rho_i . k_j| up to 256, eight times the range
+ * of parallax_attn_fwd (see "Accuracy of the prefill" above).  Each key's weights p~ and p~ * rho_i.k_j reach the
+ * matrix cores as an f16 value plus its f16 residual, which doubles the
+ * value and row-sum products (the score products are unchanged).
+ */
+parallax_status parallax_attn_fwd_precise(const void *q, const void *k, const void *v,
+                                          const void *r, float *o, float *lse, int B, int H,
+                                          int L, int d, parallax_strides sq, parallax_strides sk,
+                                          parallax_strides sv, parallax_strides sr,
+                                          parallax_strides so, float softmax_scale, int window,
+                                          int n_sink, void *workspace, size_t workspace_bytes,
+                                          void *stream);
 
 /*
  * Prefill forward for training: parallax_attn_fwd plus two saved
@@ -265,9 +302,11 @@ parallax_status parallax_attn_decode(const void *q, const void *r,
  *                query heads of a kv head (up to 16 per workgroup) are the
  *                columns of matrix-core tiles and every row is read once
  *                per workgroup; the keys are split min(num_splits, 8) ways.
- *                That path feeds the weights and values to the matrix cores
- *                as float16, like the prefill (|v| <= 65504, |rho.k| <
- *                65504); the other path computes in fp32.
+ *                That path feeds the values to the matrix cores as float16
+ *                (|v| <= 65504) and each weight as an f16 value plus its
+ *                f16 residual, like parallax_attn_fwd_precise, with the
+ *                same accuracy (the online softmax keeps p~ <= 1, so
+ *                |rho.k| < 65504); the other path computes in fp32.
  */
 parallax_status parallax_attn_decode_paged(const void *q, const void *r,
                                            const void *k_cache, const void *v_cache,

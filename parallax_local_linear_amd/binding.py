@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
                 2: "PARALLAX_ERR_UNSUPPORTED", 3: "PARALLAX_ERR_LAUNCH"}
 
 # Every symbol include/parallax.h declares.
-EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_train",
+EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_precise",
+            "parallax_attn_fwd_train",
             "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
             "parallax_attn_decode_paged", "parallax_qkvr_project", "parallax_hadamard_out",
             "parallax_based_state_floats", "parallax_based_workspace_size", "parallax_based_fwd",
@@ -65,6 +66,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.parallax_attn_fwd.restype = ctypes.c_int
     lib.parallax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, S, S, S, S, S,
                                       f, i, i, vp, ctypes.c_size_t, vp]
+    lib.parallax_attn_fwd_precise.restype = ctypes.c_int
+    lib.parallax_attn_fwd_precise.argtypes = lib.parallax_attn_fwd.argtypes
     lib.parallax_attn_fwd_train.restype = ctypes.c_int
     lib.parallax_attn_fwd_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
                                             S, S, S, S, S, f, i, i, vp, ctypes.c_size_t, vp]
@@ -170,6 +173,19 @@ def parallax_attn_fwd(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
     ``parallax_attn_fwd_workspace_size(B, H, L, d)`` bytes) is allocated with
     torch when not given.
     """
+    return _fwd("parallax_attn_fwd", q, k, v, r, softmax_scale, window, n_sink, out, lse,
+                workspace, stream)
+
+
+@_stream_ordered
+def parallax_attn_fwd_precise(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
+                              out=None, lse=None, workspace=None, stream=None):
+    """parallax_attn_fwd with two-part float16 weights (accurate for large probe scores)."""
+    return _fwd("parallax_attn_fwd_precise", q, k, v, r, softmax_scale, window, n_sink, out, lse,
+                workspace, stream)
+
+
+def _fwd(entry, q, k, v, r, softmax_scale, window, n_sink, out, lse, workspace, stream):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (r, "r")):
         _need(t, n, torch.bfloat16, 4)
         if t.shape != q.shape:
@@ -194,7 +210,7 @@ def parallax_attn_fwd(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0,
     if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
         raise TypeError("workspace must be a device tensor")
     have = workspace.numel() * workspace.element_size()
-    st = lib.parallax_attn_fwd(
+    st = getattr(lib, entry)(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, H, L, d, _strides(q), _strides(k), _strides(v), _strides(r), _strides(out),
         float(softmax_scale), int(window), int(n_sink), workspace.data_ptr(), have,

@@ -161,7 +161,7 @@ inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
 constexpr int fwd_waves(int) { return 8; }
 constexpr int fwd_block_rows(int d) { return 16 * fwd_waves(d); }
 
-hipError_t launch_fwd(const FwdArgs &a, int d, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs &a, int d, bool precise, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_proj(const ProjArgs &a, hipStream_t stream);
 hipError_t launch_hadamard(const HadArgs &a, int log2n, hipStream_t stream);

@@ -61,7 +61,7 @@ parallax_status fwd_common(const void *q, const void *k, const void *v, const vo
                            parallax_strides sq, parallax_strides sk, parallax_strides sv,
                            parallax_strides sr, parallax_strides so, float softmax_scale,
                            int window, int n_sink, void *workspace, size_t workspace_bytes,
-                           void *stream, bool train) {
+                           void *stream, bool train, bool precise) {
     if (B < 0 || H < 0 || L < 0)
         return PARALLAX_ERR_INVALID_ARG;
     if (d != 64 && d != 128)
@@ -112,7 +112,7 @@ parallax_status fwd_common(const void *q, const void *k, const void *v, const vo
     a.scale_log2 = softmax_scale * kLog2e;
     a.window = window;
     a.n_sink = n_sink;
-    hipError_t e = plx::launch_fwd(a, d, static_cast<hipStream_t>(stream));
+    hipError_t e = plx::launch_fwd(a, d, precise, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
 }
 
@@ -127,7 +127,20 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
                                   int window, int n_sink, void *workspace,
                                   size_t workspace_bytes, void *stream) {
     return fwd_common(q, k, v, r, o, lse, nullptr, nullptr, B, H, L, d, sq, sk, sv, sr, so,
-                      softmax_scale, window, n_sink, workspace, workspace_bytes, stream, false);
+                      softmax_scale, window, n_sink, workspace, workspace_bytes, stream, false,
+                      false);
+}
+
+parallax_status parallax_attn_fwd_precise(const void *q, const void *k, const void *v,
+                                          const void *r, float *o, float *lse, int B, int H,
+                                          int L, int d, parallax_strides sq, parallax_strides sk,
+                                          parallax_strides sv, parallax_strides sr,
+                                          parallax_strides so, float softmax_scale, int window,
+                                          int n_sink, void *workspace, size_t workspace_bytes,
+                                          void *stream) {
+    return fwd_common(q, k, v, r, o, lse, nullptr, nullptr, B, H, L, d, sq, sk, sv, sr, so,
+                      softmax_scale, window, n_sink, workspace, workspace_bytes, stream, false,
+                      true);
 }
 
 parallax_status parallax_attn_fwd_train(const void *q, const void *k, const void *v,
@@ -139,7 +152,8 @@ parallax_status parallax_attn_fwd_train(const void *q, const void *k, const void
                                         int n_sink, void *workspace, size_t workspace_bytes,
                                         void *stream) {
     return fwd_common(q, k, v, r, o, lse, sbar, pv, B, H, L, d, sq, sk, sv, sr, so,
-                      softmax_scale, window, n_sink, workspace, workspace_bytes, stream, true);
+                      softmax_scale, window, n_sink, workspace, workspace_bytes, stream, true,
+                      false);
 }
 
 size_t parallax_attn_bwd_workspace_size(int B, int H, int L, int d) {

@@ -486,9 +486,10 @@ __global__ __launch_bounds__(64 * NS * GW) void parallax_decode_paged_kernel(Pag
 //     as 8 keys x 8 features per lane, transposed in registers into its own
 //     LDS stage as the V^T fragments of the value MFMAs;
 //   * S^T = K Q^T and K R^T (bf16, columns past the group's heads are zero),
-//     an online softmax per column, f16 weights p~ and p~ s, then O^T +=
-//     V^T P~^T and V^T (P~ o S)^T, with the sums of p~ and p~ s from an
-//     all-ones operand (f16 MFMAs, fp32 sums), as in the prefill;
+//     an online softmax per column, weights p~ and p~ s each as an f16 value
+//     plus its f16 residual, then O^T += V^T P~^T and V^T (P~ o S)^T, with
+//     the sums of p~ and p~ s from an all-ones operand (f16 MFMAs, fp32
+//     sums), as in the prefill's precise mode;
 //   * the NS partial states of each head merge in LDS (the stage memory,
 //     reused after one barrier).
 // Each wavefront's stage count differs, so the loop synchronises within the
@@ -668,14 +669,21 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_gqa_kernel(PagedDecod
             accL[e] *= alpha;
             accS[e] *= alpha;
         }
-        f16x8 wp, ws;
+        // Each weight reaches the matrix core as two f16 parts, the rounded
+        // value and its rounded residual (about 22 significant bits): the
+        // loop is bound by the cache reads, so the extra products are free,
+        // and the output keeps its accuracy for large probe scores.
+        f16x8 wp, ws, wpl, wsl;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float p = exp2_fast(x[4 * kt + e] - msub);
+                const float w = p * sr[kt][e];
                 wp[4 * kt + e] = (_Float16)p;
-                ws[4 * kt + e] = (_Float16)(p * sr[kt][e]);
+                ws[4 * kt + e] = (_Float16)w;
+                wpl[4 * kt + e] = (_Float16)(p - (float)wp[4 * kt + e]);
+                wsl[4 * kt + e] = (_Float16)(w - (float)ws[4 * kt + e]);
             }
         // The stage's V^T writes are visible to the whole wavefront.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -688,10 +696,14 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_gqa_kernel(PagedDecod
                                                    vt + gqa_slot(16 * dt + l16, G) * 8));
         accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, wp, accL, 0, 0, 0);
         accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, ws, accS, 0, 0, 0);
+        accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, wpl, accL, 0, 0, 0);
+        accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, wsl, accS, 0, 0, 0);
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt) {
             accA[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], wp, accA[dt], 0, 0, 0);
             accC[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], ws, accC[dt], 0, 0, 0);
+            accA[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], wpl, accA[dt], 0, 0, 0);
+            accC[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], wsl, accC[dt], 0, 0, 0);
         }
         // The next stage rewrites the V^T stage: its reads are done first.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -218,8 +218,16 @@ struct Scores {
 };
 
 // f16 weights of one stage in the value MFMA's B-operand order: p~ and p~ s.
+// PRECISE adds their rounding residuals, p~ - f16(p~) and p~ s - f16(p~ s),
+// rounded to f16 again: each weight then reaches the matrix core as the sum
+// of two f16 values (about 22 significant bits instead of 11).
+template <bool PRECISE>
 struct Weights {
     f16x8 p, w;
+};
+template <>
+struct Weights<true> {
+    f16x8 p, w, plo, wlo;
 };
 
 // LDS stage buffer: K [32 keys][d] and V^T [d][32 positions], both in the
@@ -296,17 +304,29 @@ __device__ __forceinline__ void score_mfmas(const Ctx<D> &cx, const KFrags<D> &k
 }
 
 // O^T += V^T P~^T and V^T (P~ o S)^T for one stage, and the row sums
-// ell += sum p~ and S += sum p~ s of the same f16 values.
-template <int D>
-__device__ __forceinline__ void value_mfmas(Ctx<D> &cx, const VFrags<D> &vf, const Weights &pw) {
+// ell += sum p~ and S += sum p~ s of the same f16 values (with PRECISE, the
+// residual parts go into the same accumulators).
+template <int D, bool PRECISE>
+__device__ __forceinline__ void value_mfmas(Ctx<D> &cx, const VFrags<D> &vf,
+                                            const Weights<PRECISE> &pw) {
     const _Float16 one = (_Float16)1.0f;
     const f16x8 ones = {one, one, one, one, one, one, one, one};
     cx.accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw.p, cx.accL, 0, 0, 0);
     cx.accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw.w, cx.accS, 0, 0, 0);
+    if constexpr (PRECISE) {
+        cx.accL = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw.plo, cx.accL, 0, 0, 0);
+        cx.accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw.wlo, cx.accS, 0, 0, 0);
+    }
 #pragma unroll
     for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
         cx.accA[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], pw.p, cx.accA[dt], 0, 0, 0);
         cx.accC[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], pw.w, cx.accC[dt], 0, 0, 0);
+        if constexpr (PRECISE) {
+            cx.accA[dt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], pw.plo, cx.accA[dt], 0, 0, 0);
+            cx.accC[dt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f[dt], pw.wlo, cx.accC[dt], 0, 0, 0);
+        }
     }
 }
 
@@ -342,9 +362,10 @@ __device__ __forceinline__ bool init_offsets(Ctx<D> &cx, const Scores &s, float 
 
 // Weights of one stage: the per-lane running max of the raw scores, and the
 // f16 weights p~ and p~ s in the value MFMA's B-operand order (p~ s is
-// rounded once, from the f32 product).
-template <int D>
-__device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights &pw, float c) {
+// rounded once, from the f32 product; with PRECISE, also the f16 residuals).
+template <int D, bool PRECISE>
+__device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights<PRECISE> &pw,
+                                        float c) {
     cx.xlane = fmaxf(fmaxf(fmaxf(cx.xlane, s.q[0][0]), s.q[0][1]),
                      fmaxf(fmaxf(s.q[0][2], s.q[0][3]), s.q[1][0]));
     cx.xlane = fmaxf(fmaxf(fmaxf(cx.xlane, s.q[1][1]), s.q[1][2]), s.q[1][3]);
@@ -356,11 +377,27 @@ __device__ __forceinline__ void weights(Ctx<D> &cx, const Scores &s, Weights &pw
             const float p0 = exp2_fast(fmaf(s.q[kt][e], c, -cx.msub));
             const float p1 = exp2_fast(fmaf(s.q[kt][e + 1], c, -cx.msub));
             const f16x2 ph = cvt_f16x2(p0, p1);
-            const f16x2 wh = cvt_f16x2(p0 * s.r[kt][e], p1 * s.r[kt][e + 1]);
             pw.p[4 * kt + e] = ph[0];
             pw.p[4 * kt + e + 1] = ph[1];
-            pw.w[4 * kt + e] = wh[0];
-            pw.w[4 * kt + e + 1] = wh[1];
+            if constexpr (PRECISE) {
+                // The residuals are exact in f32 (the f16 values carry 11 of
+                // the 24 significant bits), then rounded to f16.
+                const float w0 = p0 * s.r[kt][e];
+                const float w1 = p1 * s.r[kt][e + 1];
+                const f16x2 wh = cvt_f16x2(w0, w1);
+                const f16x2 pl = cvt_f16x2(p0 - (float)ph[0], p1 - (float)ph[1]);
+                const f16x2 wl = cvt_f16x2(w0 - (float)wh[0], w1 - (float)wh[1]);
+                pw.w[4 * kt + e] = wh[0];
+                pw.w[4 * kt + e + 1] = wh[1];
+                pw.plo[4 * kt + e] = pl[0];
+                pw.plo[4 * kt + e + 1] = pl[1];
+                pw.wlo[4 * kt + e] = wl[0];
+                pw.wlo[4 * kt + e + 1] = wl[1];
+            } else {
+                const f16x2 wh = cvt_f16x2(p0 * s.r[kt][e], p1 * s.r[kt][e + 1]);
+                pw.w[4 * kt + e] = wh[0];
+                pw.w[4 * kt + e + 1] = wh[1];
+            }
         }
     }
 }
@@ -432,8 +469,9 @@ __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
 // WHOLE: the K slice and the V^T images of one (batch, head) each span
 // fewer than 2^31 bytes, so one buffer resource per tensor covers every
 // stage and a stage needs only an offset; otherwise every stage builds its
-// own resources.
-template <int D, bool WHOLE, bool STATS>
+// own resources.  STATS: also store sbar and pv for the backward.
+// PRECISE: weights as two f16 parts each (see Weights).
+template <int D, bool WHOLE, bool STATS, bool PRECISE>
 __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     using C = Cfg<D>;
     // One LDS variable per stage buffer, each indexed only by compile-time
@@ -597,7 +635,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     KFrags<D> kf;
     VFrags<D> vf;
     Scores sc;
-    Weights pw;
+    Weights<PRECISE> pw;
 
     // End of the M phase, when the score MFMAs are done.  Masked stages: the
     // mask of stage t's scores and the softmax offsets of rows that still
@@ -636,11 +674,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         score_mfmas<D>(cx, kf, sc);
         __builtin_amdgcn_sched_barrier(0);
         if (values)
-            value_mfmas<D>(cx, vf, pw);
+            value_mfmas<D, PRECISE>(cx, vf, pw);
         read_kfrags<D>(kf, sbuf(b0 + 1).k, fa);
 #pragma unroll
         for (int i = 0; i < 2 * C::KC; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, C::DT / C::KC, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, (PRECISE ? 2 : 1) * C::DT / C::KC, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         finish_scores(masked, t);
@@ -653,9 +691,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     auto vphase = [&](auto b0, int t) __attribute__((always_inline)) {
         read_vfrags<D>(vf, sbuf(b0).v, fa);
         __builtin_amdgcn_sched_barrier(0);
-        weights<D>(cx, sc, pw, c);
+        weights<D, PRECISE>(cx, sc, pw, c);
         pin(pw.p);
         pin(pw.w);
+        if constexpr (PRECISE) {
+            pin(pw.plo);
+            pin(pw.wlo);
+        }
         copy(t + AHEAD, b0 + AHEAD);
         wait_copies<IN_FLIGHT * C::COPIES>();
     };
@@ -766,7 +808,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             step(kMasked, t, t);
         // Value MFMAs of the last stage; the first group catches up with the
         // second group's extra barrier.
-        value_mfmas<D>(cx, vf, pw);
+        value_mfmas<D, PRECISE>(cx, vf, pw);
         if (grp == 0)
             phase_barrier();
 
@@ -822,7 +864,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
 int64_t slice_bytes(int64_t L, int64_t ld, int d) { return (L - 1) * ld * 2 + (int64_t)d * 2; }
 
 template <int D>
-hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
+hipError_t launch_fwd_t(const FwdArgs &a, bool precise, hipStream_t stream) {
     FwdArgs args = a;
     void *params[] = {&args};
     constexpr int SPB = 256 / (4 * (D / 8));  // stages per prepass block
@@ -837,18 +879,21 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
                        (int64_t)a.n_st * D * BN * 2 <= INT32_MAX;
     const void *fn;
     if (a.pv)
-        fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true, true>)
-                   : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false, true>);
+        fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true, true, false>)
+                   : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false, true, false>);
+    else if (precise)
+        fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true, false, true>)
+                   : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false, false, true>);
     else
-        fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true, false>)
-                   : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false, false>);
+        fn = whole ? reinterpret_cast<const void *>(&parallax_fwd_kernel<D, true, false, false>)
+                   : reinterpret_cast<const void *>(&parallax_fwd_kernel<D, false, false, false>);
     return hipLaunchKernel(fn, grid, block, params, 0, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs &a, int d, hipStream_t stream) {
-    return d == 64 ? launch_fwd_t<64>(a, stream) : launch_fwd_t<128>(a, stream);
+hipError_t launch_fwd(const FwdArgs &a, int d, bool precise, hipStream_t stream) {
+    return d == 64 ? launch_fwd_t<64>(a, precise, stream) : launch_fwd_t<128>(a, precise, stream);
 }
 
 }  // namespace plx

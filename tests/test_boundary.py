@@ -51,11 +51,11 @@ def test_status_strings(lib):
 
 def fwd(lib, q=A16, k=A16, v=A16, r=A16, o=A16, lse=A16, B=1, H=2, L=64, d=64,
         sq=CONTIG, sk=CONTIG, sv=CONTIG, sr=CONTIG, so=CONTIG, scale=0.125, window=0,
-        n_sink=0, ws=A16, ws_bytes=None):
+        n_sink=0, ws=A16, ws_bytes=None, entry="parallax_attn_fwd"):
     if ws_bytes is None:
         ws_bytes = 1 << 40
-    return lib.parallax_attn_fwd(q, k, v, r, o, lse, B, H, L, d, sq, sk, sv, sr, so, scale,
-                                 window, n_sink, ws, ws_bytes, None)
+    return getattr(lib, entry)(q, k, v, r, o, lse, B, H, L, d, sq, sk, sv, sr, so, scale,
+                               window, n_sink, ws, ws_bytes, None)
 
 
 def expected_workspace(B, H, L, d):
@@ -80,6 +80,7 @@ def test_workspace_size_of_empty_or_invalid_is_zero(lib, B, H, L, d):
                                 dict(ws_bytes=0)])
 def test_fwd_rejects_bad_workspace(lib, kw):
     assert fwd(lib, **kw) == INVALID
+    assert fwd(lib, entry="parallax_attn_fwd_precise", **kw) == INVALID
 
 
 def dec(lib, q=A16, r=A16, k=A16, v=A16, seqlens=None, o=A16, lse=A16, B=2, H=2, Lmax=64,
@@ -118,6 +119,7 @@ def dec(lib, q=A16, r=A16, k=A16, v=A16, seqlens=None, o=A16, lse=A16, B=2, H=2,
 ])
 def test_fwd_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
+    assert fwd(lib, entry="parallax_attn_fwd_precise", **kw) == status
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(L=0),
@@ -125,6 +127,7 @@ def test_fwd_rejects(lib, kw, status):
                                 dict(L=0, ws=None, ws_bytes=0)])
 def test_fwd_empty_problem_is_a_no_op(lib, kw):
     assert fwd(lib, **kw) == OK
+    assert fwd(lib, entry="parallax_attn_fwd_precise", **kw) == OK
 
 
 def test_fwd_empty_still_checks_d(lib):
