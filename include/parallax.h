@@ -139,6 +139,31 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
                                   void *stream);
 
 /*
+ * Causal prefill forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): parallax_attn_fwd without the workspace arguments.  The
+ * library keeps the workspace itself, in one device array of 64 MiB
+ * (67108864 bytes) per GPU that holds it until the process ends; this call
+ * allocates and frees nothing.  The array of the current device is used,
+ * so `stream` must belong to that device.
+ *
+ *   Sizes whose workspace (parallax_attn_fwd_workspace_size) exceeds 64 MiB
+ *   -- e.g. more than 2 x 16 heads x 8192 tokens at d = 128 -- return
+ *   PARALLAX_ERR_UNSUPPORTED.  Every call on a GPU shares that GPU's array
+ *   and overwrites it in full before reading it (no contents carry over
+ *   between calls), so two calls whose work overlaps on one GPU (other
+ *   streams, other host threads) race and give wrong results: order them.
+ *   Other arguments, outputs and errors as for parallax_attn_fwd;
+ *   PARALLAX_ERR_LAUNCH also reports a failed lookup of the array.
+ */
+parallax_status parallax_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                                          const void *r, float *o, float *lse, int B, int H,
+                                          int L, int d, parallax_strides sq, parallax_strides sk,
+                                          parallax_strides sv, parallax_strides sr,
+                                          parallax_strides so, float softmax_scale, int window,
+                                          int n_sink, void *stream);
+
+/*
  * Causal prefill forward with two-part float16 weights: the same operation,
  * arguments, workspace and errors as parallax_attn_fwd, accurate to 2e-2
  * absolute for probe scores |rho_i . k_j| up to 256, eight times the range

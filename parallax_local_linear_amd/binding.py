@@ -28,6 +28,7 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
 
 # Every symbol include/parallax.h declares.
 EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_precise",
+            "parallax_attn_fwd_noalloc",
             "parallax_attn_fwd_train",
             "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
             "parallax_attn_decode_paged", "parallax_qkvr_project", "parallax_hadamard_out",
@@ -68,6 +69,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                       f, i, i, vp, ctypes.c_size_t, vp]
     lib.parallax_attn_fwd_precise.restype = ctypes.c_int
     lib.parallax_attn_fwd_precise.argtypes = lib.parallax_attn_fwd.argtypes
+    lib.parallax_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.parallax_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, S, S, S, S, S,
+                                              f, i, i, vp]
     lib.parallax_attn_fwd_train.restype = ctypes.c_int
     lib.parallax_attn_fwd_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
                                             S, S, S, S, S, f, i, i, vp, ctypes.c_size_t, vp]
@@ -185,6 +189,17 @@ def parallax_attn_fwd_precise(q, k, v, r, *, softmax_scale=None, window=0, n_sin
                 workspace, stream)
 
 
+@_stream_ordered
+def parallax_attn_fwd_noalloc(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0, out, lse,
+                              stream=None):
+    """parallax_attn_fwd with the library's own 64 MiB device workspace per GPU:
+    the C call allocates nothing, so ``out`` (fp32 [B,H,L,d]) and ``lse`` (fp32
+    [B,H,L], contiguous) must be given.  Calls whose work overlaps on one GPU
+    race for that workspace."""
+    return _fwd("parallax_attn_fwd_noalloc", q, k, v, r, softmax_scale, window, n_sink, out, lse,
+                None, stream)
+
+
 def _fwd(entry, q, k, v, r, softmax_scale, window, n_sink, out, lse, workspace, stream):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (r, "r")):
         _need(t, n, torch.bfloat16, 4)
@@ -204,17 +219,17 @@ def _fwd(entry, q, k, v, r, softmax_scale, window, n_sink, out, lse, workspace, 
     if not lse.is_contiguous():
         raise ValueError("lse must be contiguous")
     lib = load_library()
-    ws_bytes = parallax_attn_fwd_workspace_size(B, H, L, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
-        raise TypeError("workspace must be a device tensor")
-    have = workspace.numel() * workspace.element_size()
-    st = getattr(lib, entry)(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), out.data_ptr(), lse.data_ptr(),
-        B, H, L, d, _strides(q), _strides(k), _strides(v), _strides(r), _strides(out),
-        float(softmax_scale), int(window), int(n_sink), workspace.data_ptr(), have,
-        _stream_handle(q.device, stream))
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), B, H, L, d, _strides(q), _strides(k), _strides(v), _strides(r),
+            _strides(out), float(softmax_scale), int(window), int(n_sink)]
+    if entry != "parallax_attn_fwd_noalloc":
+        ws_bytes = parallax_attn_fwd_workspace_size(B, H, L, d)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+            raise TypeError("workspace must be a device tensor")
+        args += [workspace.data_ptr(), workspace.numel() * workspace.element_size()]
+    st = getattr(lib, entry)(*args, _stream_handle(q.device, stream))
     _check(st)
     return out, lse
 

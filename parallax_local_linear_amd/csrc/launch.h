@@ -37,6 +37,13 @@ inline size_t fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     return (size_t)(B * H * ((L + kStageKeys - 1) / kStageKeys) * kStageKeys * d * 2);
 }
 
+// Device memory the library owns for the prefill's workspace when the caller
+// cannot allocate (parallax_attn_fwd_noalloc): one array of this many bytes
+// per GPU, for the life of the process.
+constexpr size_t kFwdScratchBytes = size_t(64) << 20;
+// Device address of the current GPU's array (looked up once per device).
+hipError_t fwd_scratch(void **ptr);
+
 struct DecodeArgs {
     const uint16_t *q, *r;          // bf16 [B,H,d] contiguous
     const uint16_t *k, *v;          // bf16 [B,H,Lmax,d] with strides

@@ -61,7 +61,7 @@ parallax_status fwd_common(const void *q, const void *k, const void *v, const vo
                            parallax_strides sq, parallax_strides sk, parallax_strides sv,
                            parallax_strides sr, parallax_strides so, float softmax_scale,
                            int window, int n_sink, void *workspace, size_t workspace_bytes,
-                           void *stream, bool train, bool precise) {
+                           void *stream, bool train, bool precise, bool use_scratch = false) {
     if (B < 0 || H < 0 || L < 0)
         return PARALLAX_ERR_INVALID_ARG;
     if (d != 64 && d != 128)
@@ -80,14 +80,21 @@ parallax_status fwd_common(const void *q, const void *k, const void *v, const vo
         return PARALLAX_ERR_INVALID_ARG;
     if (!row_stride_ok(sq) || !row_stride_ok(sk) || !row_stride_ok(sv) || !row_stride_ok(sr))
         return PARALLAX_ERR_UNSUPPORTED;
-    if (!workspace || !aligned(workspace, 16) ||
-        workspace_bytes < plx::fwd_workspace_bytes(B, H, L, d))
+    if (use_scratch) {
+        // The library's own device array replaces the caller's workspace.
+        if (plx::fwd_workspace_bytes(B, H, L, d) > plx::kFwdScratchBytes)
+            return PARALLAX_ERR_UNSUPPORTED;
+    } else if (!workspace || !aligned(workspace, 16) ||
+               workspace_bytes < plx::fwd_workspace_bytes(B, H, L, d)) {
         return PARALLAX_ERR_INVALID_ARG;
+    }
 
     const int bm = plx::fwd_block_rows(d);
     const int64_t n_qtiles = ((int64_t)L + bm - 1) / bm;
     if ((int64_t)B * H * n_qtiles > INT_MAX)
         return PARALLAX_ERR_UNSUPPORTED;
+    if (use_scratch && plx::fwd_scratch(&workspace) != hipSuccess)
+        return PARALLAX_ERR_LAUNCH;
 
     plx::FwdArgs a;
     a.q = static_cast<const uint16_t *>(q);
@@ -129,6 +136,16 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
     return fwd_common(q, k, v, r, o, lse, nullptr, nullptr, B, H, L, d, sq, sk, sv, sr, so,
                       softmax_scale, window, n_sink, workspace, workspace_bytes, stream, false,
                       false);
+}
+
+parallax_status parallax_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                                          const void *r, float *o, float *lse, int B, int H,
+                                          int L, int d, parallax_strides sq, parallax_strides sk,
+                                          parallax_strides sv, parallax_strides sr,
+                                          parallax_strides so, float softmax_scale, int window,
+                                          int n_sink, void *stream) {
+    return fwd_common(q, k, v, r, o, lse, nullptr, nullptr, B, H, L, d, sq, sk, sv, sr, so,
+                      softmax_scale, window, n_sink, nullptr, 0, stream, false, false, true);
 }
 
 parallax_status parallax_attn_fwd_precise(const void *q, const void *k, const void *v,

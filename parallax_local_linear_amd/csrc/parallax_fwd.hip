@@ -68,9 +68,40 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace plx {
+
+// The prefill's workspace for callers that cannot allocate: a file-scope
+// device array, one copy per GPU, kept until the process ends.  Host code
+// never uses its name as an address (on the host it is only a stand-in for
+// the symbol): fwd_scratch() looks up each device's address once, with that
+// device current, and every launch takes that address.
+static __device__ __align__(256) unsigned char scratch[kFwdScratchBytes];
+
+hipError_t fwd_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 namespace {
 
 constexpr int ROWS = 16;                  // query rows per wavefront

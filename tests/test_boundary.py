@@ -378,3 +378,33 @@ def test_missing_library_fails_loudly(tmp_path):
             binding.load_library(str(tmp_path / "nope.so"))
     finally:
         binding._lib = saved
+
+
+def fwd_noalloc(lib, q=A16, k=A16, v=A16, r=A16, o=A16, lse=A16, B=1, H=2, L=64, d=64,
+                sq=CONTIG, sk=CONTIG, sv=CONTIG, sr=CONTIG, so=CONTIG, scale=0.125, window=0,
+                n_sink=0):
+    return lib.parallax_attn_fwd_noalloc(q, k, v, r, o, lse, B, H, L, d, sq, sk, sv, sr, so,
+                                         scale, window, n_sink, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(B=-1), INVALID), (dict(q=None), INVALID),
+    (dict(o=A16 + 4), INVALID), (dict(window=-1), INVALID), (dict(scale=0.0), INVALID),
+    (dict(sk=S(8 * 128 * 64, 4, 64)), INVALID),
+    # workspace need above the library's 64 MiB array: 2 x 16 x 8224 tokens at d = 128
+    (dict(B=2, H=16, L=8224, d=128), UNSUPPORTED),
+    (dict(B=1, H=1, L=(1 << 19) + 32, d=64), UNSUPPORTED),
+])
+def test_fwd_noalloc_rejects(lib, kw, status):
+    """Checked on the host before the library's device array is looked up."""
+    assert fwd_noalloc(lib, **kw) == status
+
+
+def test_fwd_noalloc_empty_problem_is_a_no_op(lib):
+    assert fwd_noalloc(lib, B=0, q=None, k=None, v=None, r=None, o=None, lse=None) == OK
+    assert fwd_noalloc(lib, L=0) == OK
+
+
+def test_fwd_noalloc_limit_is_the_headline_size():
+    """The 2 x 16 x 8192 x 128 workload's workspace is exactly 64 MiB."""
+    assert expected_workspace(2, 16, 8192, 128) == 64 << 20
