@@ -26,6 +26,10 @@ struct FwdArgs {
     float scale_log2;  // softmax_scale * log2(e), > 0
     int window;        // 0 = none
     int n_sink;
+    // Windowed kernel only (set by its launcher): 64-row tiles per (batch,
+    // head), tiles per workgroup run, runs per (batch, head), workgroups
+    // with work, and workgroups per XCD.
+    int w_tiles, w_tpw, w_runs, w_blocks, w_per_xcd;
 };
 
 // Workspace layout: for each (batch, head) and each 32-key stage s, the
@@ -36,6 +40,11 @@ constexpr int kStageKeys = 32;
 inline size_t fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     return (size_t)(B * H * ((L + kStageKeys - 1) / kStageKeys) * kStageKeys * d * 2);
 }
+
+// The prefill's windowed kernel takes windows of at most this many keys with
+// at most kFwdWinSinkMax sinks; other masks use the general kernel.
+constexpr int kFwdWinMax = 128;
+constexpr int kFwdWinSinkMax = 32;
 
 // Device memory the library owns for the prefill's workspace when the caller
 // cannot allocate (parallax_attn_fwd_noalloc): one array of this many bytes

@@ -68,6 +68,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -890,12 +891,331 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Windowed prefill: sliding windows of at most kWinMax keys with at most BN
+// sink keys ("Sliding-window beats linear attention" review, sec. 1 and
+// sec. 3: a 128-key window plus 4 sinks).  Such a row sees at most
+// kWinMax + BN keys, so the work is bound by reading q, k, v, r and writing
+// o, not by the matrix cores, and the kernel is shaped for streaming:
+//   * a tile is 64 query rows (4 wavefronts x 16 rows); a workgroup walks a
+//     run of consecutive tiles of one (batch, head), so K and V pass
+//     through its LDS once, and runs of one head are placed on one XCD so
+//     the key overlap between neighbouring runs is served by its L2;
+//   * keys live in an LDS ring of 32-key stages (stage s in slot s % 8): a
+//     tile spans at most 6 stages and adds 2 to the previous tile's, which
+//     are loaded into registers while the current tile is computed and
+//     written to their slots after it; the sink stage has its own buffer;
+//   * V is converted to float16 and transposed here, 8 keys x 8 features
+//     per thread in registers, into the same swizzled V^T layout the main
+//     prefill kernel reads from its workspace: no prepass, no workspace;
+//   * each wavefront takes only the stages its 16 rows see, the diagonal
+//     stage first (every row sees its own key there, so that stage sets all
+//     offsets), then the older window stages, then the sinks; a wavefront
+//     whose scores outgrow its offsets recomputes its rows alone, since the
+//     stages stay in LDS until the tile's closing barrier.
+constexpr int WWAVES = 4;                 // wavefronts per workgroup
+constexpr int WTHREADS = 64 * WWAVES;
+constexpr int WROWS = ROWS * WWAVES;      // query rows per tile
+constexpr int WRING = 8;                  // LDS stage slots
+constexpr int WNEW = WROWS / BN;          // stages each tile adds to the previous one's
+constexpr int kWinCUs = 256;              // compute units of the chip (MI355X)
+constexpr int kWinMax = kFwdWinMax;
+// A tile spans 2 + ceil((W - 1) / BN) stages.
+static_assert(2 + (kWinMax - 1 + BN - 1) / BN + WNEW <= WRING,
+              "the ring holds a tile's stages and the next tile's new ones");
+static_assert(kFwdWinSinkMax <= BN, "the sinks fit one stage");
+
+// One thread's share of a stage's V^T image: the 8 keys x 8 features block
+// (lane group G4 of positions, feature group fg) read from the bf16 values
+// (raw, 8 x 16 bytes) ...
+template <int D>
+__device__ __forceinline__ void vblock_load(u32x4 (&raw)[8], __amdgpu_buffer_rsrc_t rv,
+                                            int64_t v_l, int G4, int fg) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int key = k < 4 ? 4 * G4 + k : 16 + 4 * G4 + (k - 4);
+        raw[k] = bufld16(rv, (uint32_t)(key * v_l * 2 + 16 * fg));
+    }
+}
+
+// ... and written to the stage as float16, transposed: feature 8 fg + cf,
+// positions 8 G4 .. 8 G4 + 7 (the keys in the value MFMA's order).
+template <int D>
+__device__ __forceinline__ void vblock_store(uint16_t *sv, const u32x4 (&raw)[8], int G4, int fg) {
+    uint32_t hv[8][4];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            hv[k][i] = __builtin_bit_cast(uint32_t, cvt_f16x2(bf16_lo(raw[k][i]), bf16_hi(raw[k][i])));
+#pragma unroll
+    for (int cf = 0; cf < 8; ++cf) {
+        u32x4 out;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+            const uint32_t lo = hv[2 * pp][cf / 2], hi = hv[2 * pp + 1][cf / 2];
+            out[pp] = (cf & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+        *reinterpret_cast<u32x4 *>(sv + vswz_slot(8 * fg + cf, G4) * 8) = out;
+    }
+}
+
+template <int D, bool STATS, bool PRECISE>
+__global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window_kernel(FwdArgs a) {
+    using C = Cfg<D>;
+    constexpr int KCH = 32 * C::CPR / WTHREADS;  // K chunks per thread per stage
+    constexpr int FG = D / 8;                    // feature groups of a V^T block
+    constexpr int NVB = 4 * FG;                  // V^T blocks per stage
+    static_assert(KCH >= 1 && WNEW * NVB <= WTHREADS, "copy split");
+    __shared__ StageBuf<D> ring[WRING];
+    __shared__ StageBuf<D> sinkbuf;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int G = lane >> 4;
+
+    // Workgroup -> (batch, head, run): each XCD (block index mod 8) takes a
+    // contiguous range of runs, in order.
+    const int bid = blockIdx.x;
+    const int lin = (bid % 8) * a.w_per_xcd + bid / 8;
+    if (lin >= a.w_blocks)
+        return;
+    const int bh = lin / a.w_runs;
+    const int run = lin - bh * a.w_runs;
+    const int b = bh / a.H;
+    const int h = bh - b * a.H;
+    const int L = a.L;
+    const int window = a.window;
+    const int n_sink = a.n_sink;
+    const float c = a.scale_log2;
+    const int m_first = run * a.w_tpw;
+    const int m_end = min(m_first + a.w_tpw, a.w_tiles);
+
+    const uint16_t *qb = a.q + (int64_t)b * a.q_b + (int64_t)h * a.q_h;
+    const uint16_t *rb = a.r + (int64_t)b * a.r_b + (int64_t)h * a.r_h;
+    const uint16_t *kb = a.k + (int64_t)b * a.k_b + (int64_t)h * a.k_h;
+    const uint16_t *vb = a.v + (int64_t)b * a.v_b + (int64_t)h * a.v_h;
+
+    // Stages of tile m: from the first row's oldest window key to the last row.
+    auto st_first = [&](int m) {
+        const int lo = m * WROWS - window + 1;
+        return lo > 0 ? lo / BN : 0;
+    };
+    auto st_last = [&](int m) { return (min(m * WROWS + WROWS, L) - 1) / BN; };
+
+    // This thread's K chunks of a stage: slot s = tid + 256 ch holds chunk
+    // (s % CPR) ^ kswz(row) of key row s / CPR.
+    uint32_t koff[KCH];
+#pragma unroll
+    for (int ch = 0; ch < KCH; ++ch) {
+        const int s = tid + WTHREADS * ch;
+        const int r = s / C::CPR;
+        koff[ch] = (uint32_t)(r * a.k_l * 2 + ((s % C::CPR) ^ kswz<D>(r)) * 16);
+    }
+    auto stage_rsrc = [&](const uint16_t *base, int64_t ld, int st) {
+        const int j0 = st * BN;
+        return make_rsrc(base + (int64_t)j0 * ld, rows_bytes(j0, L, ld, D));
+    };
+    // A whole stage into an LDS buffer (all threads; used before the first tile).
+    auto load_stage = [&](StageBuf<D> &buf, int st) {
+        const __amdgpu_buffer_rsrc_t rk = stage_rsrc(kb, a.k_l, st);
+#pragma unroll
+        for (int ch = 0; ch < KCH; ++ch)
+            *reinterpret_cast<u32x4 *>(&buf.k[(tid + WTHREADS * ch) * 8]) = bufld16(rk, koff[ch]);
+        for (int blk = tid; blk < NVB; blk += WTHREADS) {
+            u32x4 raw[8];
+            vblock_load<D>(raw, stage_rsrc(vb, a.v_l, st), a.v_l, blk / FG, blk % FG);
+            vblock_store<D>(buf.v, raw, blk / FG, blk % FG);
+        }
+    };
+
+    // The first tile's stages and the sink stage.
+    for (int st = st_first(m_first); st <= st_last(m_first); ++st)
+        load_stage(ring[st % WRING], st);
+    if (n_sink > 0)
+        load_stage(sinkbuf, 0);
+
+    // Q and R fragments of a tile (rows past L read as zeros).
+    auto load_qr = [&](bf16x8 (&qf)[C::KC], bf16x8 (&rf)[C::KC], int m) {
+        const int i0w = m * WROWS + ROWS * wave;
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(qb + (int64_t)i0w * a.q_l, rows_bytes(i0w, L, a.q_l, D));
+        const __amdgpu_buffer_rsrc_t rr =
+            make_rsrc(rb + (int64_t)i0w * a.r_l, rows_bytes(i0w, L, a.r_l, D));
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc) {
+            const uint32_t col = (32 * kc + 8 * G) * 2;
+            qf[kc] = __builtin_bit_cast(bf16x8, bufld16(rq, (uint32_t)(l16 * a.q_l * 2) + col));
+            rf[kc] = __builtin_bit_cast(bf16x8, bufld16(rr, (uint32_t)(l16 * a.r_l * 2) + col));
+        }
+    };
+    Ctx<D> cx;
+    load_qr(cx.qf, cx.rf, m_first);
+    __syncthreads();
+
+    const FragAddr<D> fa = frag_addr<D>(l16, G);
+    KFrags<D> kf;
+    VFrags<D> vf;
+    Scores sc;
+    Weights<PRECISE> pw;
+    // The next tile's new stages and Q/R, in flight during the current tile.
+    u32x4 kpre[WNEW][KCH];
+    u32x4 vpre[8];
+    bf16x8 qn[C::KC], rn[C::KC];
+    const int vu = tid / NVB;        // new stage whose V^T block this thread converts
+    const int vblk = tid % NVB;
+
+    for (int m = m_first; m < m_end; ++m) {
+        const bool more = m + 1 < m_end;
+        const int new_lo = st_last(m) + 1;
+        const int n_new = more ? st_last(m + 1) - st_last(m) : 0;
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < WNEW; ++u) {
+                const __amdgpu_buffer_rsrc_t rk =
+                    u < n_new ? stage_rsrc(kb, a.k_l, new_lo + u) : make_rsrc(kb, 0u);
+#pragma unroll
+                for (int ch = 0; ch < KCH; ++ch)
+                    kpre[u][ch] = bufld16(rk, koff[ch]);
+            }
+            if (vu < n_new)
+                vblock_load<D>(vpre, stage_rsrc(vb, a.v_l, new_lo + vu), a.v_l, vblk / FG,
+                               vblk % FG);
+            load_qr(qn, rn, m + 1);
+        }
+
+        // This wavefront's rows: the diagonal stage first, then older window
+        // stages, then the sink stage when it lies before the window.
+        const int i0w = m * WROWS + ROWS * wave;
+        if (i0w < L) {
+            const int row = i0w + l16;
+            const int lo_w = i0w - window + 1 > 0 ? (i0w - window + 1) / BN : 0;
+            const int hi_w = min(i0w + ROWS - 1, L - 1) / BN;
+            const int n_win = hi_w - lo_w + 1;
+            const int n_st = n_win + (n_sink > 0 && lo_w > 0 ? 1 : 0);
+            cx.m_ref = kNegInf;
+            cx.msub = 0.f;
+            cx.xlane = kNegInf;
+            for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    cx.accA[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    cx.accC[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                }
+                cx.accL = (f32x4){0.f, 0.f, 0.f, 0.f};
+                cx.accS = (f32x4){0.f, 0.f, 0.f, 0.f};
+                for (int u = 0; u < n_st; ++u) {
+                    const int st = u < n_win ? hi_w - u : 0;
+                    StageBuf<D> &buf = u < n_win ? ring[st % WRING] : sinkbuf;
+                    read_kfrags<D>(kf, buf.k, fa);
+                    score_mfmas<D>(cx, kf, sc);
+                    mask_scores(sc, st * BN, row, G, L, window, n_sink);
+                    if (pass == 0 && u == 0)
+                        init_offsets<D>(cx, sc, c);
+                    weights<D, PRECISE>(cx, sc, pw, c);
+                    read_vfrags<D>(vf, buf.v, fa);
+                    value_mfmas<D, PRECISE>(cx, vf, pw);
+                }
+                const float xmax = row_max4(cx.xlane);
+                if (pass == 1 || __builtin_amdgcn_ballot_w64(xmax * c > cx.m_ref + kTauHi) == 0)
+                    break;
+                // Exact offsets for the recomputation: each row's true max.
+                cx.m_ref = xmax * c;
+                cx.msub = cx.m_ref == kNegInf ? 0.f : cx.m_ref;
+            }
+
+            const float ell_t = cx.accL[0];
+            const float s_t = cx.accS[0];
+            if (row < L) {
+                const float inv = 1.f / ell_t;
+                const float keep = 1.f - s_t * inv;
+                float *ob = a.o + (int64_t)b * a.o_b + (int64_t)h * a.o_h + (int64_t)row * a.o_l;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    f32x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        out[e] = (cx.accA[dt][e] * keep + cx.accC[dt][e]) * inv;
+                    *reinterpret_cast<f32x4 *>(ob + 16 * dt + 4 * G) = out;
+                }
+                if (G == 0)
+                    a.lse[(int64_t)bh * L + row] = (cx.m_ref + log2f(ell_t)) * kLn2;
+                if constexpr (STATS) {
+                    float *pb = a.pv + ((int64_t)bh * L + row) * D;
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) {
+                        f32x4 out;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            out[e] = cx.accA[dt][e] * inv;
+                        *reinterpret_cast<f32x4 *>(pb + 16 * dt + 4 * G) = out;
+                    }
+                    if (G == 0)
+                        a.sbar[(int64_t)bh * L + row] = s_t * inv;
+                }
+            }
+        }
+
+        if (more) {
+            // The new stages' slots held stages the previous tile used last;
+            // the current tile does not read them.
+#pragma unroll
+            for (int u = 0; u < WNEW; ++u)
+                if (u < n_new) {
+                    StageBuf<D> &buf = ring[(new_lo + u) % WRING];
+#pragma unroll
+                    for (int ch = 0; ch < KCH; ++ch)
+                        *reinterpret_cast<u32x4 *>(&buf.k[(tid + WTHREADS * ch) * 8]) = kpre[u][ch];
+                }
+            if (vu < n_new)
+                vblock_store<D>(ring[(new_lo + vu) % WRING].v, vpre, vblk / FG, vblk % FG);
+#pragma unroll
+            for (int kc = 0; kc < C::KC; ++kc) {
+                cx.qf[kc] = qn[kc];
+                cx.rf[kc] = rn[kc];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Bytes from the first element of a [L, d] slice with row stride ld
 // (2-byte elements) through its last element.
 int64_t slice_bytes(int64_t L, int64_t ld, int d) { return (L - 1) * ld * 2 + (int64_t)d * 2; }
 
 template <int D>
+hipError_t launch_fwd_window(const FwdArgs &a, bool precise, hipStream_t stream) {
+    FwdArgs args = a;
+    void *params[] = {&args};
+    // One round of workgroups: runs of consecutive tiles sized so that the
+    // chip's workgroup slots (two per CU at d = 64, one at d = 128, set by
+    // LDS) each take about one run.
+    const int64_t tiles = ((int64_t)a.L + WROWS - 1) / WROWS;
+    const int64_t slots = (int64_t)kWinCUs * (D == 64 ? 2 : 1);
+    const int64_t total = (int64_t)a.B * a.H * tiles;
+    const int64_t tpw = std::max<int64_t>(1, (total + slots - 1) / slots);
+    args.w_tiles = (int)tiles;
+    args.w_tpw = (int)std::min<int64_t>(tpw, tiles);
+    args.w_runs = (int)((tiles + args.w_tpw - 1) / args.w_tpw);
+    args.w_blocks = a.B * a.H * args.w_runs;
+    args.w_per_xcd = (args.w_blocks + 7) / 8;
+    const void *fn;
+    if (a.pv)
+        fn = reinterpret_cast<const void *>(&parallax_fwd_window_kernel<D, true, false>);
+    else if (precise)
+        fn = reinterpret_cast<const void *>(&parallax_fwd_window_kernel<D, false, true>);
+    else
+        fn = reinterpret_cast<const void *>(&parallax_fwd_window_kernel<D, false, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)(8 * args.w_per_xcd)), dim3(WTHREADS), params, 0,
+                           stream);
+}
+
+template <int D>
 hipError_t launch_fwd_t(const FwdArgs &a, bool precise, hipStream_t stream) {
+    if (a.window > 0 && a.window <= kFwdWinMax && a.n_sink <= kFwdWinSinkMax)
+        return launch_fwd_window<D>(a, precise, stream);
     FwdArgs args = a;
     void *params[] = {&args};
     constexpr int SPB = 256 / (4 * (D / 8));  // stages per prepass block

@@ -268,3 +268,30 @@ def test_side_stream_with_internal_workspace():
     junk.fill_(0x55)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+
+
+# Windows of at most 128 keys with at most 32 sinks take the windowed kernel:
+# 64-row tiles streamed in runs through a ring of key stages.  The first two
+# cases have more tiles than the chip has workgroup slots, so workgroups run
+# several consecutive tiles (2 at d = 64, 3 at d = 128).
+WINDOW_CASES = [
+    # (B, H, L, d, window, n_sink)
+    (1, 8, 5000, 64, 128, 4),
+    (1, 8, 5000, 128, 128, 4),
+    (2, 3, 777, 64, 1, 0),
+    (1, 2, 1000, 64, 16, 31),
+    (1, 2, 1000, 128, 33, 32),
+    (1, 2, 1000, 64, 100, 1),
+    (1, 2, 1000, 128, 127, 0),
+    (1, 1, 65, 64, 64, 4),
+    (1, 1, 31, 128, 128, 4),
+    (3, 2, 300, 64, 128, 32),
+]
+
+
+@pytest.mark.parametrize("B,H,L,d,window,n_sink", WINDOW_CASES)
+def test_window_kernel_shapes(orc, B, H, L, d, window, n_sink):
+    seed = 31 * L + 7 * d + window + 1000 * n_sink + B + 10 * H
+    q, k, v, r = (rand((B, H, L, d), seed + t) for t in range(4))
+    full_check(orc, q, k, v, r, window=window, n_sink=n_sink,
+               what="window kernel B%d H%d L%d d%d" % (B, H, L, d))
