@@ -45,6 +45,7 @@ inline size_t fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
 // at most kFwdWinSinkMax sinks; other masks use the general kernel.
 constexpr int kFwdWinMax = 128;
 constexpr int kFwdWinSinkMax = 32;
+constexpr int64_t kFwdWinMaxRowStride = int64_t(1) << 20;
 
 // Device memory the library owns for the prefill's workspace when the caller
 // cannot allocate (parallax_attn_fwd_noalloc): one array of this many bytes

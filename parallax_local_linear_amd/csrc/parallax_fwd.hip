@@ -378,6 +378,16 @@ __device__ __forceinline__ void mask_scores(Scores &s, int j0, int row, int G, i
     }
 }
 
+// Mask of a stage by a per-lane range of key offsets: element (kt, e), key
+// j0 + 4G + 16 kt + e, stays visible iff lo <= 16 kt + e <= hi.
+__device__ __forceinline__ void mask_range(Scores &s, int lo, int hi) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            s.q[kt][e] = (16 * kt + e >= lo && 16 * kt + e <= hi) ? s.q[kt][e] : kNegInf;
+}
+
 // Sets the softmax offset of rows that have none yet from this stage's row
 // max (+ kMargin); rows whose scores so far are all -inf stay unset.
 // Returns whether every row of the wavefront now has its offset.
@@ -919,44 +929,44 @@ constexpr int WROWS = ROWS * WWAVES;      // query rows per tile
 constexpr int WRING = 8;                  // LDS stage slots
 constexpr int WNEW = WROWS / BN;          // stages each tile adds to the previous one's
 constexpr int kWinCUs = 256;              // compute units of the chip (MI355X)
+constexpr int WPRO = 2 + (kFwdWinMax - 1 + BN - 1) / BN;  // most stages of one tile (6)
 constexpr int kWinMax = kFwdWinMax;
 // A tile spans 2 + ceil((W - 1) / BN) stages.
 static_assert(2 + (kWinMax - 1 + BN - 1) / BN + WNEW <= WRING,
               "the ring holds a tile's stages and the next tile's new ones");
 static_assert(kFwdWinSinkMax <= BN, "the sinks fit one stage");
 
-// One thread's share of a stage's V^T image: the 8 keys x 8 features block
-// (lane group G4 of positions, feature group fg) read from the bf16 values
-// (raw, 8 x 16 bytes) ...
-template <int D>
-__device__ __forceinline__ void vblock_load(u32x4 (&raw)[8], __amdgpu_buffer_rsrc_t rv,
-                                            int64_t v_l, int G4, int fg) {
+// One thread's share of a stage's V^T image: the 8 keys x 4 features block
+// (lane group G4 of positions, feature quad fq) of the stage starting at row
+// `row0` of the resource, read from the bf16 values (8 x 8 bytes) ...
+__device__ __forceinline__ void vblock_load(u32x2 (&raw)[8], __amdgpu_buffer_rsrc_t rv,
+                                            int64_t v_l, int row0, int G4, int fq) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const int key = k < 4 ? 4 * G4 + k : 16 + 4 * G4 + (k - 4);
-        raw[k] = bufld16(rv, (uint32_t)(key * v_l * 2 + 16 * fg));
+        const int key = row0 + (k < 4 ? 4 * G4 + k : 16 + 4 * G4 + (k - 4));
+        raw[k] = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(key * v_l * 2 + 8 * fq), 0, 0);
     }
 }
 
-// ... and written to the stage as float16, transposed: feature 8 fg + cf,
-// positions 8 G4 .. 8 G4 + 7 (the keys in the value MFMA's order).
-template <int D>
-__device__ __forceinline__ void vblock_store(uint16_t *sv, const u32x4 (&raw)[8], int G4, int fg) {
-    uint32_t hv[8][4];
+// ... and written to the stage as float16, transposed: feature 4 fq + cf,
+// positions 8 G4 .. 8 G4 + 7 (the keys in the value MFMA's order), one
+// 16-byte chunk per feature.
+__device__ __forceinline__ void vblock_store(uint16_t *sv, const u32x2 (&raw)[8], int G4, int fq) {
+    uint32_t hv[8][2];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
             hv[k][i] = __builtin_bit_cast(uint32_t, cvt_f16x2(bf16_lo(raw[k][i]), bf16_hi(raw[k][i])));
 #pragma unroll
-    for (int cf = 0; cf < 8; ++cf) {
+    for (int cf = 0; cf < 4; ++cf) {
         u32x4 out;
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
             const uint32_t lo = hv[2 * pp][cf / 2], hi = hv[2 * pp + 1][cf / 2];
             out[pp] = (cf & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
         }
-        *reinterpret_cast<u32x4 *>(sv + vswz_slot(8 * fg + cf, G4) * 8) = out;
+        *reinterpret_cast<u32x4 *>(sv + vswz_slot(4 * fq + cf, G4) * 8) = out;
     }
 }
 
@@ -964,9 +974,11 @@ template <int D, bool STATS, bool PRECISE>
 __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window_kernel(FwdArgs a) {
     using C = Cfg<D>;
     constexpr int KCH = 32 * C::CPR / WTHREADS;  // K chunks per thread per stage
-    constexpr int FG = D / 8;                    // feature groups of a V^T block
-    constexpr int NVB = 4 * FG;                  // V^T blocks per stage
-    static_assert(KCH >= 1 && WNEW * NVB <= WTHREADS, "copy split");
+    constexpr int FG = D / 4;                    // feature quads of a V^T block
+    constexpr int NVB = 4 * FG;                  // V^T blocks (8 keys x 4 features) per stage
+    constexpr int BPW = WNEW * NVB / WWAVES;     // new-stage V^T blocks per wavefront
+    constexpr int VPRO = ((WPRO + 1) * NVB + WTHREADS - 1) / WTHREADS;  // first-tile blocks per thread
+    static_assert(KCH >= 1 && BPW <= 64 && WNEW * NVB % WWAVES == 0, "copy split");
     __shared__ StageBuf<D> ring[WRING];
     __shared__ StageBuf<D> sinkbuf;
 
@@ -1014,28 +1026,12 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
         const int r = s / C::CPR;
         koff[ch] = (uint32_t)(r * a.k_l * 2 + ((s % C::CPR) ^ kswz<D>(r)) * 16);
     }
+    // Resource over the rows from stage st on (rows past L read as zeros);
+    // row strides of at most 2^20 keep 6 stages of offsets within 32 bits.
     auto stage_rsrc = [&](const uint16_t *base, int64_t ld, int st) {
         const int j0 = st * BN;
         return make_rsrc(base + (int64_t)j0 * ld, rows_bytes(j0, L, ld, D));
     };
-    // A whole stage into an LDS buffer (all threads; used before the first tile).
-    auto load_stage = [&](StageBuf<D> &buf, int st) {
-        const __amdgpu_buffer_rsrc_t rk = stage_rsrc(kb, a.k_l, st);
-#pragma unroll
-        for (int ch = 0; ch < KCH; ++ch)
-            *reinterpret_cast<u32x4 *>(&buf.k[(tid + WTHREADS * ch) * 8]) = bufld16(rk, koff[ch]);
-        for (int blk = tid; blk < NVB; blk += WTHREADS) {
-            u32x4 raw[8];
-            vblock_load<D>(raw, stage_rsrc(vb, a.v_l, st), a.v_l, blk / FG, blk % FG);
-            vblock_store<D>(buf.v, raw, blk / FG, blk % FG);
-        }
-    };
-
-    // The first tile's stages and the sink stage.
-    for (int st = st_first(m_first); st <= st_last(m_first); ++st)
-        load_stage(ring[st % WRING], st);
-    if (n_sink > 0)
-        load_stage(sinkbuf, 0);
 
     // Q and R fragments of a tile (rows past L read as zeros).
     auto load_qr = [&](bf16x8 (&qf)[C::KC], bf16x8 (&rf)[C::KC], int m) {
@@ -1053,19 +1049,78 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
     };
     Ctx<D> cx;
     load_qr(cx.qf, cx.rf, m_first);
+
+    // The first tile's stages (at most WPRO) and the sink stage, every load
+    // issued before the first LDS write.
+    {
+        const int s0 = st_first(m_first);
+        const int n0 = st_last(m_first) - s0 + 1;
+        const bool sink = n_sink > 0;
+        const __amdgpu_buffer_rsrc_t rk = stage_rsrc(kb, a.k_l, s0);
+        const __amdgpu_buffer_rsrc_t rv = stage_rsrc(vb, a.v_l, s0);
+        const __amdgpu_buffer_rsrc_t rk0 = stage_rsrc(kb, a.k_l, 0);
+        const __amdgpu_buffer_rsrc_t rv0 = stage_rsrc(vb, a.v_l, 0);
+        u32x4 kraw[WPRO + 1][KCH];
+        u32x2 vraw[VPRO][8];
+#pragma unroll
+        for (int p = 0; p <= WPRO; ++p)
+#pragma unroll
+            for (int ch = 0; ch < KCH; ++ch)
+                if (p < n0)
+                    kraw[p][ch] = bufld16(rk, koff[ch] + (uint32_t)(p * BN * a.k_l * 2));
+                else if (p == WPRO && sink)
+                    kraw[p][ch] = bufld16(rk0, koff[ch]);
+#pragma unroll
+        for (int i = 0; i < VPRO; ++i) {
+            const int blk = tid + WTHREADS * i;
+            const int p = blk / NVB;
+            const int vb_ = blk % NVB;
+            // Lanes of one wavefront may take blocks of two stages: the
+            // resource is uniform, the stage is in each lane's offset.
+            if (p < n0)
+                vblock_load(vraw[i], rv, a.v_l, p * BN, vb_ / FG, vb_ % FG);
+            else if (p == WPRO && sink)
+                vblock_load(vraw[i], rv0, a.v_l, 0, vb_ / FG, vb_ % FG);
+        }
+#pragma unroll
+        for (int p = 0; p <= WPRO; ++p)
+#pragma unroll
+            for (int ch = 0; ch < KCH; ++ch)
+                if (p < n0 || (p == WPRO && sink)) {
+                    StageBuf<D> &buf = p < WPRO ? ring[(s0 + p) % WRING] : sinkbuf;
+                    *reinterpret_cast<u32x4 *>(&buf.k[(tid + WTHREADS * ch) * 8]) = kraw[p][ch];
+                }
+#pragma unroll
+        for (int i = 0; i < VPRO; ++i) {
+            const int blk = tid + WTHREADS * i;
+            const int p = blk / NVB;
+            const int vb_ = blk % NVB;
+            if (p < n0 || (p == WPRO && sink)) {
+                StageBuf<D> &buf = p < WPRO ? ring[(s0 + p) % WRING] : sinkbuf;
+                vblock_store(buf.v, vraw[i], vb_ / FG, vb_ % FG);
+            }
+        }
+    }
+
+    // Every load so far has landed before the tile loop: the loop's wait
+    // counts then only cover the loads each tile issues for the next one
+    // (otherwise the first tile's Q/R loads would make every stage wait for
+    // the whole prefetch).
+    wait_copies<0>();
     __syncthreads();
 
     const FragAddr<D> fa = frag_addr<D>(l16, G);
-    KFrags<D> kf;
     VFrags<D> vf;
-    Scores sc;
     Weights<PRECISE> pw;
     // The next tile's new stages and Q/R, in flight during the current tile.
     u32x4 kpre[WNEW][KCH];
-    u32x4 vpre[8];
+    u32x2 vpre[8];
     bf16x8 qn[C::KC], rn[C::KC];
-    const int vu = tid / NVB;        // new stage whose V^T block this thread converts
-    const int vblk = tid % NVB;
+    // The new stages' V^T blocks are spread evenly over the wavefronts:
+    // lane < BPW of wavefront w converts block w * BPW + lane.
+    const bool v_role = lane < BPW;
+    const int vu = (wave * BPW + lane) / NVB;  // new stage of this lane's block
+    const int vblk = (wave * BPW + lane) % NVB;
 
     for (int m = m_first; m < m_end; ++m) {
         const bool more = m + 1 < m_end;
@@ -1080,9 +1135,9 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
                 for (int ch = 0; ch < KCH; ++ch)
                     kpre[u][ch] = bufld16(rk, koff[ch]);
             }
-            if (vu < n_new)
-                vblock_load<D>(vpre, stage_rsrc(vb, a.v_l, new_lo + vu), a.v_l, vblk / FG,
-                               vblk % FG);
+            if (v_role && vu < n_new)
+                vblock_load(vpre, stage_rsrc(vb, a.v_l, new_lo), a.v_l, vu * BN, vblk / FG,
+                            vblk % FG);
             load_qr(qn, rn, m + 1);
         }
 
@@ -1106,17 +1161,57 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
                 }
                 cx.accL = (f32x4){0.f, 0.f, 0.f, 0.f};
                 cx.accS = (f32x4){0.f, 0.f, 0.f, 0.f};
-                for (int u = 0; u < n_st; ++u) {
+                // Stage u of the list: window stage hi_w - u, or the sinks.
+                auto stage_buf = [&](int u) -> StageBuf<D> & {
+                    return u < n_win ? ring[(hi_w - u) % WRING] : sinkbuf;
+                };
+                // Window stages every row of the wavefront sees in full need
+                // no mask: keys [j_full_lo, j_full_hi] are visible to all 16.
+                const int j_full_lo = i0w + ROWS - window;
+                const int j_full_hi = min(i0w, L - 1);
+                // Software pipeline over the stages: step u reads stage u's
+                // V^T fragments, issues stage u+1's score MFMAs (their K
+                // fragments were read two steps earlier), reads stage u+3's
+                // K fragments into the buffer those MFMAs free, and meanwhile
+                // forms stage u's weights on the VALU, then issues its value
+                // MFMAs.  The matrix core and the VALU of one wavefront then
+                // overlap instead of waiting on each other.
+                auto step = [&](int u, Scores &cur, KFrags<D> &knext, Scores &nxt)
+                    __attribute__((always_inline)) {
                     const int st = u < n_win ? hi_w - u : 0;
-                    StageBuf<D> &buf = u < n_win ? ring[st % WRING] : sinkbuf;
-                    read_kfrags<D>(kf, buf.k, fa);
-                    score_mfmas<D>(cx, kf, sc);
-                    mask_scores(sc, st * BN, row, G, L, window, n_sink);
+                    read_vfrags<D>(vf, stage_buf(u).v, fa);
+                    if (u + 1 < n_st)
+                        score_mfmas<D>(cx, knext, nxt);
+                    if (u + 3 < n_st)
+                        read_kfrags<D>(knext, stage_buf(u + 3).k, fa);
+                    const int j0 = st * BN;
+                    const bool full = u < n_win && j0 >= j_full_lo && j0 + BN - 1 <= j_full_hi;
+                    // Lane offsets of its keys from the row: key j0 + 4G + o
+                    // is at o - (row - j0 - 4G) from it.
+                    const int rel = row - j0 - 4 * G;
+                    if (u >= n_win)
+                        mask_range(cur, INT32_MIN / 2, n_sink - 1 - 4 * G);  // sinks: j < n_sink
+                    else if (j0 < n_sink)
+                        mask_scores(cur, j0, row, G, L, window, n_sink);  // sinks inside the span
+                    else if (!full)
+                        mask_range(cur, rel - window + 1, rel);  // window and causal bounds
                     if (pass == 0 && u == 0)
-                        init_offsets<D>(cx, sc, c);
-                    weights<D, PRECISE>(cx, sc, pw, c);
-                    read_vfrags<D>(vf, buf.v, fa);
+                        init_offsets<D>(cx, cur, c);
+                    weights<D, PRECISE>(cx, cur, pw, c);
                     value_mfmas<D, PRECISE>(cx, vf, pw);
+                };
+                KFrags<D> kf0, kf1;
+                Scores sc0, sc1;
+                read_kfrags<D>(kf0, stage_buf(0).k, fa);
+                if (n_st > 1)
+                    read_kfrags<D>(kf1, stage_buf(1).k, fa);
+                score_mfmas<D>(cx, kf0, sc0);
+                if (n_st > 2)
+                    read_kfrags<D>(kf0, stage_buf(2).k, fa);
+                for (int u = 0; u < n_st; u += 2) {
+                    step(u, sc0, kf1, sc1);
+                    if (u + 1 < n_st)
+                        step(u + 1, sc1, kf0, sc0);
                 }
                 const float xmax = row_max4(cx.xlane);
                 if (pass == 1 || __builtin_amdgcn_ballot_w64(xmax * c > cx.m_ref + kTauHi) == 0)
@@ -1169,8 +1264,8 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
                     for (int ch = 0; ch < KCH; ++ch)
                         *reinterpret_cast<u32x4 *>(&buf.k[(tid + WTHREADS * ch) * 8]) = kpre[u][ch];
                 }
-            if (vu < n_new)
-                vblock_store<D>(ring[(new_lo + vu) % WRING].v, vpre, vblk / FG, vblk % FG);
+            if (v_role && vu < n_new)
+                vblock_store(ring[(new_lo + vu) % WRING].v, vpre, vblk / FG, vblk % FG);
 #pragma unroll
             for (int kc = 0; kc < C::KC; ++kc) {
                 cx.qf[kc] = qn[kc];
@@ -1214,7 +1309,9 @@ hipError_t launch_fwd_window(const FwdArgs &a, bool precise, hipStream_t stream)
 
 template <int D>
 hipError_t launch_fwd_t(const FwdArgs &a, bool precise, hipStream_t stream) {
-    if (a.window > 0 && a.window <= kFwdWinMax && a.n_sink <= kFwdWinSinkMax)
+    if (a.window > 0 && a.window <= kFwdWinMax && a.n_sink <= kFwdWinSinkMax &&
+        a.q_l <= kFwdWinMaxRowStride && a.k_l <= kFwdWinMaxRowStride &&
+        a.v_l <= kFwdWinMaxRowStride && a.r_l <= kFwdWinMaxRowStride)
         return launch_fwd_window<D>(a, precise, stream);
     FwdArgs args = a;
     void *params[] = {&args};
