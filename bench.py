@@ -251,6 +251,45 @@ def time_prefill_leg(cfg, bound, runs, warmup, stream, flush=None, precise=False
             "tflops": round(tflops, 2), "gbs": round(gbs, 1), "roofline": roof}
 
 
+def recomputed_tiles(ws, cfg):
+    """Query tiles the last prefill call on workspace `ws` recomputed: the
+    counter the library leaves after the f16 V image."""
+    import torch
+    image = cfg.B * cfg.H * (-(-cfg.L // 32)) * 32 * cfg.d * 2
+    return int(ws[image:image + 4].view(torch.int32).item())
+
+
+def time_rising(cfg, runs, warmup, stream):
+    """The prefill call on inputs whose scores rise along the sequence (most
+    query tiles then repeat with the exact row maxima): the cost of that
+    second pass at full size.  Same FLOP count as the plain call."""
+    import statistics
+
+    import torch
+
+    from parallax_local_linear_amd import (accounting, parallax_attn_fwd,
+                                           parallax_attn_fwd_workspace_size, workloads)
+    dev = torch.device("cuda:0")
+    q, k, v, r = workloads.rising_inputs(cfg.B, cfg.H, cfg.L, cfg.d, seed=1000 + cfg.seed,
+                                         device=dev)
+    o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(parallax_attn_fwd_workspace_size(cfg.B, cfg.H, cfg.L, cfg.d),
+                     dtype=torch.uint8, device=dev)
+    times = time_each_call(lambda: parallax_attn_fwd(q, k, v, r, out=o, lse=lse, workspace=ws,
+                                                     stream=stream), runs, warmup, stream)
+    med = statistics.median(times)
+    n_tiles = cfg.B * cfg.H * (-(-cfg.L // 128))
+    count = recomputed_tiles(ws, cfg)
+    tflops = accounting.prefill_flops(cfg) / (med * 1e-3) / 1e12
+    return {"workload": cfg.name + " with rising scores", "ms_median": round(med, 4),
+            "ms_min": round(min(times), 4), "value": round(tflops, 2), "unit": "TFLOP/s",
+            "recomputed_tiles": count, "tiles": n_tiles,
+            "recompute_fraction": round(count / n_tiles, 4),
+            "inputs": "q = 3u + 0.1z, k_j = (46 (d/64)^1/2 j/L) u + 0.1z, v ~ N(0,1), "
+                      "r ~ 0.25 N(0,1)"}
+
+
 def time_backward(cfg, steps, warmup, stream):
     """Mean time (HIP events on `stream`) of parallax_attn_bwd on one prefill workload."""
     import torch
@@ -557,6 +596,8 @@ def main():
     print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
 
     total_ms = t_start.elapsed_time(t_end)
+    n_tiles = pcfg.B * pcfg.H * (-(-pcfg.L // 128))
+    recomputed = recomputed_tiles(ws, pcfg)
     pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
     pre_avg = sum(pre_ms) / len(pre_ms)
@@ -589,6 +630,8 @@ def main():
             "precision": "bf16 inputs; bf16 score MFMA, f16 value MFMA, fp32 accumulate; fp32 O",
         },
         "prefill_ms": round(pre_avg, 4),
+        "prefill_recompute": {"recomputed_tiles": recomputed, "tiles": n_tiles,
+                              "fraction": round(recomputed / n_tiles, 4)},
         "prefill_ms_median": round(statistics.median(pre_ms), 4),
         "prefill_ms_min": round(min(pre_ms), 4),
         "roofline": {
@@ -641,6 +684,8 @@ def main():
     res["local_swa128_sink4"] = time_prefill_leg(workloads.LOCAL, "hbm", 20, 5, stream, flush)
     print("[bench] timing the precise prefill", file=sys.stderr, flush=True)
     res["precise"] = time_prefill_leg(pcfg, "mfma", 20, 3, stream, precise=True)
+    print("[bench] timing the prefill on rising scores", file=sys.stderr, flush=True)
+    res["rising"] = time_rising(pcfg, 10, 2, stream)
     del flush
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -93,10 +93,19 @@ typedef struct {
 
 /*
  * Bytes of device workspace parallax_attn_fwd needs for these sizes: the
- * values converted to float16 and laid out per 32-key stage, i.e.
- * B * H * ceil(L / 32) * 32 * d * 2 bytes (0 when B, H or L is 0).  Returns
- * 0 for sizes parallax_attn_fwd would reject (negative sizes, d not in
- * {64, 128}).
+ * values converted to float16 and laid out per 32-key stage,
+ * I = B * H * ceil(L / 32) * 32 * d * 2 bytes, then 256 bytes of counters
+ * (I + 256 in all; 0 when B, H or L is 0).  Returns 0 for sizes
+ * parallax_attn_fwd would reject (negative sizes, d not in {64, 128}).
+ *
+ * Diagnostics: once a call's work has finished, the 4 bytes at offset I of
+ * its workspace hold, as an unsigned 32-bit integer, the number of
+ * 128-row query tiles whose workgroup took the exact second pass (the
+ * first pass fixes each row's softmax offset at its first stage; a row
+ * whose scores later rise more than 2^5 above it makes its tile repeat
+ * with the exact row maximum).  Calls that take the windowed kernel (a
+ * window of at most 128 keys with at most 32 sinks) recompute per
+ * 16-row wavefront and leave these bytes unwritten.
  */
 size_t parallax_attn_fwd_workspace_size(int B, int H, int L, int d);
 
@@ -142,12 +151,12 @@ parallax_status parallax_attn_fwd(const void *q, const void *k, const void *v, c
  * Causal prefill forward for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): parallax_attn_fwd without the workspace arguments.  The
- * library keeps the workspace itself, in one device array of 64 MiB
- * (67108864 bytes) per GPU that holds it until the process ends; this call
- * allocates and frees nothing.  The array of the current device is used,
+ * library keeps the workspace itself, in one device array of 64 MiB + 256
+ * bytes (67109120 bytes) per GPU that holds it until the process ends;
+ * this call allocates and frees nothing.  The array of the current device is used,
  * so `stream` must belong to that device.
  *
- *   Sizes whose workspace (parallax_attn_fwd_workspace_size) exceeds 64 MiB
+ *   Sizes whose workspace (parallax_attn_fwd_workspace_size) exceeds that
  *   -- e.g. more than 2 x 16 heads x 8192 tokens at d = 128 -- return
  *   PARALLAX_ERR_UNSUPPORTED.  Every call on a GPU shares that GPU's array
  *   and overwrites it in full before reading it (no contents carry over

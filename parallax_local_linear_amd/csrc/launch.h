@@ -15,6 +15,7 @@ struct FwdArgs {
     float *sbar;                    // optional [B,H,L] contiguous: sum_j p_ij rho_i.k_j
     float *pv;                      // optional [B,H,L,d] contiguous: sum_j p_ij v_j
     uint16_t *vt;                   // workspace: f16 bits, [B*H][n_st][d][32] (see below)
+    unsigned *counters;             // workspace after the image: [0] = query tiles recomputed
     int64_t q_b, q_h, q_l;
     int64_t k_b, k_h, k_l;
     int64_t v_b, v_h, v_l;
@@ -36,9 +37,16 @@ struct FwdArgs {
 // values of keys 32s .. 32s+31 as float16, transposed to [d features][32
 // positions] with the keys permuted as the prefill's value MFMA reads them
 // (zeros for keys >= L).
+// After the image, a block of counters: [0] counts the 128-row query tiles
+// of the general kernel that took the exact second pass.
 constexpr int kStageKeys = 32;
-inline size_t fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
+constexpr size_t kFwdCounterBytes = 256;
+inline size_t fwd_image_bytes(int64_t B, int64_t H, int64_t L, int d) {
     return (size_t)(B * H * ((L + kStageKeys - 1) / kStageKeys) * kStageKeys * d * 2);
+}
+inline size_t fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
+    const size_t image = fwd_image_bytes(B, H, L, d);
+    return image ? image + kFwdCounterBytes : 0;
 }
 
 // The prefill's windowed kernel takes windows of at most this many keys with
@@ -50,7 +58,7 @@ constexpr int64_t kFwdWinMaxRowStride = int64_t(1) << 20;
 // Device memory the library owns for the prefill's workspace when the caller
 // cannot allocate (parallax_attn_fwd_noalloc): one array of this many bytes
 // per GPU, for the life of the process.
-constexpr size_t kFwdScratchBytes = size_t(64) << 20;
+constexpr size_t kFwdScratchBytes = (size_t(64) << 20) + kFwdCounterBytes;
 // Device address of the current GPU's array (looked up once per device).
 hipError_t fwd_scratch(void **ptr);
 

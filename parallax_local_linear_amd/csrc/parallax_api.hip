@@ -106,6 +106,8 @@ parallax_status fwd_common(const void *q, const void *k, const void *v, const vo
     a.sbar = train ? sbar : nullptr;
     a.pv = train ? pv : nullptr;
     a.vt = static_cast<uint16_t *>(workspace);
+    a.counters = reinterpret_cast<unsigned *>(static_cast<char *>(workspace) +
+                                              plx::fwd_image_bytes(B, H, L, d));
     a.q_b = sq.b; a.q_h = sq.h; a.q_l = sq.l;
     a.k_b = sk.b; a.k_h = sk.h; a.k_l = sk.l;
     a.v_b = sv.b; a.v_h = sv.h; a.v_l = sv.l;

@@ -470,6 +470,9 @@ __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
     // First stage of this wavefront: the buffer resource starts there, so
     // it is uniform and offsets stay small for any row stride.
     const int s_wave = blockIdx.x * SPB + (threadIdx.x / 64) * SPW;
+    // The main kernel, which runs after this one, counts recomputed tiles.
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        a.counters[0] = 0u;
     if (s_wave >= a.n_st)
         return;
     const int j0 = s * BN;
@@ -861,6 +864,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         wait_copies<0>();
         if (!__syncthreads_or(overflow))
             break;
+        if (tid == 0)
+            atomicAdd(a.counters, 1u);
         // Exact offsets for the recomputation: each row's true max.
         cx.m_ref = xmax * c;
         cx.msub = cx.m_ref == kNegInf ? 0.f : cx.m_ref;

@@ -119,6 +119,24 @@ def based_inputs(cfg: Based, device="cpu", dtype=torch.bfloat16):
     return q, k, v
 
 
+def rising_inputs(B: int, H: int, L: int, d: int, seed: int, device="cpu",
+                  dtype=torch.bfloat16):
+    """(q, k, v, r) whose attention scores rise along the sequence: with u a
+    seeded random unit vector, q_i = 3u + 0.1 z, k_j = (46 (d/64)^1/2 j / L) u
+    + 0.1 z, v ~ N(0, 1), r ~ 0.25 N(0, 1) (z i.i.d. N(0, 1)).  A row's later
+    keys then score about 25 log2 units above its first ones."""
+    g = _gen(device, seed)
+    u = torch.randn(d, generator=g, device=device)
+    u = u / u.norm()
+    ramp = 46.0 * (d / 64) ** 0.5 * torch.arange(L, dtype=torch.float32, device=device) / L
+    shape = (B, H, L, d)
+    q = 3.0 * u + 0.1 * torch.randn(shape, generator=g, device=device)
+    k = ramp[:, None] * u + 0.1 * torch.randn(shape, generator=g, device=device)
+    v = torch.randn(shape, generator=g, device=device)
+    r = 0.25 * torch.randn(shape, generator=g, device=device)
+    return tuple(x.to(dtype) for x in (q, k, v, r))
+
+
 def random_tensor(shape, seed: int, device="cpu", scale: float = 1.0, dtype=torch.bfloat16):
     """One seeded N(0, scale^2) tensor (edge-case tests)."""
     g = _gen(device, seed)

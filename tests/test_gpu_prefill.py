@@ -295,3 +295,31 @@ def test_window_kernel_shapes(orc, B, H, L, d, window, n_sink):
     q, k, v, r = (rand((B, H, L, d), seed + t) for t in range(4))
     full_check(orc, q, k, v, r, window=window, n_sink=n_sink,
                what="window kernel B%d H%d L%d d%d" % (B, H, L, d))
+
+
+@pytest.mark.parametrize("rising", [False, True], ids=["normal", "rising"])
+def test_recompute_counter(orc, rising):
+    """The workspace's counter (4 bytes after the V image) holds the number of
+    128-row query tiles that took the exact second pass: most tiles for keys
+    whose scores rise along the sequence, about none for N(0,1) inputs; the
+    outputs match the oracle either way."""
+    B, H, L, d = 1, 2, 1024, 128
+    if rising:
+        q, k, v, r = workloads.rising_inputs(B, H, L, d, seed=77)
+    else:
+        q, k, v, r = (rand((B, H, L, d), 7700 + t) for t in range(4))
+    n_tiles = B * H * (L // 128)
+    image = B * H * (L // 32) * 32 * d * 2
+    ws = torch.full((parallax_attn_fwd_workspace_size(B, H, L, d),), 0xAB, dtype=torch.uint8,
+                    device=DEV)
+    o, lse = parallax_attn_fwd(*(x.to(DEV) for x in (q, k, v, r)), workspace=ws)
+    torch.cuda.synchronize()
+    count = int(ws[image:image + 4].view(torch.int32).item())
+    say("[counter] %s: %d of %d tiles recomputed" % ("rising" if rising else "normal", count,
+                                                      n_tiles))
+    if rising:
+        assert n_tiles // 2 <= count <= n_tiles
+    else:
+        assert 0 <= count <= 1
+    o_ref, lse_ref = orc.fwd(f64(q), f64(k), f64(v), f64(r))
+    compare(f64(o), f64(lse), o_ref, lse_ref, "recompute counter %s" % rising)
