@@ -31,7 +31,14 @@ and one parallax_based_decode step for 64 x 16 heads, bytes: the fp32 state
 read and written) under "based"; then the prefill backward (parallax_attn_bwd: dq, dk, dv,
 drho of the same prefill workload, with a seeded N(0,1) output gradient) is
 timed separately and reported under "backward" (algorithmic FLOP: 16d per
-visible pair); it is not part of a step.
+visible pair); it is not part of a step.  Then the 0.6B-like causal prefill
+("prefill_0.6b", matrix-core roofline) and the windowed prefill with a
+128-key window and 4 sinks ("local_swa128_sink4", HBM roofline), each timed
+call by call with a 512 MB buffer overwritten between calls (median and
+min); the precise prefill on the headline workload ("precise"); and the
+headline prefill on inputs whose scores rise along the sequence ("rising",
+with the fraction of query tiles that took the exact second pass).
+`--legs` selects a subset of these secondary legs (profiling runs).
 """
 from __future__ import annotations
 
@@ -76,6 +83,9 @@ PREFILL_KERNELS = {
                           "parallax_fwd_kernel<64, true, false, false>",
 }
 FLUSH_BYTES = 512 << 20     # overwritten between timed calls: more than L2 + the 256 MB MALL
+# Legs timed after the steps, each reported under its own key.
+SECONDARY_LEGS = ("decode_paged", "projection", "hadamard", "based", "backward", "prefill_0.6b",
+                  "local_swa128_sink4", "precise", "rising")
 
 
 def parse():
@@ -92,6 +102,9 @@ def parse():
                         "computes")
     p.add_argument("--no-backward", action="store_true",
                    help="skip timing the prefill backward")
+    p.add_argument("--legs", default=None,
+                   help="comma-separated subset of the secondary legs to time after the "
+                        "steps (default: all of %s)" % ",".join(SECONDARY_LEGS))
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a plain 1 GiB device-to-device copy kernel three times, "
                         "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -662,31 +675,45 @@ def main():
             },
         },
     }
-    print("[bench] timing the general decode", file=sys.stderr, flush=True)
-    res["decode_paged"] = time_decode_paged(dcfg, min(args.steps, 20),
-                                            max(1, min(args.warmup, 3)), stream)
-    print("[bench] timing the projections", file=sys.stderr, flush=True)
-    res["projection"] = time_projection(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
-                                        stream)
-    print("[bench] timing the Hadamard output projection", file=sys.stderr, flush=True)
-    res["hadamard"] = time_hadamard(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
-                                    stream)
-    print("[bench] timing Based linear attention", file=sys.stderr, flush=True)
-    res["based"] = time_based(min(args.steps, 20), max(1, min(args.warmup, 3)), stream)
-    if not args.no_backward:
+    legs = set(SECONDARY_LEGS if args.legs is None else args.legs.split(","))
+    unknown = legs - set(SECONDARY_LEGS)
+    if unknown:
+        sys.exit("unknown --legs %s (known: %s)" % (",".join(sorted(unknown)),
+                                                    ",".join(SECONDARY_LEGS)))
+    if args.no_backward:
+        legs.discard("backward")
+    few, warm = min(args.steps, 20), max(1, min(args.warmup, 3))
+    if "decode_paged" in legs:
+        print("[bench] timing the general decode", file=sys.stderr, flush=True)
+        res["decode_paged"] = time_decode_paged(dcfg, few, warm, stream)
+    if "projection" in legs:
+        print("[bench] timing the projections", file=sys.stderr, flush=True)
+        res["projection"] = time_projection(pcfg, few, warm, stream)
+    if "hadamard" in legs:
+        print("[bench] timing the Hadamard output projection", file=sys.stderr, flush=True)
+        res["hadamard"] = time_hadamard(pcfg, few, warm, stream)
+    if "based" in legs:
+        print("[bench] timing Based linear attention", file=sys.stderr, flush=True)
+        res["based"] = time_based(few, warm, stream)
+    if "backward" in legs:
         print("[bench] timing the backward", file=sys.stderr, flush=True)
-        res["backward"] = time_backward(pcfg, min(args.steps, 20), max(1, min(args.warmup, 3)),
-                                        stream)
-    print("[bench] timing the 0.6B-like and windowed prefill workloads", file=sys.stderr,
-          flush=True)
+        res["backward"] = time_backward(pcfg, few, warm, stream)
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    res["prefill_0.6b"] = time_prefill_leg(workloads.PREFILL_06B, "mfma", 20, 5, stream, flush)
-    res["local_swa128_sink4"] = time_prefill_leg(workloads.LOCAL, "hbm", 20, 5, stream, flush)
-    print("[bench] timing the precise prefill", file=sys.stderr, flush=True)
-    res["precise"] = time_prefill_leg(pcfg, "mfma", 20, 3, stream, precise=True)
-    print("[bench] timing the prefill on rising scores", file=sys.stderr, flush=True)
-    res["rising"] = time_rising(pcfg, 10, 2, stream)
+    if "prefill_0.6b" in legs:
+        print("[bench] timing the 0.6B-like prefill", file=sys.stderr, flush=True)
+        res["prefill_0.6b"] = time_prefill_leg(workloads.PREFILL_06B, "mfma", 20, 5, stream,
+                                               flush)
+    if "local_swa128_sink4" in legs:
+        print("[bench] timing the windowed prefill", file=sys.stderr, flush=True)
+        res["local_swa128_sink4"] = time_prefill_leg(workloads.LOCAL, "hbm", 20, 5, stream,
+                                                     flush)
     del flush
+    if "precise" in legs:
+        print("[bench] timing the precise prefill", file=sys.stderr, flush=True)
+        res["precise"] = time_prefill_leg(pcfg, "mfma", 20, 3, stream, precise=True)
+    if "rising" in legs:
+        print("[bench] timing the prefill on rising scores", file=sys.stderr, flush=True)
+        res["rising"] = time_rising(pcfg, 10, 2, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(pcfg, args.cpu_sample_heads, workloads.PREFILL_06B,
