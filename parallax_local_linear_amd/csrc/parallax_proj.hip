@@ -20,13 +20,22 @@
 //     chunks.  The product is taken transposed (Y^T = W X^T): a lane's
 //     accumulator holds four consecutive output features of one token,
 //     stored as one 8-byte write.
-//   * Each k chunk of both operands is copied into LDS as 1 KiB blocks in
-//     fragment order (lane l holds row l % 16, k offsets 8 (l / 16) .. +7),
-//     directly from global memory, three chunks ahead of use in four stage
-//     buffers; fragment reads are one 16-byte LDS read per lane at l * 16.
-//   * The fragments of chunk k + 1 are read into a second register set
-//     while the 64 MFMAs of chunk k run, so LDS latency and the per-chunk
-//     barrier hide behind the matrix cores.
+//   * Operands reach LDS in stages 64 k wide, copied directly from global
+//     memory into two stage buffers, a stage's copy issued while the stage
+//     before it runs.  Each copy moves
+//     8 rows x 128 bytes, whole 128-byte lines: copies of 16 rows x 64 bytes
+//     (a 32-k chunk) move about a quarter as many bytes per clock from L2.
+//     A row's eight 16-byte pieces land in LDS XOR-swizzled by the row
+//     (piece c of row r at slot c ^ (r % 8) ^ ((r / 8) % 2)), so the
+//     fragment reads (16 rows x 16 bytes per 16 lanes) hit distinct banks.
+//   * The fragments of the next 32-k half are read into a second register
+//     set while the 64 MFMAs of the current half run, so LDS latency and
+//     the per-stage barrier hide behind the matrix cores; in a stage's first
+//     half the reads are spread between the MFMAs.
+//   * Persistent: one workgroup per compute unit walks its tiles with one
+//     stream of stages across them, so the next tile's first stages are
+//     copied while the current tile's last ones run and its outputs are
+//     stored while the next tile's first MFMAs run.
 //   * Blocks past the edges of X or W read zeros (buffer resources that end
 //     at the last row); rows and columns past M and N are not stored.
 #include "device_common.h"
@@ -39,25 +48,22 @@ namespace {
 
 constexpr int TM = 256;      // tokens per workgroup tile
 constexpr int TN = 256;      // output features per workgroup tile
-constexpr int TK = 32;       // k per stage
+constexpr int TK = 64;       // k per stage (two 32-k halves)
 constexpr int PW = 4;        // wavefronts per workgroup
 constexpr int WM = 128;      // tokens per wavefront tile
 constexpr int WN = 128;      // features per wavefront tile
-constexpr int NSTAGE = 4;
-constexpr int XBLK = TM / 16;  // X blocks per stage (16 rows x 32 k each)
-constexpr int WBLK = TN / 16;  // W blocks per stage
-constexpr int CPW = (XBLK + WBLK) / PW;  // copies per wave per stage
+constexpr int XGRP = TM / 8;  // 8-row copy groups of X per stage
+constexpr int WGRP = TN / 8;  // of W
+constexpr int CPW = (XGRP + WGRP) / PW;  // copies per wave per stage
 
-static_assert((XBLK + WBLK) % PW == 0 && XBLK % PW == 0, "copy split");
+static_assert((XGRP + WGRP) % PW == 0 && XGRP % PW == 0, "copy split");
 static_assert(TM == 2 * WM && TN == 2 * WN, "2 x 2 wavefronts");
 
+// One stage: rows of 128 bytes (64 k), pieces swizzled as described above.
 struct ProjStage {
-    u32x4 x[XBLK][64];
-    u32x4 w[WBLK][64];
+    u32x4 x[TM][8];
+    u32x4 w[TN][8];
 };
-
-template <int I>
-using SBuf = std::integral_constant<int, I % NSTAGE>;
 
 __device__ __forceinline__ void stage_barrier() {
     __builtin_amdgcn_sched_barrier(0);
@@ -74,37 +80,25 @@ __device__ __forceinline__ void wait_copies() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// LDS slot of 16-byte piece c of row r within its stage operand.
+__device__ __forceinline__ int piece_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 typedef __attribute__((address_space(3))) void lds_void;
 
-__global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
-    __shared__ ProjStage s0, s1, s2, s3;
-    auto sbuf = [&](auto b) -> ProjStage & {
-        constexpr int i = decltype(b)::value % NSTAGE;
-        if constexpr (i == 0) return s0;
-        else if constexpr (i == 1) return s1;
-        else if constexpr (i == 2) return s2;
-        else return s3;
-    };
+struct Tile {
+    int m0, n0;
+};
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15;
-    const int G = lane >> 4;
-    const int wm = wave / 2;  // wavefront row (tokens)
-    const int wn = wave % 2;  // wavefront column (features)
-
-    // Tile order.  Workgroups are dealt to the 8 XCDs round-robin
-    // (blockIdx % 8), each XCD with its own L2, so the block index is first
-    // renumbered to give every XCD one contiguous run of tiles; within the
-    // run, tiles walk M fastest inside groups of GROUP M tiles, so that the
-    // workgroups running together on one XCD share their X and W tiles in
-    // that XCD's L2.
-    const int n_tm = (a.M + TM - 1) / TM;
-    const int n_tn = (a.N + TN - 1) / TN;
+// Tile of virtual block v.  Workgroups are dealt to the 8 XCDs round-robin
+// (v % 8, with a grid that is a multiple of 8), each XCD with its own L2, so
+// v is first renumbered to give every XCD one contiguous run of tiles;
+// within the run, tiles walk M fastest inside groups of GROUP M tiles, so
+// that the workgroups running together on one XCD share their X and W tiles
+// in that XCD's L2.
+__device__ __forceinline__ Tile tile_of(int v, int n_tm, int n_tn) {
     const int n_tiles = n_tm * n_tn;
-    const int xcd = blockIdx.x % 8;
-    const int slot = blockIdx.x / 8;
+    const int xcd = v % 8;
+    const int slot = v / 8;
     const int per = n_tiles / 8, extra = n_tiles % 8;
     const int bid = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) +
                     slot;
@@ -114,68 +108,105 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
     const int gsize = min(n_tm - first_m, GROUP);
     const int tile_m = first_m + (bid % (GROUP * n_tn)) % gsize;
     const int tile_n = (bid % (GROUP * n_tn)) / gsize;
-    const int m0 = tile_m * TM;
-    const int n0 = tile_n * TN;
+    return {tile_m * TM, tile_n * TN};
+}
+
+__global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
+    __shared__ ProjStage stg[2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int G = lane >> 4;
+    const int wm = wave / 2;  // wavefront row (tokens)
+    const int wn = wave % 2;  // wavefront column (features)
+
+    const int n_tm = (a.M + TM - 1) / TM;
+    const int n_tn = (a.N + TN - 1) / TN;
+    const int n_tiles = n_tm * n_tn;
+    const int grid = (int)gridDim.x;
+    // This workgroup's tiles: virtual blocks blockIdx.x + t * grid.
+    const int ntl = (n_tiles - (int)blockIdx.x + grid - 1) / grid;
 
     const int K = a.K;
-    const int nk = (K + TK - 1) / TK;
-    // Buffer resources over this tile's rows (rows past M or N read zeros;
-    // columns past K read zeros because K is a multiple of 8 and each
-    // 16-byte chunk is either fully inside or fully outside).
-    const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(a.x + (int64_t)m0 * a.ldx, rows_bytes(m0, a.M, a.ldx, K));
-    const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(a.w + (int64_t)n0 * a.ldw, rows_bytes(n0, a.N, a.ldw, K));
+    const int nh = K / 32;           // 32-k halves (the host requires K % 32 == 0)
+    const int ns = (nh + 1) / 2;     // stages per tile
+    // Buffer resources over a tile's rows: rows past M or N read zeros.
+    // With K % 64 == 32 the last stage's second half reads the 64 bytes past
+    // K of each row (the next row's start, row padding, or zeros past the
+    // resource); its MFMAs are skipped.
+    auto rsrc_x = [&](int m0) {
+        return make_rsrc(a.x + (int64_t)m0 * a.ldx, rows_bytes(m0, a.M, a.ldx, K));
+    };
+    auto rsrc_w = [&](int n0) {
+        return make_rsrc(a.w + (int64_t)n0 * a.ldw, rows_bytes(n0, a.N, a.ldw, K));
+    };
 
-    // This lane's byte offsets for its copies (block c: rows 16 blk + l16,
-    // k offset 8 G within the chunk); the chunk adds 2 * TK * kk bytes.
-    uint32_t xoff[CPW], loff[CPW];
-    bool is_x[CPW];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        const int bi = PW * c + wave;
-        is_x[c] = bi < XBLK;
-        const int blk = is_x[c] ? bi : bi - XBLK;
-        const int row = 16 * blk + l16;
-        const int64_t ld = is_x[c] ? a.ldx : a.ldw;
-        // k positions past K are zero-filled by a second resource check:
-        // the chunk lies inside the row whenever 8 G + 32 kk < K.
-        xoff[c] = (uint32_t)(row * ld * 2 + 16 * G);
-        loff[c] = (uint32_t)(bi * 1024);
-    }
-    auto copy = [&](int kk, auto buf) __attribute__((always_inline)) {
-        const int kc = min(kk, nk - 1);
-        char *base = reinterpret_cast<char *>(&sbuf(buf));
+    // This lane's copies: copy c of wave w moves 8-row group g = PW c + w
+    // (of X for g < XGRP, then of W), row 8 g' + l / 8 of the operand, the
+    // 16-byte piece whose swizzled slot is l % 8, into 1 KiB of LDS per
+    // group, lane-linear.  The swizzle of row 8 g' + l / 8 is
+    // (l / 8) ^ (g' % 2) = (l / 8) ^ (w % 2) (PW is even), the same for
+    // every copy of the wave, so copies differ by the uniform 8 PW rows per
+    // copy: one per-lane offset per operand and scalar offsets.
+    static_assert(PW % 2 == 0, "swizzle of a copy group");
+    const int crow = 8 * wave + (lane >> 3);
+    const int cpiece = (lane & 7) ^ piece_swizzle(crow);
+    const uint32_t gx = (uint32_t)(crow * a.ldx * 2 + 16 * cpiece);
+    const uint32_t gw = (uint32_t)(crow * a.ldw * 2 + 16 * cpiece);
+    const uint32_t sx = (uint32_t)(8 * PW * a.ldx * 2);  // per copy
+    const uint32_t sw_ = (uint32_t)(8 * PW * a.ldw * 2);
+    // Copy stream: stage c_st of this workgroup's c_tile-th tile; past the
+    // last stage it copies the last stage again (in bounds, never used).
+    int c_tile = 0, c_st = 0;
+    Tile ct = tile_of((int)blockIdx.x, n_tm, n_tn);
+    __amdgpu_buffer_rsrc_t crx = rsrc_x(ct.m0), crw = rsrc_w(ct.n0);
+    auto copy_next = [&](int buf) __attribute__((always_inline)) {
+        char *base = reinterpret_cast<char *>(&stg[buf]);
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
-            // Columns k >= K are outside every row's data only at the last
-            // chunk; K % 32 == 0 is required by the host, so no chunk
-            // crosses the end of a row.
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_x[c] ? rx : rw,
-                                                     (lds_void *)(base + loff[c]), 16,
-                                                     (int)xoff[c], kc * TK * 2, 0, 0);
+            const int gi = PW * c + wave;
+            if (PW * c < XGRP)  // the same for every wave
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(crx, (lds_void *)(base + gi * 1024), 16,
+                                                         (int)gx, (int)(c * sx) + c_st * TK * 2,
+                                                         0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    crw, (lds_void *)(base + (int)sizeof(ProjStage::x) + (gi - XGRP) * 1024), 16,
+                    (int)gw, (int)((c - XGRP / PW) * sw_) + c_st * TK * 2, 0, 0);
+        }
+        if (c_st + 1 < ns) {
+            ++c_st;
+        } else if (c_tile + 1 < ntl) {
+            c_st = 0;
+            ++c_tile;
+            ct = tile_of((int)blockIdx.x + c_tile * grid, n_tm, n_tn);
+            crx = rsrc_x(ct.m0);
+            crw = rsrc_w(ct.n0);
         }
     };
 
     f32x4 acc[WN / 16][WM / 16];  // [feature tile][token tile], Y^T blocks
-#pragma unroll
-    for (int i = 0; i < WN / 16; ++i)
-#pragma unroll
-        for (int j = 0; j < WM / 16; ++j)
-            acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // Fragments of one chunk in registers.
+    // Fragment reads: lane l holds row l16 of a 16-row block, k offsets
+    // 8 G .. 8 G + 7 of a 32-k half h, i.e. piece 4 h + G of the row.  Rows
+    // of a block are 16-aligned, so the swizzle depends on l16 only.
+    const int sw = piece_swizzle(l16);
+    const int roff0 = l16 * 8 + ((0 + G) ^ sw);
+    const int roff1 = l16 * 8 + ((4 + G) ^ sw);
     struct Frags {
         bf16x8 w[WN / 16], x[WM / 16];
     };
-    auto read = [&](Frags &f, auto buf) __attribute__((always_inline)) {
-        const ProjStage &S = sbuf(buf);
+    auto read = [&](Frags &f, int buf, int ro) __attribute__((always_inline)) {
+        const u32x4 *S = &stg[buf].x[0][0];
+        const u32x4 *Wp = &stg[buf].w[0][0];
 #pragma unroll
         for (int i = 0; i < WN / 16; ++i)
-            f.w[i] = __builtin_bit_cast(bf16x8, S.w[wn * (WN / 16) + i][lane]);
+            f.w[i] = __builtin_bit_cast(bf16x8, Wp[(wn * WN + 16 * i) * 8 + ro]);
 #pragma unroll
         for (int j = 0; j < WM / 16; ++j)
-            f.x[j] = __builtin_bit_cast(bf16x8, S.x[wm * (WM / 16) + j][lane]);
+            f.x[j] = __builtin_bit_cast(bf16x8, S[(wm * WM + 16 * j) * 8 + ro]);
     };
     auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
 #pragma unroll
@@ -185,56 +216,77 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[i], f.x[j], acc[i][j], 0,
                                                                     0, 0);
     };
-    // Step kk (chunk kk in buffer kk % 4, its fragments already in `cur`):
-    // wait for this wave's copies of chunk kk + 1; the barrier then also
-    // means every wave is done with the buffer of chunk kk - 1, which the
-    // copy of chunk kk + 3 refills; read chunk kk + 1 into `nxt` and run
-    // the MFMAs of chunk kk.
-    auto step = [&](int kk, Frags &cur, Frags &nxt, auto buf) __attribute__((always_inline)) {
-        wait_copies<CPW>();
+
+    // Spread the first half's LDS reads between its 64 MFMAs, one read per
+    // 4 MFMAs: issued in one burst they fill the LDS command queue and stall
+    // the wave, and with one wave per SIMD the matrix core with it.
+    auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // First half of a stage (its fragments in `fa`): read the second half
+    // into `fb`, run, then wait for the next stage's copies; the barrier also
+    // means every wave is done with this stage's buffer, which the copy
+    // stream refills (the stage after next).
+    Frags fa, fb;
+    int buf = 0;  // buffer of the current stage
+    auto first_half = [&]() __attribute__((always_inline)) {
+        read(fb, buf, roff1);
+        mfmas(fa);
+        interleave();
+        wait_copies<0>();
         stage_barrier();
-        copy(kk + 3, SBuf<decltype(buf)::value + 3>{});
-        read(nxt, SBuf<decltype(buf)::value + 1>{});
-        if (kk < nk)
-            mfmas(cur);
     };
 
-    Frags fa, fb;
-    copy(0, SBuf<0>{});
-    copy(1, SBuf<1>{});
-    copy(2, SBuf<2>{});
-    wait_copies<2 * CPW>();  // chunk 0
+    copy_next(0);
+    copy_next(1);
+    wait_copies<CPW>();  // stage 0
     stage_barrier();
-    read(fa, SBuf<0>{});
-    // Four steps per iteration keep the buffer numbers compile-time; the
-    // fragment sets alternate.  Steps past the last chunk copy and read
-    // the last chunk again (in bounds) and skip their MFMAs.
-    for (int kk = 0; kk < nk; kk += 4) {
-        step(kk, fa, fb, SBuf<0>{});
-        step(kk + 1, fb, fa, SBuf<1>{});
-        step(kk + 2, fa, fb, SBuf<2>{});
-        step(kk + 3, fb, fa, SBuf<3>{});
-    }
-    wait_copies<0>();
-
-    // Y^T block (i, j): lane holds features 4 G .. 4 G + 3 of token l16.
+    read(fa, 0, roff0);
+    for (int t = 0; t < ntl; ++t) {
 #pragma unroll
-    for (int j = 0; j < WM / 16; ++j) {
-        const int m = m0 + wm * WM + 16 * j + l16;
-        if (m >= a.M)
-            continue;
-        uint16_t *yrow = a.y + (int64_t)m * a.ldy;
+        for (int i = 0; i < WN / 16; ++i)
 #pragma unroll
-        for (int i = 0; i < WN / 16; ++i) {
-            const int n = n0 + wn * WN + 16 * i + 4 * G;
-            if (n >= a.N)
+            for (int j = 0; j < WM / 16; ++j)
+                acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        // Second half: read the next stage's first half into `fa` (the next
+        // tile's, after a tile's last stage) and run; with K % 64 == 32 the
+        // last stage has no second half.  (The MFMAs stay in a block of their
+        // own: with the reads and copies in the same block the register
+        // allocator moves accumulators between register files.)
+        for (int st = 0; st < ns; ++st) {
+            first_half();
+            copy_next(buf);
+            buf ^= 1;
+            read(fa, buf, roff0);
+            if (2 * st + 1 < nh)
+                mfmas(fb);
+        }
+        // Y^T block (i, j): lane holds features 4 G .. 4 G + 3 of token l16.
+        const Tile tt = tile_of((int)blockIdx.x + t * grid, n_tm, n_tn);
+#pragma unroll
+        for (int j = 0; j < WM / 16; ++j) {
+            const int m = tt.m0 + wm * WM + 16 * j + l16;
+            if (m >= a.M)
                 continue;
-            const f32x4 c = acc[i][j];
-            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-            const bf16x4 h = __builtin_convertvector(c, bf16x4);
-            *reinterpret_cast<u32x2 *>(yrow + n) = __builtin_bit_cast(u32x2, h);
+            uint16_t *yrow = a.y + (int64_t)m * a.ldy;
+#pragma unroll
+            for (int i = 0; i < WN / 16; ++i) {
+                const int n = tt.n0 + wn * WN + 16 * i + 4 * G;
+                if (n >= a.N)
+                    continue;
+                const f32x4 c = acc[i][j];
+                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                const bf16x4 h = __builtin_convertvector(c, bf16x4);
+                *reinterpret_cast<u32x2 *>(yrow + n) = __builtin_bit_cast(u32x2, h);
+            }
         }
     }
+    wait_copies<0>();
 }
 
 }  // namespace
@@ -246,7 +298,19 @@ size_t proj_tiles(int M, int N) {
 hipError_t launch_proj(const ProjArgs &a, hipStream_t stream) {
     ProjArgs args = a;
     void *params[] = {&args};
-    const dim3 grid((unsigned)proj_tiles(a.M, a.N));
+    // One workgroup per compute unit (the kernel's LDS allows one), a
+    // multiple of 8 so that every workgroup stays on one XCD's tiles.
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    const size_t tiles = proj_tiles(a.M, a.N);
+    size_t g = tiles < (size_t)cus ? tiles : (size_t)cus;
+    if (g >= 8)
+        g -= g % 8;
+    const dim3 grid((unsigned)(g > 0 ? g : 1));
     return hipLaunchKernel(reinterpret_cast<const void *>(&parallax_proj_kernel), grid,
                            dim3(64 * PW), params, 0, stream);
 }

@@ -60,6 +60,22 @@ def test_projection_strided(orc):
     assert torch.isnan(yb[:, :8]).all() and torch.isnan(yb[:, 8 + N:]).all()
 
 
+@pytest.mark.parametrize("K", [32, 96])
+def test_projection_odd_k_ignores_row_padding(orc, K):
+    """K % 64 == 32: the last 64-k stage reads 32 k past K of every row (row
+    padding here, NaN) and must not use it."""
+    M, N = 300, 264
+    say("[case] projection odd K=%d with NaN row padding" % K)
+    xb = torch.full((M, K + 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wb = torch.full((N, K + 32), float("nan"), dtype=torch.bfloat16, device=DEV)
+    x, w = xb[:, :K], wb[:, :K]
+    x.copy_(workloads.random_tensor((M, K), 3101 + K).to(DEV))
+    w.copy_(workloads.random_tensor((N, K), 3102 + K, scale=K ** -0.5).to(DEV))
+    y = parallax_qkvr_project(x, w)
+    torch.cuda.synchronize()
+    check(orc, y, x, w, "projection odd K=%d" % K)
+
+
 def test_projection_full_size_sampled(orc):
     """The 1.7B-like layer: 2 x 8192 tokens, width 2048, 4 x 16 heads x 128;
     sampled token rows against the oracle."""
