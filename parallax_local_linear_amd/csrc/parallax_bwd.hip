@@ -51,7 +51,8 @@
 //     row-major k blocks the same way.
 //   * Row-major operands (q, rho, dO in the key kernel; k, v in the query
 //     kernel) are stored as one 16-byte fragment per lane, so each
-//     1 KiB block is read back at lane * 16.  All of a stage's blocks are
+//     1 KiB block is read back with one 16-byte read per lane (at a slot
+//     permuted so that the transpose reads are free of bank conflicts).  All of a stage's blocks are
 //     one contiguous record, copied with one buffer resource and a scalar
 //     offset per stage (no per-copy address arithmetic).
 //
@@ -128,8 +129,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint3
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)off, 0, 0, 0);
 }
 
+// Slot of a lane's 16-byte fragment piece within a 1 KiB operand block:
+// lanes 16..31 and 48..63 are stored with slot bits 2 and 3 flipped.  The
+// transpose reads below address, per 16-lane group, pieces of lanes
+// {4G .. 4G+3} and {16+4G .. 16+4G+3}; stored unswizzled those sit 256
+// bytes apart, in the same banks (a two-way conflict on every transpose
+// read); with the flip they fall on distinct banks for 128-byte and
+// 256-byte LDS cycles alike, and each 8 or 16 lanes of a row-major read
+// still cover every bank once.
+__device__ __forceinline__ int rec_slot(int lane) { return lane ^ (((lane >> 4) & 1) * 12); }
+
 __device__ __forceinline__ bf16x8 lds_frag(const u32x4 *block, int lane) {
-    return __builtin_bit_cast(bf16x8, block[lane]);
+    return __builtin_bit_cast(bf16x8, block[rec_slot(lane)]);
 }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
             const int row = 8 * G + e;
             const int blk = rm_block0 + (row / 16) * KC + fc / 4;
             const int lane = (row % 16) + 16 * (fc % 4);
-            *reinterpret_cast<u32x4 *>(rec + (size_t)blk * BLK + lane * 8) = in[e];
+            *reinterpret_cast<u32x4 *>(rec + (size_t)blk * BLK + rec_slot(lane) * 8) = in[e];
         }
     }
 }
@@ -269,14 +280,15 @@ struct KvStage {
 // therefore addresses row 16h + 4G + s/4, features 16 dt + 4 (s % 4) .. +3,
 // whose place in the fragment-order row-major blocks is
 //   block (h, dt / 2), lane (4G + s/4) + 16 (2 (dt % 2) + (s % 4) / 2),
-//   byte 8 ((s % 4) % 2) of its 16.
+//   byte 8 ((s % 4) % 2) of its 16 (stored at slot rec_slot(lane)).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 template <int KC>
 __device__ __forceinline__ bf16x8 lds_frag_t(const u32x4 (*blocks)[64], int dt, int lane) {
     const int G = lane >> 4, s = lane & 15;
     const int a4 = s & 3;
-    const int off = ((4 * G + (s >> 2)) + 16 * (2 * (dt & 1) + (a4 >> 1))) * 16 + 8 * (a4 & 1);
+    const int off =
+        rec_slot((4 * G + (s >> 2)) + 16 * (2 * (dt & 1) + (a4 >> 1))) * 16 + 8 * (a4 & 1);
     const char *b0 = reinterpret_cast<const char *>(&blocks[0 * KC + dt / 2][0]) + off;
     const char *b1 = reinterpret_cast<const char *>(&blocks[1 * KC + dt / 2][0]) + off;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(b0));
