@@ -14,10 +14,11 @@
 //   Y: bf16 [M, N] row-major, fp32 accumulation, rounded to nearest even
 //
 // Mapping onto CDNA4:
-//   * A workgroup computes a 256 x 256 tile of Y with 4 wavefronts (2 x 2),
-//     one per SIMD, each a 128 x 128 tile as 8 x 8 blocks of 16 x 16 (256
+//   * A workgroup computes a 256 x 256 tile of Y with 8 wavefronts (2 x 4),
+//     two per SIMD, each a 128 x 64 tile as 4 x 8 blocks of 16 x 16 (128
 //     accumulator registers), with v_mfma_f32_16x16x32_bf16 over 32-wide k
-//     chunks.  The product is taken transposed (Y^T = W X^T): a lane's
+//     chunks.  Two wavefronts per SIMD read LDS at about 1.4 times the rate
+//     of one, and each covers the other's waits.  The product is taken transposed (Y^T = W X^T): a lane's
 //     accumulator holds four consecutive output features of one token,
 //     stored as one 8-byte write.
 //   * Operands reach LDS in stages 64 k wide, copied directly from global
@@ -30,8 +31,8 @@
 //     fragment reads (16 rows x 16 bytes per 16 lanes) hit distinct banks.
 //   * The fragments of the next 32-k half are read into a second register
 //     set while the 64 MFMAs of the current half run, so LDS latency and
-//     the per-stage barrier hide behind the matrix cores; in a stage's first
-//     half the reads are spread between the MFMAs.
+//     the per-stage barrier hide behind the matrix cores; the reads are
+//     spread between the MFMAs.
 //   * Persistent: one workgroup per compute unit walks its tiles with one
 //     stream of stages across them, so the next tile's first stages are
 //     copied while the current tile's last ones run and its outputs are
@@ -49,15 +50,15 @@ namespace {
 constexpr int TM = 256;      // tokens per workgroup tile
 constexpr int TN = 256;      // output features per workgroup tile
 constexpr int TK = 64;       // k per stage (two 32-k halves)
-constexpr int PW = 4;        // wavefronts per workgroup
+constexpr int PW = 8;        // wavefronts per workgroup (2 x 4, two per SIMD)
 constexpr int WM = 128;      // tokens per wavefront tile
-constexpr int WN = 128;      // features per wavefront tile
+constexpr int WN = 64;       // features per wavefront tile
 constexpr int XGRP = TM / 8;  // 8-row copy groups of X per stage
 constexpr int WGRP = TN / 8;  // of W
 constexpr int CPW = (XGRP + WGRP) / PW;  // copies per wave per stage
 
 static_assert((XGRP + WGRP) % PW == 0 && XGRP % PW == 0, "copy split");
-static_assert(TM == 2 * WM && TN == 2 * WN, "2 x 2 wavefronts");
+static_assert(TM == 2 * WM && TN == 4 * WN, "2 x 4 wavefronts");
 
 // One stage: rows of 128 bytes (64 k), pieces swizzled as described above.
 struct ProjStage {
@@ -111,6 +112,8 @@ __device__ __forceinline__ Tile tile_of(int v, int n_tm, int n_tn) {
     return {tile_m * TM, tile_n * TN};
 }
 
+// ODD: K % 64 == 32 (each tile's last stage has one live half).
+template <bool ODD>
 __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
     __shared__ ProjStage stg[2];
 
@@ -119,8 +122,8 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int G = lane >> 4;
-    const int wm = wave / 2;  // wavefront row (tokens)
-    const int wn = wave % 2;  // wavefront column (features)
+    const int wm = wave / 4;  // wavefront row (tokens)
+    const int wn = wave % 4;  // wavefront column (features)
 
     const int n_tm = (a.M + TM - 1) / TM;
     const int n_tn = (a.N + TN - 1) / TN;
@@ -217,14 +220,13 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
                                                                     0, 0);
     };
 
-    // Spread the first half's LDS reads between its 64 MFMAs, one read per
-    // 4 MFMAs: issued in one burst they fill the LDS command queue and stall
-    // the wave, and with one wave per SIMD the matrix core with it.
+    // Spread a half's LDS reads between its MFMAs: issued in one burst they
+    // fill the LDS command queue and stall the wave.
     auto interleave = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < (WM + WN) / 16; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x008, (WM / 16) * (WN / 16) / ((WM + WN) / 16), 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -254,17 +256,25 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
             for (int j = 0; j < WM / 16; ++j)
                 acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
         // Second half: read the next stage's first half into `fa` (the next
-        // tile's, after a tile's last stage) and run; with K % 64 == 32 the
-        // last stage has no second half.  (The MFMAs stay in a block of their
-        // own: with the reads and copies in the same block the register
-        // allocator moves accumulators between register files.)
+        // tile's, after a tile's last stage) and run.  With K % 64 == 32 the
+        // last stage's second half lies past K: its fragments (whatever the
+        // bytes past K hold) are replaced by zeros, so it adds nothing.
         for (int st = 0; st < ns; ++st) {
             first_half();
+            if constexpr (ODD) {
+                const bool past_k = st == ns - 1;
+#pragma unroll
+                for (int i = 0; i < WN / 16; ++i)
+                    fb.w[i] = past_k ? bf16x8{} : fb.w[i];
+#pragma unroll
+                for (int j = 0; j < WM / 16; ++j)
+                    fb.x[j] = past_k ? bf16x8{} : fb.x[j];
+            }
             copy_next(buf);
             buf ^= 1;
             read(fa, buf, roff0);
-            if (2 * st + 1 < nh)
-                mfmas(fb);
+            mfmas(fb);
+            interleave();
         }
         // Y^T block (i, j): lane holds features 4 G .. 4 G + 3 of token l16.
         const Tile tt = tile_of((int)blockIdx.x + t * grid, n_tm, n_tn);
@@ -311,7 +321,9 @@ hipError_t launch_proj(const ProjArgs &a, hipStream_t stream) {
     if (g >= 8)
         g -= g % 8;
     const dim3 grid((unsigned)(g > 0 ? g : 1));
-    return hipLaunchKernel(reinterpret_cast<const void *>(&parallax_proj_kernel), grid,
+    const void *fn = (a.K % 64) ? reinterpret_cast<const void *>(&parallax_proj_kernel<true>)
+                                : reinterpret_cast<const void *>(&parallax_proj_kernel<false>);
+    return hipLaunchKernel(fn, grid,
                            dim3(64 * PW), params, 0, stream);
 }
 
