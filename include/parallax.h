@@ -173,6 +173,32 @@ parallax_status parallax_attn_fwd_noalloc(const void *q, const void *k, const vo
                                           int n_sink, void *stream);
 
 /*
+ * Causal prefill forward in fp32, for fp32 inputs: the same operation as
+ * parallax_attn_fwd (same visible set, scale, outputs), with every product,
+ * exponential and sum taken in fp32 (expf, logf) instead of bf16/f16
+ * matrix-core operands, so the inputs keep their fp32 precision (the bf16
+ * rounding of fp32 inputs alone moves o by about 0.07 on the tiny reference
+ * workload).  Against the exact result it is accurate to fp32 rounding
+ * (about 1e-5 relative).  It is untiled: O(L^2 d) arithmetic per head and
+ * one wavefront per query row, meant for small problems; large ones belong
+ * on parallax_attn_fwd.
+ *
+ *   q, k, v, r : fp32 [B, H, L, d] with strides sq, sk, sv, sr (element
+ *                strides >= 0; d contiguous; 4-byte aligned).
+ *   o          : fp32 [B, H, L, d] with strides so (4-byte aligned).
+ *   lse        : fp32 [B, H, L], contiguous (4-byte aligned).
+ *   B, H, L, d, softmax_scale, window, n_sink : as for parallax_attn_fwd.
+ *
+ * No workspace; one kernel on `stream`.  Errors as for parallax_attn_fwd.
+ */
+parallax_status parallax_attn_fwd_f32(const float *q, const float *k, const float *v,
+                                      const float *r, float *o, float *lse, int B, int H, int L,
+                                      int d, parallax_strides sq, parallax_strides sk,
+                                      parallax_strides sv, parallax_strides sr,
+                                      parallax_strides so, float softmax_scale, int window,
+                                      int n_sink, void *stream);
+
+/*
  * Causal prefill forward with two-part float16 weights: the same operation,
  * arguments, workspace and errors as parallax_attn_fwd, accurate to 2e-2
  * absolute for probe scores |rho_i . k_j| up to 256, eight times the range

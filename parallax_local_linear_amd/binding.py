@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "PARALLAX_OK", 1: "PARALLAX_ERR_INVALID_ARG",
 
 # Every symbol include/parallax.h declares.
 EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_attn_fwd_precise",
-            "parallax_attn_fwd_noalloc",
+            "parallax_attn_fwd_noalloc", "parallax_attn_fwd_f32",
             "parallax_attn_fwd_train",
             "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
             "parallax_attn_decode_paged", "parallax_qkvr_project", "parallax_hadamard_out",
@@ -69,6 +69,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                       f, i, i, vp, ctypes.c_size_t, vp]
     lib.parallax_attn_fwd_precise.restype = ctypes.c_int
     lib.parallax_attn_fwd_precise.argtypes = lib.parallax_attn_fwd.argtypes
+    lib.parallax_attn_fwd_f32.restype = ctypes.c_int
+    lib.parallax_attn_fwd_f32.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, S, S, S, S, S,
+                                          f, i, i, vp]
     lib.parallax_attn_fwd_noalloc.restype = ctypes.c_int
     lib.parallax_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, S, S, S, S, S,
                                               f, i, i, vp]
@@ -198,6 +201,36 @@ def parallax_attn_fwd_noalloc(q, k, v, r, *, softmax_scale=None, window=0, n_sin
     race for that workspace."""
     return _fwd("parallax_attn_fwd_noalloc", q, k, v, r, softmax_scale, window, n_sink, out, lse,
                 None, stream)
+
+
+@_stream_ordered
+def parallax_attn_fwd_f32(q, k, v, r, *, softmax_scale=None, window=0, n_sink=0, out=None,
+                          lse=None, stream=None):
+    """The prefill in fp32 throughout for fp32 inputs (untiled; small problems).
+    q, k, v, r: fp32 [B,H,L,d] -> (o fp32 [B,H,L,d], lse fp32 [B,H,L])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (r, "r")):
+        _need(t, n, torch.float32, 4)
+        if t.shape != q.shape:
+            raise ValueError("q, k, v and r must share one [B,H,L,d] shape")
+    B, H, L, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 4)
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(out.shape) != (B, H, L, d) or tuple(lse.shape) != (B, H, L):
+        raise ValueError("out / lse have the wrong shape")
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    st = load_library().parallax_attn_fwd_f32(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, H, L, d, _strides(q), _strides(k), _strides(v), _strides(r), _strides(out),
+        float(softmax_scale), int(window), int(n_sink), _stream_handle(q.device, stream))
+    _check(st)
+    return out, lse
 
 
 def _fwd(entry, q, k, v, r, softmax_scale, window, n_sink, out, lse, workspace, stream):

@@ -187,6 +187,18 @@ constexpr int fwd_waves(int) { return 8; }
 constexpr int fwd_block_rows(int d) { return 16 * fwd_waves(d); }
 
 hipError_t launch_fwd(const FwdArgs &a, int d, bool precise, hipStream_t stream);
+
+// fp32 prefill (parallax_attn_fwd_f32): fp32 tensors, element strides.
+struct F32Args {
+    const float *q, *k, *v, *r;
+    float *o, *lse;
+    int64_t q_b, q_h, q_l, k_b, k_h, k_l, v_b, v_h, v_l, r_b, r_h, r_l, o_b, o_h, o_l;
+    int B, H, L;
+    float scale;
+    int window, n_sink;
+};
+hipError_t launch_fwd_f32(const F32Args &a, int d, hipStream_t stream);
+int64_t fwd_f32_blocks(int B, int H, int L);
 hipError_t launch_bwd(const BwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_proj(const ProjArgs &a, hipStream_t stream);
 hipError_t launch_hadamard(const HadArgs &a, int log2n, hipStream_t stream);

@@ -150,6 +150,45 @@ parallax_status parallax_attn_fwd_noalloc(const void *q, const void *k, const vo
                       softmax_scale, window, n_sink, nullptr, 0, stream, false, false, true);
 }
 
+parallax_status parallax_attn_fwd_f32(const float *q, const float *k, const float *v,
+                                      const float *r, float *o, float *lse, int B, int H, int L,
+                                      int d, parallax_strides sq, parallax_strides sk,
+                                      parallax_strides sv, parallax_strides sr,
+                                      parallax_strides so, float softmax_scale, int window,
+                                      int n_sink, void *stream) {
+    if (B < 0 || H < 0 || L < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return PARALLAX_ERR_UNSUPPORTED;
+    if (!scale_ok(softmax_scale) || window < 0 || n_sink < 0)
+        return PARALLAX_ERR_INVALID_ARG;
+    if ((int64_t)B * H * L == 0)
+        return PARALLAX_OK;
+    if (!q || !k || !v || !r || !o || !lse)
+        return PARALLAX_ERR_INVALID_ARG;
+    if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(r, 4) || !aligned(o, 4) ||
+        !aligned(lse, 4))
+        return PARALLAX_ERR_INVALID_ARG;
+    for (const parallax_strides *s : {&sq, &sk, &sv, &sr, &so})
+        if (s->b < 0 || s->h < 0 || s->l < 0)
+            return PARALLAX_ERR_INVALID_ARG;
+    if (plx::fwd_f32_blocks(B, H, L) > INT_MAX)
+        return PARALLAX_ERR_UNSUPPORTED;
+    plx::F32Args a;
+    a.q = q; a.k = k; a.v = v; a.r = r; a.o = o; a.lse = lse;
+    a.q_b = sq.b; a.q_h = sq.h; a.q_l = sq.l;
+    a.k_b = sk.b; a.k_h = sk.h; a.k_l = sk.l;
+    a.v_b = sv.b; a.v_h = sv.h; a.v_l = sv.l;
+    a.r_b = sr.b; a.r_h = sr.h; a.r_l = sr.l;
+    a.o_b = so.b; a.o_h = so.h; a.o_l = so.l;
+    a.B = B; a.H = H; a.L = L;
+    a.scale = softmax_scale;
+    a.window = window;
+    a.n_sink = n_sink;
+    hipError_t e = plx::launch_fwd_f32(a, d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
 parallax_status parallax_attn_fwd_precise(const void *q, const void *k, const void *v,
                                           const void *r, float *o, float *lse, int B, int H,
                                           int L, int d, parallax_strides sq, parallax_strides sk,

@@ -410,3 +410,23 @@ def test_fwd_noalloc_empty_problem_is_a_no_op(lib):
 def test_fwd_noalloc_limit_is_the_headline_size():
     """The 2 x 16 x 8192 x 128 workload's workspace fills the 64 MiB + 256 array."""
     assert expected_workspace(2, 16, 8192, 128) == (64 << 20) + 256
+
+
+def fwd_f32(lib, q=A16, k=A16, v=A16, r=A16, o=A16, lse=A16, B=1, H=2, L=64, d=64,
+            sq=CONTIG, sk=CONTIG, sv=CONTIG, sr=CONTIG, so=CONTIG, scale=0.125, window=0,
+            n_sink=0):
+    return lib.parallax_attn_fwd_f32(q, k, v, r, o, lse, B, H, L, d, sq, sk, sv, sr, so, scale,
+                                     window, n_sink, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(L=-1), INVALID), (dict(r=None), INVALID),
+    (dict(lse=None), INVALID), (dict(o=A16 + 2), INVALID), (dict(n_sink=-1), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(sv=S(-64, 64, 64)), INVALID),
+])
+def test_fwd_f32_rejects(lib, kw, status):
+    assert fwd_f32(lib, **kw) == status
+
+
+def test_fwd_f32_empty_problem_is_a_no_op(lib):
+    assert fwd_f32(lib, H=0, q=None, k=None, v=None, r=None, o=None, lse=None) == OK
