@@ -93,6 +93,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--settle", type=int, default=25,
+                   help="untimed steps before the warm-up steps: the GPU's clock settles over "
+                        "the first 15-20 calls (the prefill runs up to 25%% slower on calls "
+                        "3-15 than from call 20 on); reported as settle_steps")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (profiling runs)")
     p.add_argument("--cpu-sample-heads", type=int, default=16,
@@ -592,8 +596,9 @@ def main():
         if events is not None:
             events[2].record(stream)
 
-    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    print("[bench] settle %d, warmup %d" % (args.settle, args.warmup), file=sys.stderr,
+          flush=True)
+    for _ in range(args.settle + args.warmup):
         step()
     torch.cuda.synchronize()
 
@@ -628,6 +633,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": args.settle,
         "ms_per_step": round(total_ms / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
