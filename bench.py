@@ -70,6 +70,7 @@ KERNEL_SOURCES = {
     "hadamard": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_hadamard.hip"),
     "based": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_based.hip"),
     "prefill_0.6b": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_fwd.hip"),
+    "precise": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_fwd.hip"),
     "local_swa128_sink4": os.path.join(ROOT, "parallax_local_linear_amd", "csrc",
                                        "parallax_fwd.hip"),
 }
@@ -254,7 +255,7 @@ def time_prefill_leg(cfg, bound, runs, warmup, stream, flush=None, precise=False
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
                 "algorithmic_flop_per_launch": flops}
-    roof["traffic"] = None if precise else measured_traffic(cfg.name)
+    roof["traffic"] = measured_traffic("precise" if precise else cfg.name)
     roof["kernel"] = PREFILL_KERNELS[cfg.name]
     if precise:
         roof["kernel"] = (roof["kernel"].replace("parallax_attn_fwd call",
