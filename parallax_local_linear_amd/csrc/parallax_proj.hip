@@ -30,9 +30,11 @@
 //     (piece c of row r at slot c ^ (r % 8) ^ ((r / 8) % 2)), so the
 //     fragment reads (16 rows x 16 bytes per 16 lanes) hit distinct banks.
 //   * The fragments of the next 32-k half are read into a second register
-//     set while the 64 MFMAs of the current half run, so LDS latency and
-//     the per-stage barrier hide behind the matrix cores; the reads are
-//     spread between the MFMAs.
+//     set while the MFMAs of the current half run, so LDS latency and the
+//     per-stage barrier hide behind the matrix cores.  A half runs in four
+//     fenced chunks, each a few fragment reads (and, in a second half, two
+//     copies) followed by 8 MFMAs, so reads and copies leave spread over
+//     the half instead of in one burst.
 //   * Persistent: one workgroup per compute unit walks its tiles with one
 //     stream of stages across them, so the next tile's first stages are
 //     copied while the current tile's last ones run and its outputs are
@@ -165,20 +167,18 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
     int c_tile = 0, c_st = 0;
     Tile ct = tile_of((int)blockIdx.x, n_tm, n_tn);
     __amdgpu_buffer_rsrc_t crx = rsrc_x(ct.m0), crw = rsrc_w(ct.n0);
-    auto copy_next = [&](int buf) __attribute__((always_inline)) {
+    auto copy_one = [&](int buf, int c) __attribute__((always_inline)) {
         char *base = reinterpret_cast<char *>(&stg[buf]);
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const int gi = PW * c + wave;
-            if (PW * c < XGRP)  // the same for every wave
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(crx, (lds_void *)(base + gi * 1024), 16,
-                                                         (int)gx, (int)(c * sx) + c_st * TK * 2,
-                                                         0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    crw, (lds_void *)(base + (int)sizeof(ProjStage::x) + (gi - XGRP) * 1024), 16,
-                    (int)gw, (int)((c - XGRP / PW) * sw_) + c_st * TK * 2, 0, 0);
-        }
+        const int gi = PW * c + wave;
+        if (PW * c < XGRP)  // the same for every wave
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(crx, (lds_void *)(base + gi * 1024), 16,
+                                                     (int)gx, (int)(c * sx) + c_st * TK * 2, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                crw, (lds_void *)(base + (int)sizeof(ProjStage::x) + (gi - XGRP) * 1024), 16,
+                (int)gw, (int)((c - XGRP / PW) * sw_) + c_st * TK * 2, 0, 0);
+    };
+    auto copy_advance = [&]() __attribute__((always_inline)) {
         if (c_st + 1 < ns) {
             ++c_st;
         } else if (c_tile + 1 < ntl) {
@@ -188,6 +188,12 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
             crx = rsrc_x(ct.m0);
             crw = rsrc_w(ct.n0);
         }
+    };
+    auto copy_next = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+            copy_one(buf, c);
+        copy_advance();
     };
 
     f32x4 acc[WN / 16][WM / 16];  // [feature tile][token tile], Y^T blocks
@@ -211,37 +217,48 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
         for (int j = 0; j < WM / 16; ++j)
             f.x[j] = __builtin_bit_cast(bf16x8, S[(wm * WM + 16 * j) * 8 + ro]);
     };
-    auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < WN / 16; ++i)
-#pragma unroll
-            for (int j = 0; j < WM / 16; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[i], f.x[j], acc[i][j], 0,
-                                                                    0, 0);
+    // A half in WN / 16 chunks: chunk i runs the MFMAs of feature block i
+    // with the reads of one W and two X fragments of the other register set
+    // (and, in a second half, two of the copies of the stage after next)
+    // placed before them, each chunk fenced, so reads and copies spread over
+    // the half instead of leaving in one burst.
+    static_assert(WM / 16 == 2 * (WN / 16) && CPW == 2 * (WN / 16), "chunk split");
+    auto chunk_reads = [&](Frags &f, int b, int ro, int i) __attribute__((always_inline)) {
+        const u32x4 *S = &stg[b].x[0][0];
+        const u32x4 *Wp = &stg[b].w[0][0];
+        f.w[i] = __builtin_bit_cast(bf16x8, Wp[(wn * WN + 16 * i) * 8 + ro]);
+        f.x[2 * i] = __builtin_bit_cast(bf16x8, S[(wm * WM + 32 * i) * 8 + ro]);
+        f.x[2 * i + 1] = __builtin_bit_cast(bf16x8, S[(wm * WM + 32 * i + 16) * 8 + ro]);
     };
-
-    // Spread a half's LDS reads between its MFMAs: issued in one burst they
-    // fill the LDS command queue and stall the wave.
-    auto interleave = [&]() __attribute__((always_inline)) {
+    auto chunk_mfmas = [&](const Frags &f, int i) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < (WM + WN) / 16; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, (WM / 16) * (WN / 16) / ((WM + WN) / 16), 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < WM / 16; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[i], f.x[j], acc[i][j], 0, 0, 0);
     };
-    // First half of a stage (its fragments in `fa`): read the second half
-    // into `fb`, run, then wait for the next stage's copies; the barrier also
-    // means every wave is done with this stage's buffer, which the copy
-    // stream refills (the stage after next).
     Frags fa, fb;
     int buf = 0;  // buffer of the current stage
     auto first_half = [&]() __attribute__((always_inline)) {
-        read(fb, buf, roff1);
-        mfmas(fa);
-        interleave();
+#pragma unroll
+        for (int i = 0; i < WN / 16; ++i) {
+            chunk_reads(fb, buf, roff1, i);
+            chunk_mfmas(fa, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         wait_copies<0>();
         stage_barrier();
+    };
+    auto second_half = [&]() __attribute__((always_inline)) {
+        const int old = buf;
+        buf ^= 1;
+#pragma unroll
+        for (int i = 0; i < WN / 16; ++i) {
+            copy_one(old, 2 * i);
+            copy_one(old, 2 * i + 1);
+            chunk_reads(fa, buf, roff0, i);
+            chunk_mfmas(fb, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        copy_advance();
     };
 
     copy_next(0);
@@ -270,11 +287,7 @@ __global__ __launch_bounds__(64 * PW) void parallax_proj_kernel(ProjArgs a) {
                 for (int j = 0; j < WM / 16; ++j)
                     fb.x[j] = past_k ? bf16x8{} : fb.x[j];
             }
-            copy_next(buf);
-            buf ^= 1;
-            read(fa, buf, roff0);
-            mfmas(fb);
-            interleave();
+            second_half();
         }
         // Y^T block (i, j): lane holds features 4 G .. 4 G + 3 of token l16.
         const Tile tt = tile_of((int)blockIdx.x + t * grid, n_tm, n_tn);
