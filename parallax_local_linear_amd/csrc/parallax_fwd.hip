@@ -494,19 +494,35 @@ __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
         if (s >= a.n_st)
             continue;
         uint16_t *dst = a.vt + ((int64_t)bh * a.n_st + s) * (D * BN);
+        u32x4 out[8];
 #pragma unroll
         for (int cf = 0; cf < 8; ++cf) {
             // Feature 8fg+cf at positions 8G .. 8G+7: half cf%2 of word cf/2
             // of keys k = 0..7.
-            u32x4 out;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const uint32_t lo = hv[2 * pp][cf / 2], hi = hv[2 * pp + 1][cf / 2];
-                out[pp] = (cf & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                   : ((lo & 0xffffu) | (hi << 16));
+                out[cf][pp] = (cf & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                                       : ((lo & 0xffffu) | (hi << 16));
             }
-            const int f = 8 * fg + cf;
-            *reinterpret_cast<u32x4 *>(dst + vswz_slot(f, G) * 8) = out;
+        }
+        // Feature rows 2m and 2m+1 (64 bytes each) share a 128-byte line.
+        // Lanes fg and fg ^ 1 (adjacent lanes) trade one chunk per row pair,
+        // so that each store instruction writes whole lines: the first of a
+        // pair writes rows 8F + c and 8F + c + 1 of even F (lane F its own
+        // row, lane F + 1 the one it received), the second those of odd F.
+        const int e = fg & 1;
+#pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+            const u32x4 send = e ? out[c] : out[c + 1];
+            u32x4 recv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                recv[i] = (uint32_t)__shfl_xor((int)send[i], 1, 64);
+            const int fa = e ? 8 * (fg - 1) + c + 1 : 8 * fg + c;
+            const int fb = e ? 8 * fg + c + 1 : 8 * (fg + 1) + c;
+            *reinterpret_cast<u32x4 *>(dst + vswz_slot(fa, G) * 8) = e ? recv : out[c];
+            *reinterpret_cast<u32x4 *>(dst + vswz_slot(fb, G) * 8) = e ? out[c + 1] : recv;
         }
     }
 }
