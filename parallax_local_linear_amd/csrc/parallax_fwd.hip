@@ -991,6 +991,60 @@ __device__ __forceinline__ void vblock_store(uint16_t *sv, const u32x2 (&raw)[8]
     }
 }
 
+// One pass over the stages of a wavefront in the common case of a window of
+// NW stages: its 16 rows lie inside the sequence and past the window's start,
+// so the stage list is always the diagonal stage (each row sees the keys up
+// to itself), NW - 2 stages every row sees in full, the window's oldest
+// stage (each row sees the keys from row - W + 1 on) and, with SINK, the
+// sink stage.  Every stage's kind and ring slot are then known at compile
+// time: the pass is straight-line code (the same software pipeline as the
+// general stage loop, without its branches, the register copies at their
+// joins and the waits for loads a branch might have skipped), and a stage's
+// mask is one per-lane threshold on the key offset 16 kt + e.
+template <int D, bool PRECISE, int NW, bool SINK>
+__device__ __forceinline__ void window_pass(Ctx<D> &cx, VFrags<D> &vf, Weights<PRECISE> &pw,
+                                            const StageBuf<D> *ring, const StageBuf<D> &sinkbuf,
+                                            int hi_w, const FragAddr<D> &fa, int t_diag,
+                                            int t_edge, int t_sink, float c) {
+    static_assert(NW >= 3 && (WRING & (WRING - 1)) == 0, "window stages, ring slots");
+    constexpr int NST = NW + (SINK ? 1 : 0);
+    // Window stage hi_w - u (hi_w >= u here), or the sinks.
+    auto buf = [&](int u) -> const StageBuf<D> & {
+        return u < NW ? ring[(hi_w - u) & (WRING - 1)] : sinkbuf;
+    };
+    KFrags<D> kf[2];
+    Scores sc[2];
+    read_kfrags<D>(kf[0], buf(0).k, fa);
+    read_kfrags<D>(kf[1], buf(1).k, fa);
+    score_mfmas<D>(cx, kf[0], sc[0]);
+    read_kfrags<D>(kf[0], buf(2).k, fa);
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+        Scores &cur = sc[u & 1];
+        read_vfrags<D>(vf, buf(u).v, fa);
+        // The V^T reads go first: the value MFMAs at the step's end wait
+        // for them.
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < NST)
+            score_mfmas<D>(cx, kf[(u + 1) & 1], sc[(u + 1) & 1]);
+        if (u + 3 < NST)
+            read_kfrags<D>(kf[(u + 1) & 1], buf(u + 3).k, fa);
+        if (u == 0)
+            mask_range(cur, INT32_MIN / 2, t_diag);
+        else if (u == NW - 1)
+            mask_range(cur, t_edge, INT32_MAX / 2);
+        else if (u == NW)
+            mask_range(cur, INT32_MIN / 2, t_sink);
+        if (u == 0)
+            init_offsets<D>(cx, cur, c);
+        weights<D, PRECISE>(cx, cur, pw, c);
+        value_mfmas<D, PRECISE>(cx, vf, pw);
+        // Steps stay in order, so that later stages' reads are not hoisted
+        // into this one (their registers would overlap the live ones).
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int D, bool STATS, bool PRECISE>
 __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window_kernel(FwdArgs a) {
     using C = Cfg<D>;
@@ -1165,8 +1219,8 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
         // This wavefront's rows: the diagonal stage first, then older window
         // stages, then the sink stage when it lies before the window.
         const int i0w = m * WROWS + ROWS * wave;
+        const int row = i0w + l16;
         if (i0w < L) {
-            const int row = i0w + l16;
             const int lo_w = i0w - window + 1 > 0 ? (i0w - window + 1) / BN : 0;
             const int hi_w = min(i0w + ROWS - 1, L - 1) / BN;
             const int n_win = hi_w - lo_w + 1;
@@ -1174,7 +1228,36 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
             cx.m_ref = kNegInf;
             cx.msub = 0.f;
             cx.xlane = kNegInf;
-            for (int pass = 0; pass < 2; ++pass) {
+            // The common case takes the straight-line pass; the general stage
+            // loop below covers the other tiles and the recomputation.
+            int pass0 = 0;
+            const int nw = !PRECISE && window == 128 && n_sink > 0 ? 5 : 0;
+            if (nw > 0 && n_win == nw && lo_w > 0 && i0w + ROWS <= L) {
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    cx.accA[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    cx.accC[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                }
+                cx.accL = (f32x4){0.f, 0.f, 0.f, 0.f};
+                cx.accS = (f32x4){0.f, 0.f, 0.f, 0.f};
+                // Key offsets 16 kt + e visible to this lane's row: at most
+                // t_diag in the diagonal stage, at least t_edge in the oldest
+                // window stage, at most t_sink among the sinks.
+                const int t_diag = row - hi_w * BN - 4 * G;
+                const int t_edge = row - (hi_w - nw + 1) * BN - 4 * G - window + 1;
+                const int t_sink = n_sink - 1 - 4 * G;
+                window_pass<D, PRECISE, 5, true>(cx, vf, pw, ring, sinkbuf, hi_w, fa,
+                                                 t_diag, t_edge, t_sink, c);
+                const float xmax = row_max4(cx.xlane);
+                if (__builtin_amdgcn_ballot_w64(xmax * c > cx.m_ref + kTauHi) == 0) {
+                    pass0 = 2;
+                } else {
+                    cx.m_ref = xmax * c;
+                    cx.msub = cx.m_ref == kNegInf ? 0.f : cx.m_ref;
+                    pass0 = 1;
+                }
+            }
+            for (int pass = pass0; pass < 2; ++pass) {
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
                     cx.accA[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -1241,37 +1324,6 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
                 cx.m_ref = xmax * c;
                 cx.msub = cx.m_ref == kNegInf ? 0.f : cx.m_ref;
             }
-
-            const float ell_t = cx.accL[0];
-            const float s_t = cx.accS[0];
-            if (row < L) {
-                const float inv = 1.f / ell_t;
-                const float keep = 1.f - s_t * inv;
-                float *ob = a.o + (int64_t)b * a.o_b + (int64_t)h * a.o_h + (int64_t)row * a.o_l;
-#pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt) {
-                    f32x4 out;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        out[e] = (cx.accA[dt][e] * keep + cx.accC[dt][e]) * inv;
-                    *reinterpret_cast<f32x4 *>(ob + 16 * dt + 4 * G) = out;
-                }
-                if (G == 0)
-                    a.lse[(int64_t)bh * L + row] = (cx.m_ref + log2f(ell_t)) * kLn2;
-                if constexpr (STATS) {
-                    float *pb = a.pv + ((int64_t)bh * L + row) * D;
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt) {
-                        f32x4 out;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            out[e] = cx.accA[dt][e] * inv;
-                        *reinterpret_cast<f32x4 *>(pb + 16 * dt + 4 * G) = out;
-                    }
-                    if (G == 0)
-                        a.sbar[(int64_t)bh * L + row] = s_t * inv;
-                }
-            }
         }
 
         if (more) {
@@ -1291,6 +1343,42 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
             for (int kc = 0; kc < C::KC; ++kc) {
                 cx.qf[kc] = qn[kc];
                 cx.rf[kc] = rn[kc];
+            }
+        }
+        // This tile's output goes out only now, after the wait for the
+        // prefetched loads above: vmcnt counts stores as well, so stores
+        // issued before that wait would hold every wavefront at the tile's
+        // end until they are acknowledged.  Issued here, they drain while the
+        // next tile is computed.
+        __builtin_amdgcn_sched_barrier(0);
+        if (i0w < L && row < L) {
+            const float ell_t = cx.accL[0];
+            const float s_t = cx.accS[0];
+            const float inv = 1.f / ell_t;
+            const float keep = 1.f - s_t * inv;
+            float *ob = a.o + (int64_t)b * a.o_b + (int64_t)h * a.o_h + (int64_t)row * a.o_l;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                f32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    out[e] = (cx.accA[dt][e] * keep + cx.accC[dt][e]) * inv;
+                *reinterpret_cast<f32x4 *>(ob + 16 * dt + 4 * G) = out;
+            }
+            if (G == 0)
+                a.lse[(int64_t)bh * L + row] = (cx.m_ref + log2f(ell_t)) * kLn2;
+            if constexpr (STATS) {
+                float *pb = a.pv + ((int64_t)bh * L + row) * D;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    f32x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        out[e] = cx.accA[dt][e] * inv;
+                    *reinterpret_cast<f32x4 *>(pb + 16 * dt + 4 * G) = out;
+                }
+                if (G == 0)
+                    a.sbar[(int64_t)bh * L + row] = s_t * inv;
             }
         }
         __syncthreads();

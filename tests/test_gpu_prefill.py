@@ -286,6 +286,8 @@ WINDOW_CASES = [
     (1, 1, 65, 64, 64, 4),
     (1, 1, 31, 128, 128, 4),
     (3, 2, 300, 64, 128, 32),
+    (1, 2, 1000, 64, 128, 1),
+    (1, 2, 700, 128, 128, 32),
 ]
 
 
@@ -295,6 +297,15 @@ def test_window_kernel_shapes(orc, B, H, L, d, window, n_sink):
     q, k, v, r = (rand((B, H, L, d), seed + t) for t in range(4))
     full_check(orc, q, k, v, r, window=window, n_sink=n_sink,
                what="window kernel B%d H%d L%d d%d" % (B, H, L, d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_kernel_rising_scores(orc, d):
+    """Keys whose scores rise along the sequence make most wavefronts of the
+    windowed kernel recompute their rows with exact offsets, after the first
+    pass took the window's common-case schedule."""
+    q, k, v, r = workloads.rising_inputs(1, 2, 1000, d, seed=91 + d)
+    full_check(orc, q, k, v, r, window=128, n_sink=4, what="window kernel rising d%d" % d)
 
 
 @pytest.mark.parametrize("rising", [False, True], ids=["normal", "rising"])
