@@ -80,10 +80,9 @@ PREFILL_KERNELS = {
                          "parallax_fwd_kernel<128, true, false, false>",
     "prefill_0.6b": "parallax_attn_fwd call = parallax_vprep_kernel<64> + "
                     "parallax_fwd_kernel<64, true, false, false>",
-    "local_swa128_sink4": "parallax_attn_fwd call = parallax_vprep_kernel<64> + "
-                          "parallax_fwd_kernel<64, true, false, false>",
+    "local_swa128_sink4": "parallax_attn_fwd call = parallax_fwd_window_kernel<64, false, false>",
 }
-FLUSH_BYTES = 512 << 20     # overwritten between timed calls: more than L2 + the 256 MB MALL
+FLUSH_BYTES = 512 << 20     # flush buffers between timed calls: more than L2 + the 256 MB MALL
 # Legs timed after the steps, each reported under its own key.
 SECONDARY_LEGS = ("decode_paged", "projection", "hadamard", "based", "backward", "prefill_0.6b",
                   "local_swa128_sink4", "precise", "rising")
@@ -197,11 +196,32 @@ def cpu_baseline(cfg, n_heads: int, single_cfg, single_heads: int):
                              flops1 / 1e9, dt1)}}
 
 
-def time_each_call(fn, runs, warmup, stream, flush=None):
+class CacheFlush:
+    """Evicts a call's inputs from L2 and the MALL between timed calls.
+
+    `clean` (the default) overwrites one 512 MB buffer, which evicts
+    everything else, then reads a second one, which displaces the first
+    one's dirty lines: the timed call starts with its inputs in HBM and
+    caches that hold no dirty data.  `dirty` only overwrites the buffer, so
+    the timed call also pays for writing 256 MB of the flush's own lines
+    back to HBM as its reads evict them."""
+
+    def __init__(self, dev):
+        import torch
+        self.a = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.b = torch.zeros(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+        self.total = None
+
+    def __call__(self, i, dirty=False):
+        self.a.fill_(i & 0xff)
+        if not dirty:
+            self.total = self.b.sum()
+
+
+def time_each_call(fn, runs, warmup, stream, flush=None, dirty=False):
     """Per-call times (ms) from HIP events recorded on `stream` around each
-    call; with `flush` (a device byte tensor), the tensor is overwritten on
-    the same stream before every call, outside the timed region, so that the
-    call starts with its inputs out of L2 and the MALL."""
+    call; with `flush` (a CacheFlush), the caches are flushed on the same
+    stream before every call, outside the timed region."""
     import torch
     for _ in range(warmup):
         fn()
@@ -210,7 +230,7 @@ def time_each_call(fn, runs, warmup, stream, flush=None):
     for i in range(runs):
         if flush is not None:
             with torch.cuda.stream(stream):
-                flush.fill_(i & 0xff)
+                flush(i, dirty)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -239,10 +259,10 @@ def time_prefill_leg(cfg, bound, runs, warmup, stream, flush=None, precise=False
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, parallax_attn_fwd_workspace_size(cfg.B, cfg.H, cfg.L, cfg.d)),
                      dtype=torch.uint8, device=dev)
-    times = time_each_call(
-        lambda: fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,
-                    workspace=ws, stream=stream),
-        runs, warmup, stream, flush)
+    call = lambda: fwd(q, k, v, r, window=cfg.window, n_sink=cfg.n_sink, out=o, lse=lse,  # noqa: E731
+                       workspace=ws, stream=stream)
+    times = time_each_call(call, runs, warmup, stream, flush)
+    dirty = time_each_call(call, runs, 0, stream, flush, dirty=True) if flush else None
     med = statistics.median(times)
     flops = accounting.prefill_flops(cfg)
     nbytes = accounting.prefill_bytes(cfg)
@@ -261,12 +281,18 @@ def time_prefill_leg(cfg, bound, runs, warmup, stream, flush=None, precise=False
         roof["kernel"] = (roof["kernel"].replace("parallax_attn_fwd call",
                                                  "parallax_attn_fwd_precise call")
                           .replace("false, false>", "false, true>"))
-    return {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "L": cfg.L, "d": cfg.d,
-            "window": cfg.window, "n_sink": cfg.n_sink,
-            "ms_median": round(med, 4), "ms_min": round(min(times), 4), "runs": runs,
-            "mall_flush": flush is not None,
-            "value": roof["achieved"], "unit": roof["unit"],
-            "tflops": round(tflops, 2), "gbs": round(gbs, 1), "roofline": roof}
+    out = {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "L": cfg.L, "d": cfg.d,
+           "window": cfg.window, "n_sink": cfg.n_sink,
+           "ms_median": round(med, 4), "ms_min": round(min(times), 4), "runs": runs,
+           "mall_flush": flush is not None,
+           "value": roof["achieved"], "unit": roof["unit"],
+           "tflops": round(tflops, 2), "gbs": round(gbs, 1), "roofline": roof}
+    if flush:
+        out["flush"] = ("512 MB written, then another 512 MB read, before each call "
+                        "(inputs out of L2 and the MALL, no dirty lines left)")
+        out["ms_median_dirty_flush"] = round(statistics.median(dirty), 4)
+        out["ms_min_dirty_flush"] = round(min(dirty), 4)
+    return out
 
 
 def recomputed_tiles(ws, cfg):
@@ -705,7 +731,7 @@ def main():
     if "backward" in legs:
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         res["backward"] = time_backward(pcfg, few, warm, stream)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(dev)
     if "prefill_0.6b" in legs:
         print("[bench] timing the 0.6B-like prefill", file=sys.stderr, flush=True)
         res["prefill_0.6b"] = time_prefill_leg(workloads.PREFILL_06B, "mfma", 20, 5, stream,
