@@ -1125,6 +1125,31 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
     Ctx<D> cx;
     load_qr(cx.qf, cx.rf, m_first);
 
+    // The next tile's loads go through resources that move by a fixed number
+    // of rows per tile (two K/V stages, 64 Q/R rows): a pointer and the bytes
+    // left to the slice's last element, advanced by one addition each,
+    // instead of 64-bit products of row indices and strides for five
+    // resources at every tile.  A stream whose first row is past L has no
+    // bytes, so its rows read as zeros, as with rows_bytes.
+    struct RowStream {
+        const char *p;
+        int64_t rem;
+    };
+    auto stream_at = [&](const uint16_t *base, int64_t ld, int row) -> RowStream {
+        return {reinterpret_cast<const char *>(base + (int64_t)row * ld),
+                ((int64_t)L - 1 - row) * ld * 2 + 2 * D};
+    };
+    auto stream_rsrc = [&](const RowStream &st, int row) {
+        const uint32_t n = row >= L || st.rem <= 0 ? 0u
+                           : st.rem >= 0xffffffffll ? 0xffffffffu
+                                                    : (uint32_t)st.rem;
+        return make_rsrc(st.p, n);
+    };
+    const int kv_row0 = (st_last(m_first) + 1) * BN;
+    const int qr_row0 = (m_first + 1) * WROWS + ROWS * wave;
+    RowStream ks = stream_at(kb, a.k_l, kv_row0), vs = stream_at(vb, a.v_l, kv_row0);
+    RowStream qs = stream_at(qb, a.q_l, qr_row0), rs = stream_at(rb, a.r_l, qr_row0);
+
     // The first tile's stages (at most WPRO) and the sink stage, every load
     // issued before the first LDS write.
     {
@@ -1202,18 +1227,39 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
         const int new_lo = st_last(m) + 1;
         const int n_new = more ? st_last(m + 1) - st_last(m) : 0;
         if (more) {
+            // Stage new_lo + u is u * BN rows into the K stream (new_lo is
+            // 2 (m + 1) here: tile m is not the sequence's last).
+            const int kv_row = new_lo * BN;
+            const __amdgpu_buffer_rsrc_t rk = stream_rsrc(ks, kv_row);
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(kb, 0u);
 #pragma unroll
-            for (int u = 0; u < WNEW; ++u) {
-                const __amdgpu_buffer_rsrc_t rk =
-                    u < n_new ? stage_rsrc(kb, a.k_l, new_lo + u) : make_rsrc(kb, 0u);
+            for (int u = 0; u < WNEW; ++u)
 #pragma unroll
                 for (int ch = 0; ch < KCH; ++ch)
-                    kpre[u][ch] = bufld16(rk, koff[ch]);
-            }
+                    kpre[u][ch] = __builtin_amdgcn_raw_buffer_load_b128(
+                        u < n_new ? rk : rz, (int)koff[ch], (int)(u * BN * a.k_l * 2), 0);
             if (v_role && vu < n_new)
-                vblock_load(vpre, stage_rsrc(vb, a.v_l, new_lo), a.v_l, vu * BN, vblk / FG,
-                            vblk % FG);
-            load_qr(qn, rn, m + 1);
+                vblock_load(vpre, stream_rsrc(vs, kv_row), a.v_l, vu * BN, vblk / FG, vblk % FG);
+            const int qr_row = (m + 1) * WROWS + ROWS * wave;
+            const __amdgpu_buffer_rsrc_t rq = stream_rsrc(qs, qr_row);
+            const __amdgpu_buffer_rsrc_t rr = stream_rsrc(rs, qr_row);
+#pragma unroll
+            for (int kc = 0; kc < C::KC; ++kc) {
+                const uint32_t col = (32 * kc + 8 * G) * 2;
+                qn[kc] = __builtin_bit_cast(bf16x8, bufld16(rq, (uint32_t)(l16 * a.q_l * 2) + col));
+                rn[kc] = __builtin_bit_cast(bf16x8, bufld16(rr, (uint32_t)(l16 * a.r_l * 2) + col));
+            }
+        }
+        {
+            const int64_t rows = WROWS;
+            ks.p += rows * a.k_l * 2;
+            ks.rem -= rows * a.k_l * 2;
+            vs.p += rows * a.v_l * 2;
+            vs.rem -= rows * a.v_l * 2;
+            qs.p += rows * a.q_l * 2;
+            qs.rem -= rows * a.q_l * 2;
+            rs.p += rows * a.r_l * 2;
+            rs.rem -= rows * a.r_l * 2;
         }
 
         // This wavefront's rows: the diagonal stage first, then older window
