@@ -991,18 +991,80 @@ __device__ __forceinline__ void vblock_store(uint16_t *sv, const u32x2 (&raw)[8]
     }
 }
 
+// Stages of which only one key tile (keys 16 h .. 16 h + 15) can be visible
+// to the wavefront's rows take half the work: the score MFMAs, mask and
+// weights of that tile only, and zero weights for the other one.
+template <int D>
+__device__ __forceinline__ void read_kfrags_half(KFrags<D> &kf, const uint16_t *sk,
+                                                 const FragAddr<D> &fa, int h) {
+    const char *base = reinterpret_cast<const char *>(sk);
+#pragma unroll
+    for (int kc = 0; kc < Cfg<D>::KC; ++kc)
+        kf.f[h][kc] = *reinterpret_cast<const bf16x8 *>(base + fa.ka[kc] + h * 16 * Cfg<D>::CPR * 16);
+}
+
+template <int D>
+__device__ __forceinline__ void score_mfmas_half(const Ctx<D> &cx, const KFrags<D> &kf, Scores &s,
+                                                 int h) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    s.q[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[h][0], cx.qf[0], z, 0, 0, 0);
+    s.r[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[h][0], cx.rf[0], z, 0, 0, 0);
+#pragma unroll
+    for (int kc = 1; kc < Cfg<D>::KC; ++kc) {
+        s.q[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[h][kc], cx.qf[kc], s.q[h], 0, 0, 0);
+        s.r[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[h][kc], cx.rf[kc], s.r[h], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void mask_range_half(Scores &s, int lo, int hi, int h) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        s.q[h][e] = (16 * h + e >= lo && 16 * h + e <= hi) ? s.q[h][e] : kNegInf;
+}
+
+template <int D>
+__device__ __forceinline__ void init_offsets_half(Ctx<D> &cx, const Scores &s, float c, int h) {
+    float mt = fmaxf(fmaxf(s.q[h][0], s.q[h][1]), fmaxf(s.q[h][2], s.q[h][3]));
+    mt = row_max4(mt);
+    cx.m_ref = (cx.m_ref == kNegInf) ? fmaf(mt, c, kMargin) : cx.m_ref;
+    cx.msub = (cx.m_ref == kNegInf) ? 0.f : cx.m_ref;
+}
+
+template <int D>
+__device__ __forceinline__ void weights_half(Ctx<D> &cx, const Scores &s, Weights<false> &pw,
+                                             float c, int h) {
+    cx.xlane = fmaxf(fmaxf(cx.xlane, s.q[h][0]), fmaxf(fmaxf(s.q[h][1], s.q[h][2]), s.q[h][3]));
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+        const float p0 = exp2_fast(fmaf(s.q[h][e], c, -cx.msub));
+        const float p1 = exp2_fast(fmaf(s.q[h][e + 1], c, -cx.msub));
+        const f16x2 ph = cvt_f16x2(p0, p1);
+        const f16x2 wh = cvt_f16x2(p0 * s.r[h][e], p1 * s.r[h][e + 1]);
+        pw.p[4 * h + e] = ph[0];
+        pw.p[4 * h + e + 1] = ph[1];
+        pw.w[4 * h + e] = wh[0];
+        pw.w[4 * h + e + 1] = wh[1];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        pw.p[4 * (1 - h) + e] = (_Float16)0.f;
+        pw.w[4 * (1 - h) + e] = (_Float16)0.f;
+    }
+}
+
 // One pass over the stages of a wavefront in the common case of a window of
 // NW stages: its 16 rows lie inside the sequence and past the window's start,
 // so the stage list is always the diagonal stage (each row sees the keys up
 // to itself), NW - 2 stages every row sees in full, the window's oldest
 // stage (each row sees the keys from row - W + 1 on) and, with SINK, the
-// sink stage.  Every stage's kind and ring slot are then known at compile
-// time: the pass is straight-line code (the same software pipeline as the
-// general stage loop, without its branches, the register copies at their
-// joins and the waits for loads a branch might have skipped), and a stage's
-// mask is one per-lane threshold on the key offset 16 kt + e.
-template <int D, bool PRECISE, int NW, bool SINK>
-__device__ __forceinline__ void window_pass(Ctx<D> &cx, VFrags<D> &vf, Weights<PRECISE> &pw,
+// sink stage (at most 16 sinks).  Every stage's kind and ring slot are then
+// known at compile time: the pass is straight-line code (the same software
+// pipeline as the general stage loop, without its branches, the register
+// copies at their joins and the waits for loads a branch might have
+// skipped), and a stage's mask is one per-lane threshold on the key offset
+// 16 kt + e.  The sinks are keys 0-15, so the sink stage takes half the work.
+template <int D, int NW, bool SINK>
+__device__ __forceinline__ void window_pass(Ctx<D> &cx, VFrags<D> &vf, Weights<false> &pw,
                                             const StageBuf<D> *ring, const StageBuf<D> &sinkbuf,
                                             int hi_w, const FragAddr<D> &fa, int t_diag,
                                             int t_edge, int t_sink, float c) {
@@ -1012,33 +1074,62 @@ __device__ __forceinline__ void window_pass(Ctx<D> &cx, VFrags<D> &vf, Weights<P
     auto buf = [&](int u) -> const StageBuf<D> & {
         return u < NW ? ring[(hi_w - u) & (WRING - 1)] : sinkbuf;
     };
+    // The one key tile of stage u that can be visible, or -1 for both.
+    auto live = [](int u) { return u == NW ? 0 : -1; };
+    auto read_k = [&](KFrags<D> &kf, int u) {
+        if (live(u) < 0)
+            read_kfrags<D>(kf, buf(u).k, fa);
+        else
+            read_kfrags_half<D>(kf, buf(u).k, fa, live(u));
+    };
+    auto scores = [&](const KFrags<D> &kf, Scores &sc, int u) {
+        if (live(u) < 0)
+            score_mfmas<D>(cx, kf, sc);
+        else
+            score_mfmas_half<D>(cx, kf, sc, live(u));
+    };
     KFrags<D> kf[2];
     Scores sc[2];
-    read_kfrags<D>(kf[0], buf(0).k, fa);
-    read_kfrags<D>(kf[1], buf(1).k, fa);
-    score_mfmas<D>(cx, kf[0], sc[0]);
-    read_kfrags<D>(kf[0], buf(2).k, fa);
+    read_k(kf[0], 0);
+    read_k(kf[1], 1);
+    scores(kf[0], sc[0], 0);
+    read_k(kf[0], 2);
 #pragma unroll
     for (int u = 0; u < NST; ++u) {
         Scores &cur = sc[u & 1];
+        const int h = live(u);
         read_vfrags<D>(vf, buf(u).v, fa);
         // The V^T reads go first: the value MFMAs at the step's end wait
         // for them.
         __builtin_amdgcn_sched_barrier(0);
         if (u + 1 < NST)
-            score_mfmas<D>(cx, kf[(u + 1) & 1], sc[(u + 1) & 1]);
+            scores(kf[(u + 1) & 1], sc[(u + 1) & 1], u + 1);
         if (u + 3 < NST)
-            read_kfrags<D>(kf[(u + 1) & 1], buf(u + 3).k, fa);
-        if (u == 0)
-            mask_range(cur, INT32_MIN / 2, t_diag);
-        else if (u == NW - 1)
-            mask_range(cur, t_edge, INT32_MAX / 2);
-        else if (u == NW)
-            mask_range(cur, INT32_MIN / 2, t_sink);
-        if (u == 0)
-            init_offsets<D>(cx, cur, c);
-        weights<D, PRECISE>(cx, cur, pw, c);
-        value_mfmas<D, PRECISE>(cx, vf, pw);
+            read_k(kf[(u + 1) & 1], u + 3);
+        if (u == 0) {
+            if (h < 0)
+                mask_range(cur, INT32_MIN / 2, t_diag);
+            else
+                mask_range_half(cur, INT32_MIN / 2, t_diag, h);
+        } else if (u == NW - 1) {
+            if (h < 0)
+                mask_range(cur, t_edge, INT32_MAX / 2);
+            else
+                mask_range_half(cur, t_edge, INT32_MAX / 2, h);
+        } else if (u == NW) {
+            mask_range_half(cur, INT32_MIN / 2, t_sink, h);
+        }
+        if (u == 0) {
+            if (h < 0)
+                init_offsets<D>(cx, cur, c);
+            else
+                init_offsets_half<D>(cx, cur, c, h);
+        }
+        if (h < 0)
+            weights<D, false>(cx, cur, pw, c);
+        else
+            weights_half<D>(cx, cur, pw, c, h);
+        value_mfmas<D, false>(cx, vf, pw);
         // Steps stay in order, so that later stages' reads are not hoisted
         // into this one (their registers would overlap the live ones).
         __builtin_amdgcn_sched_barrier(0);
@@ -1277,7 +1368,7 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
             // The common case takes the straight-line pass; the general stage
             // loop below covers the other tiles and the recomputation.
             int pass0 = 0;
-            const int nw = !PRECISE && window == 128 && n_sink > 0 ? 5 : 0;
+            const int nw = !PRECISE && window == 128 && n_sink > 0 && n_sink <= 16 ? 5 : 0;
             if (nw > 0 && n_win == nw && lo_w > 0 && i0w + ROWS <= L) {
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
@@ -1292,8 +1383,10 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
                 const int t_diag = row - hi_w * BN - 4 * G;
                 const int t_edge = row - (hi_w - nw + 1) * BN - 4 * G - window + 1;
                 const int t_sink = n_sink - 1 - 4 * G;
-                window_pass<D, PRECISE, 5, true>(cx, vf, pw, ring, sinkbuf, hi_w, fa,
-                                                 t_diag, t_edge, t_sink, c);
+                if constexpr (!PRECISE) {
+                    window_pass<D, 5, true>(cx, vf, pw, ring, sinkbuf, hi_w, fa, t_diag, t_edge,
+                                            t_sink, c);
+                }
                 const float xmax = row_max4(cx.xlane);
                 if (__builtin_amdgcn_ballot_w64(xmax * c > cx.m_ref + kTauHi) == 0) {
                     pass0 = 2;
