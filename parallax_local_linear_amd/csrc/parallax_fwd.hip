@@ -1160,6 +1160,15 @@ __global__ __launch_bounds__(WTHREADS, D == 64 ? 2 : 1) void parallax_fwd_window
     const int lin = (bid % 8) * a.w_per_xcd + bid / 8;
     if (lin >= a.w_blocks)
         return;
+    // The two workgroups on a CU run the same schedule: left in step, their
+    // loads, stores and barriers fall together while the matrix cores idle,
+    // and every workgroup of the chip loads its first tile at the same time.
+    // Every other workgroup of an XCD therefore starts about 8000 cycles
+    // (most of a tile) later when runs are long enough to amortise it.
+    if (D == 64 && a.w_tpw >= 4 && ((bid / 8) & 1)) {
+        __builtin_amdgcn_s_sleep(64);
+        __builtin_amdgcn_s_sleep(64);
+    }
     const int bh = lin / a.w_runs;
     const int run = lin - bh * a.w_runs;
     const int b = bh / a.H;
