@@ -570,7 +570,7 @@ def time_based(steps, warmup, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs on a single MI355X and has no "
+        print("bench.py measures one GPU only: the library runs on a single MI355X and has no "
               "multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

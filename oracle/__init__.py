@@ -283,7 +283,7 @@ _default = None
 
 
 def default_threads() -> int:
-    """Host threads for the oracle: all cores, at most 16 (a GPU machine's CPU share)."""
+    """Host threads for the oracle: all cores, at most 16."""
     return max(1, min(16, os.cpu_count() or 1))
 
 
