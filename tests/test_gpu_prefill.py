@@ -288,6 +288,10 @@ WINDOW_CASES = [
     (3, 2, 300, 64, 128, 32),
     (1, 2, 1000, 64, 128, 1),
     (1, 2, 700, 128, 128, 32),
+    # 16 sinks: the largest count whose sink stage takes half the work; 17
+    # takes the general stage loop
+    (1, 4, 2000, 64, 128, 16),
+    (1, 4, 2000, 64, 128, 17),
 ]
 
 
