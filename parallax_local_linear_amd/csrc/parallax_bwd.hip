@@ -217,15 +217,21 @@ __global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
     constexpr int TPS = 4 * FC;      // threads per stage
     constexpr int SPB = 256 / TPS;   // stages per block
     constexpr int BLK = 64 * 8;      // bf16 elements per operand block
+    constexpr int NB = 2 * KC;       // operand blocks per stage (two 16-row halves)
+    constexpr int RS = FC + 1;       // LDS row stride in 16-byte pieces (padded)
+    static_assert(SPB * NB * 64 == 256 * 8, "each thread stores 8 pieces");
+    // The block's stages pass through LDS, so that each store instruction
+    // writes one whole 1 KiB operand block (lane i to its slot i) instead of
+    // 64 pieces in 64 different lines.
+    __shared__ u32x4 rows_lds[SPB * BS * RS];
     const int t = threadIdx.x;
-    const int s = blockIdx.x * SPB + t / TPS;
+    const int st_in = t / TPS;
+    const int s = blockIdx.x * SPB + st_in;
     const int G = (t % TPS) / FC;
     const int fc = t % FC;
     const int which = blockIdx.y;
     const int L = a.L;
     const int BH = a.B * a.H;
-    if (s >= a.n_st)
-        return;
     const uint16_t *src = which == 0 ? a.q : which == 1 ? a.r : which == 2 ? a.dout
                         : which == 3 ? a.k : a.v;
     const int64_t sb = which == 0 ? a.q_b : which == 1 ? a.r_b : which == 2 ? a.do_b
@@ -240,25 +246,42 @@ __global__ __launch_bounds__(256) void parallax_bwd_record_kernel(BwdArgs a) {
     const size_t rec_elems = kv_side ? bwd_kv_record_bytes(D) / 2 : bwd_q_record_bytes(D) / 2;
     uint16_t *recs = kv_side ? a.kvrec : a.qrec;
     const int rm_block0 = x * 2 * KC;
+    // Stores: wavefront w writes operand blocks 8w .. 8w+7 of the block's
+    // stages; lane i holds slot i, the piece of lane rec_slot(i) of the
+    // fragment order (rec_slot is its own inverse).
+    const int lane = t & 63;
+    const int w = t >> 6;
+    const int l = rec_slot(lane);
     for (int bh = blockIdx.z; bh < BH; bh += gridDim.z) {
         const int b = bh / a.H;
         const int h = bh - b * a.H;
-        const int i0 = s * BS;
-        const uint16_t *base = src + b * sb + h * sh + (int64_t)i0 * sl;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows_bytes(i0, L, sl, D));
-        uint16_t *rec = recs + ((size_t)bh * a.n_st + s) * rec_elems;
-        u32x4 in[8];
+        if (s < a.n_st) {
+            const int i0 = s * BS;
+            const uint16_t *base = src + b * sb + h * sh + (int64_t)i0 * sl;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows_bytes(i0, L, sl, D));
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            in[e] = bufld16(rs, (uint32_t)((8 * G + e) * sl * 2 + fc * 16));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // Row-major block (row / 16, fc / 4), lane row % 16 + 16 (fc % 4).
-            const int row = 8 * G + e;
-            const int blk = rm_block0 + (row / 16) * KC + fc / 4;
-            const int lane = (row % 16) + 16 * (fc % 4);
-            *reinterpret_cast<u32x4 *>(rec + (size_t)blk * BLK + rec_slot(lane) * 8) = in[e];
+            for (int e = 0; e < 8; ++e) {
+                const int row = 8 * G + e;
+                rows_lds[(st_in * BS + row) * RS + fc] =
+                    bufld16(rs, (uint32_t)(row * sl * 2 + fc * 16));
+            }
         }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ob = 8 * w + i;
+            const int so = ob / NB;           // stage of the block, within this workgroup's
+            const int bis = ob - so * NB;     // its block: rows 16 R .., chunks 4 F ..
+            const int R = bis / KC, F = bis - R * KC;
+            const int s_out = blockIdx.x * SPB + so;
+            if (s_out < a.n_st) {
+                const u32x4 piece = rows_lds[(so * BS + 16 * R + (l & 15)) * RS + 4 * F + (l >> 4)];
+                uint16_t *rec = recs + ((size_t)bh * a.n_st + s_out) * rec_elems;
+                *reinterpret_cast<u32x4 *>(rec + (size_t)(rm_block0 + R * KC + F) * BLK +
+                                           lane * 8) = piece;
+            }
+        }
+        __syncthreads();
     }
 }
 
