@@ -1023,14 +1023,6 @@ __device__ __forceinline__ void mask_range_half(Scores &s, int lo, int hi, int h
 }
 
 template <int D>
-__device__ __forceinline__ void init_offsets_half(Ctx<D> &cx, const Scores &s, float c, int h) {
-    float mt = fmaxf(fmaxf(s.q[h][0], s.q[h][1]), fmaxf(s.q[h][2], s.q[h][3]));
-    mt = row_max4(mt);
-    cx.m_ref = (cx.m_ref == kNegInf) ? fmaf(mt, c, kMargin) : cx.m_ref;
-    cx.msub = (cx.m_ref == kNegInf) ? 0.f : cx.m_ref;
-}
-
-template <int D>
 __device__ __forceinline__ void weights_half(Ctx<D> &cx, const Scores &s, Weights<false> &pw,
                                              float c, int h) {
     cx.xlane = fmaxf(fmaxf(cx.xlane, s.q[h][0]), fmaxf(fmaxf(s.q[h][1], s.q[h][2]), s.q[h][3]));
@@ -1074,19 +1066,18 @@ __device__ __forceinline__ void window_pass(Ctx<D> &cx, VFrags<D> &vf, Weights<f
     auto buf = [&](int u) -> const StageBuf<D> & {
         return u < NW ? ring[(hi_w - u) & (WRING - 1)] : sinkbuf;
     };
-    // The one key tile of stage u that can be visible, or -1 for both.
-    auto live = [](int u) { return u == NW ? 0 : -1; };
+    // The sink stage (u == NW) holds the sinks in keys 0-15: half the work.
     auto read_k = [&](KFrags<D> &kf, int u) {
-        if (live(u) < 0)
-            read_kfrags<D>(kf, buf(u).k, fa);
+        if (u == NW)
+            read_kfrags_half<D>(kf, buf(u).k, fa, 0);
         else
-            read_kfrags_half<D>(kf, buf(u).k, fa, live(u));
+            read_kfrags<D>(kf, buf(u).k, fa);
     };
     auto scores = [&](const KFrags<D> &kf, Scores &sc, int u) {
-        if (live(u) < 0)
-            score_mfmas<D>(cx, kf, sc);
+        if (u == NW)
+            score_mfmas_half<D>(cx, kf, sc, 0);
         else
-            score_mfmas_half<D>(cx, kf, sc, live(u));
+            score_mfmas<D>(cx, kf, sc);
     };
     KFrags<D> kf[2];
     Scores sc[2];
@@ -1097,7 +1088,6 @@ __device__ __forceinline__ void window_pass(Ctx<D> &cx, VFrags<D> &vf, Weights<f
 #pragma unroll
     for (int u = 0; u < NST; ++u) {
         Scores &cur = sc[u & 1];
-        const int h = live(u);
         read_vfrags<D>(vf, buf(u).v, fa);
         // The V^T reads go first: the value MFMAs at the step's end wait
         // for them.
@@ -1106,29 +1096,19 @@ __device__ __forceinline__ void window_pass(Ctx<D> &cx, VFrags<D> &vf, Weights<f
             scores(kf[(u + 1) & 1], sc[(u + 1) & 1], u + 1);
         if (u + 3 < NST)
             read_k(kf[(u + 1) & 1], u + 3);
-        if (u == 0) {
-            if (h < 0)
-                mask_range(cur, INT32_MIN / 2, t_diag);
-            else
-                mask_range_half(cur, INT32_MIN / 2, t_diag, h);
-        } else if (u == NW - 1) {
-            if (h < 0)
-                mask_range(cur, t_edge, INT32_MAX / 2);
-            else
-                mask_range_half(cur, t_edge, INT32_MAX / 2, h);
-        } else if (u == NW) {
-            mask_range_half(cur, INT32_MIN / 2, t_sink, h);
-        }
-        if (u == 0) {
-            if (h < 0)
-                init_offsets<D>(cx, cur, c);
-            else
-                init_offsets_half<D>(cx, cur, c, h);
-        }
-        if (h < 0)
-            weights<D, false>(cx, cur, pw, c);
+        if (u == 0)
+            mask_range(cur, INT32_MIN / 2, t_diag);
+        else if (u == NW - 1)
+            mask_range(cur, t_edge, INT32_MAX / 2);
+        else if (u == NW)
+            mask_range_half(cur, INT32_MIN / 2, t_sink, 0);
+        // The diagonal stage sets the offsets: every row sees its own key.
+        if (u == 0)
+            init_offsets<D>(cx, cur, c);
+        if (u == NW)
+            weights_half<D>(cx, cur, pw, c, 0);
         else
-            weights_half<D>(cx, cur, pw, c, h);
+            weights<D, false>(cx, cur, pw, c);
         value_mfmas<D, false>(cx, vf, pw);
         // Steps stay in order, so that later stages' reads are not hoisted
         // into this one (their registers would overlap the live ones).
