@@ -292,6 +292,9 @@ WINDOW_CASES = [
     # takes the general stage loop
     (1, 4, 2000, 64, 128, 16),
     (1, 4, 2000, 64, 128, 17),
+    # runs of 5 tiles (the staggered start and the row streams over several
+    # tiles) ending in a ragged tile
+    (1, 16, 8200, 64, 128, 4),
 ]
 
 
