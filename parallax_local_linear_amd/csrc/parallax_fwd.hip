@@ -30,9 +30,11 @@
 //        V phase: LDS reads of the V fragments of stage t, weights of
 //                 stage t, and the copy of its group's half of stage t+5
 //                 from global memory to LDS.
-//   * Keys stream through LDS in stages of 32 keys with six buffers.  The
-//     copies go straight from global memory into LDS (buffer loads with
-//     the LDS destination, which puts lane i's 16 bytes at 16 i), five
+//   * Keys stream through LDS in stages of 32 keys (64 at d = 64: two
+//     32-key halves, so that a step carries about the same matrix-core
+//     work per barrier at either d) with six buffers.  The copies go
+//     straight from global memory into LDS (buffer loads with the LDS
+//     destination, which puts lane i's 16 bytes at 16 i), five
 //     stages ahead of use, and each wave waits for its own copies of three
 //     stages back at the end of its V phase.  K comes from the K tensor
 //     through a buffer resource that ends at the last valid row, so rows
@@ -109,7 +111,7 @@ constexpr int ROWS = 16;                  // query rows per wavefront
 constexpr int NWAVES = 8;                 // two groups of four wavefronts
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int BM = ROWS * NWAVES;         // query rows per workgroup
-constexpr int BN = 32;                    // keys per stage
+constexpr int BN = 32;                    // keys per half stage (one V^T image, a score tile pair)
 constexpr int NBUF = 6;                   // LDS stage buffers
 constexpr int AHEAD = 5;                  // stages between a copy and its use
 constexpr int IN_FLIGHT = 2;              // stages a wave's copies may still be in flight
@@ -127,16 +129,18 @@ struct Cfg {
     static constexpr int KC = D / 32;     // reduction chunks of the score MFMA
     static constexpr int DT = D / 16;     // output tiles of the value MFMA
     static constexpr int CPR = D / 8;     // 16-byte chunks per K row
-    static constexpr int K_ELEMS = BN * D;
-    static constexpr int V_ELEMS = D * BN;
-    // 16-byte copies of a half stage (one group's share) of K and of V^T.
-    // At d = 128 every wave of the group copies one K and one V^T chunk per
-    // lane; at d = 64 the group's first two waves copy K, the others V^T.
-    static constexpr int HALF_K = BN / 2 * CPR;
-    static constexpr int HALF_V = D / 2 * (BN / 8);
-    static constexpr bool SPLIT = HALF_K < 256;
-    static constexpr int COPIES = SPLIT ? 1 : 2;  // copy instructions per wave per stage
-    static_assert(HALF_K == HALF_V && (HALF_K == 256 || HALF_K == 128), "copy split");
+    // Keys per stage of the main kernel: 32 at d = 128, 64 at d = 64 (two
+    // 32-key halves), so that a stage is 16 KB of K and V^T at either d and
+    // a step at d = 64 carries as many score MFMAs as at d = 128 against
+    // the same per-step costs (barriers, waits, copy issue, latencies).
+    static constexpr int NVH = D == 64 ? 2 : 1;  // 32-key halves per stage
+    static constexpr int SBN = BN * NVH;
+    // 16-byte copies of a half stage (one group's share) of K and of V^T:
+    // every wave of the group copies one K and one V^T chunk per lane.
+    static constexpr int HALF_K = SBN / 2 * CPR;
+    static constexpr int HALF_V = D / 2 * (SBN / 8);
+    static constexpr int COPIES = 2;  // copy instructions per wave per stage
+    static_assert(HALF_K == 256 && HALF_V == 256, "one K and one V^T chunk per lane");
 };
 
 // Row swizzle of the K layout: chunk c of row r sits in slot
@@ -213,9 +217,11 @@ __device__ __forceinline__ void wait_copies() {
     __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
 
-// Floor and ceiling of a / BN for any sign of a.
-__device__ __forceinline__ int floor_div_bn(int a) { return a >= 0 ? a / BN : -((-a + BN - 1) / BN); }
-__device__ __forceinline__ int ceil_div_bn(int a) { return -floor_div_bn(-a); }
+// Floor and ceiling of a / S for any sign of a.
+template <int S>
+__device__ __forceinline__ int floor_div(int a) { return a >= 0 ? a / S : -((-a + S - 1) / S); }
+template <int S>
+__device__ __forceinline__ int ceil_div(int a) { return -floor_div<S>(-a); }
 
 template <int D>
 struct Ctx {
@@ -262,12 +268,13 @@ struct Weights<true> {
     f16x8 p, w, plo, wlo;
 };
 
-// LDS stage buffer: K [32 keys][d] and V^T [d][32 positions], both in the
-// swizzled 16-byte-chunk layouts above.
-template <int D>
+// LDS stage buffer of SK keys: K [SK keys][d] and V^T as SK / 32 images of
+// [d][32 positions] (one per 32-key half), both in the swizzled
+// 16-byte-chunk layouts above.
+template <int D, int SK = BN>
 struct __attribute__((aligned(16))) StageBuf {
-    uint16_t k[Cfg<D>::K_ELEMS];
-    uint16_t v[Cfg<D>::V_ELEMS];
+    uint16_t k[SK * D];
+    uint16_t v[D * SK];
 };
 
 // Compile-time stage buffer number.
@@ -535,11 +542,14 @@ __global__ __launch_bounds__(256) void parallax_vprep_kernel(FwdArgs a) {
 template <int D, bool WHOLE, bool STATS, bool PRECISE>
 __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     using C = Cfg<D>;
+    constexpr int NVH = C::NVH;  // 32-key halves per stage
+    constexpr int SBN = C::SBN;  // keys per stage
+    using SBuf = StageBuf<D, SBN>;
     // One LDS variable per stage buffer, each indexed only by compile-time
     // buffer numbers: the compiler then tells the buffers apart and waits
     // before a fragment read only for the copies into that buffer.
-    __shared__ StageBuf<D> sb0, sb1, sb2, sb3, sb4, sb5;
-    auto sbuf = [&](auto b) -> StageBuf<D> & {
+    __shared__ SBuf sb0, sb1, sb2, sb3, sb4, sb5;
+    auto sbuf = [&](auto b) -> SBuf & {
         if constexpr (std::is_same_v<decltype(b), int>) {
             const int i = b % NBUF;
             return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : i == 3 ? sb3 : i == 4 ? sb4 : sb5;
@@ -608,16 +618,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
 
     // Stages with at least one visible pair for rows [i0, i1]: the sink
     // stages that lie before the window, then the window/causal span.
-    const int st_hi = i1 / BN;
+    const int st_hi = i1 / SBN;
     int st_lo = 0, n_ss = 0;
     if (window > 0) {
         const int lo = i0 - window + 1;
-        st_lo = lo > 0 ? lo / BN : 0;
-        n_ss = min((n_sink + BN - 1) / BN, st_lo);
+        st_lo = lo > 0 ? lo / SBN : 0;
+        n_ss = min((n_sink + SBN - 1) / SBN, st_lo);
     }
     const int n = n_ss + (st_hi - st_lo + 1);
     // Key offset of stage u of that list.
-    auto list_j0 = [&](int u) { return (u < n_ss ? u : st_lo + (u - n_ss)) * BN; };
+    auto list_j0 = [&](int u) { return (u < n_ss ? u : st_lo + (u - n_ss)) * SBN; };
 
     // Stages of the window/causal run that every row of the workgroup sees
     // in full: [f_lo, f_hi).  A stage starting at key j0 qualifies when its
@@ -628,10 +638,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // every stage.
     int f_lo = n, f_hi = n;
     {
-        const int jmax = min(i0 - (BN - 1), L - BN);
+        const int jmax = min(i0 - (SBN - 1), L - SBN);
         const int jmin = window > 0 ? i1 - window + 1 : 0;
-        const int lo = n_ss + max(0, ceil_div_bn(jmin) - st_lo);
-        const int hi = min(n, n_ss + floor_div_bn(jmax) - st_lo + 1);
+        const int lo = n_ss + max(0, ceil_div<SBN>(jmin) - st_lo);
+        const int hi = min(n, n_ss + floor_div<SBN>(jmax) - st_lo + 1);
         if (jmax >= 0 && lo < hi) {
             f_lo = lo;
             f_hi = hi;
@@ -651,9 +661,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // so each lane fetches the chunk that the swizzled layout puts there.
     // Copies past the last stage reload the last stage (into a buffer
     // nobody reads again), which keeps the loop branch-free.
-    const bool k_role = !C::SPLIT || wg < 2;  // d = 64: waves copying K
-    const int kslot0 = grp * C::HALF_K + wg * 64;                       // K slots of this wave
-    const int vslot0 = grp * C::HALF_V + (C::SPLIT ? wg - 2 : wg) * 64;  // V^T slots of this wave
+    const int kslot0 = grp * C::HALF_K + wg * 64;  // K slots of this wave
+    const int vslot0 = grp * C::HALF_V + wg * 64;  // V^T slots of this wave
     uint32_t kgoff;  // byte offset of this lane's K chunk from the stage's first row
     {
         const int s = kslot0 + lane;
@@ -661,42 +670,57 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         const int ch = (s % C::CPR) ^ kswz<D>(r);
         kgoff = (uint32_t)(r * a.k_l * 2 + ch * 16);
     }
+    // A stage's V^T is NVH consecutive 32-key images of the workspace, so
+    // this lane's chunk lies vgoff bytes past the stage's first image.
     const uint32_t vgoff = (uint32_t)(vslot0 + lane) * 16u;
-    constexpr uint32_t kImage = D * BN * 2;  // bytes of one stage's V^T image
+    constexpr uint32_t kImage = D * BN * 2;  // bytes of one 32-key V^T image
     const __amdgpu_buffer_rsrc_t rk_all = make_rsrc(kb, WHOLE ? rows_bytes(0, L, a.k_l, D) : 0u);
     const __amdgpu_buffer_rsrc_t rv_all = make_rsrc(vtb, WHOLE ? (uint32_t)a.n_st * kImage : 0u);
     typedef __attribute__((address_space(3))) void lds_void;
     auto copy = [&](int t, auto buf) __attribute__((always_inline)) {
         const int j0 = __builtin_amdgcn_readfirstlane(stage_j0(min(t, n - 1)));
-        const int si = j0 / BN;
+        const int si = j0 / BN;  // first 32-key image of the stage
         lds_void *kdst = (lds_void *)&sbuf(buf).k[kslot0 * 8];
         lds_void *vdst = (lds_void *)&sbuf(buf).v[vslot0 * 8];
         if constexpr (WHOLE) {
             // Offsets stay below 2^32: the K slice is < 2^31 bytes and a
-            // stage reaches at most 31 rows (< 2^30 bytes) past its end; the
-            // V^T images of the slice span < 2^31 bytes.
+            // stage reaches at most SBN - 1 rows (< 2^31 bytes at row
+            // strides below 2^24 elements) past its end; the V^T images of
+            // the slice span < 2^31 bytes, and images past the last one
+            // (the second half of a last 64-key stage) read as zeros.
             const uint32_t ko = (uint32_t)j0 * (uint32_t)a.k_l * 2u;
             const uint32_t vo = (uint32_t)si * kImage;
-            if (k_role)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk_all, kdst, 16, (int)(kgoff + ko), 0, 0, 0);
-            if (!C::SPLIT || !k_role)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv_all, vdst, 16, (int)(vgoff + vo), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk_all, kdst, 16, (int)(kgoff + ko), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv_all, vdst, 16, (int)(vgoff + vo), 0, 0, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rk =
                 make_rsrc(kb + (int64_t)j0 * a.k_l, rows_bytes(j0, L, a.k_l, D));
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vtb + (int64_t)si * (D * BN), kImage);
-            if (k_role)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, (int)kgoff, 0, 0, 0);
-            if (!C::SPLIT || !k_role)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, (int)vgoff, 0, 0, 0);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(
+                vtb + (int64_t)si * (D * BN), (uint32_t)min(NVH, a.n_st - si) * kImage);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, (int)kgoff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, (int)vgoff, 0, 0, 0);
         }
     };
 
+    // Fragments, scores and weights of a stage, one set per 32-key half
+    // (half h: keys 32 h .. 32 h + 31 of the stage).
     const FragAddr<D> fa = frag_addr<D>(l16, G);
-    KFrags<D> kf;
-    VFrags<D> vf;
-    Scores sc;
-    Weights<PRECISE> pw;
+    KFrags<D> kf[NVH];
+    VFrags<D> vf[NVH];
+    Scores sc[NVH];
+    Weights<PRECISE> pw[NVH];
+    auto read_k = [&](auto b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < NVH; ++h)
+            read_kfrags<D>(kf[h], sbuf(b).k + h * BN * D, fa);
+    };
+    auto all_offsets = [&]() __attribute__((always_inline)) {
+        bool set = false;
+#pragma unroll
+        for (int h = 0; h < NVH; ++h)
+            set = init_offsets<D>(cx, sc[h], c);
+        return set;
+    };
 
     // End of the M phase, when the score MFMAs are done.  Masked stages: the
     // mask of stage t's scores and the softmax offsets of rows that still
@@ -709,20 +733,26 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         if constexpr (decltype(masked)::value == 2) {
             const int dlim = min(row, L - 1) - stage_j0(t) - 4 * G;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int h = 0; h < NVH; ++h)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sc.q[kt][e] = (16 * kt + e <= dlim) ? sc.q[kt][e] : kNegInf;
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sc[h].q[kt][e] = (BN * h + 16 * kt + e <= dlim) ? sc[h].q[kt][e] : kNegInf;
         } else if constexpr (decltype(masked)::value) {
-            mask_scores(sc, stage_j0(t), row, G, L, window, n_sink);
+#pragma unroll
+            for (int h = 0; h < NVH; ++h)
+                mask_scores(sc[h], stage_j0(t) + BN * h, row, G, L, window, n_sink);
             if (!offsets_set)
-                offsets_set = init_offsets<D>(cx, sc, c);
+                offsets_set = all_offsets();
         }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            pin(sc.q[kt]);
-            pin(sc.r[kt]);
-        }
+        for (int h = 0; h < NVH; ++h)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                pin(sc[h].q[kt]);
+                pin(sc[h].r[kt]);
+            }
         pin(cx.msub);
     };
     // M phase of step t (b0 = t % NBUF, always a compile-time constant):
@@ -732,13 +762,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // issue slots between its MFMAs, while a V-phase wave stalls on each
     // LDS read that the busy LDS cannot take yet.
     auto mphase = [&](auto masked, auto b0, int t, bool values) __attribute__((always_inline)) {
-        score_mfmas<D>(cx, kf, sc);
-        __builtin_amdgcn_sched_barrier(0);
-        if (values)
-            value_mfmas<D, PRECISE>(cx, vf, pw);
-        read_kfrags<D>(kf, sbuf(b0 + 1).k, fa);
 #pragma unroll
-        for (int i = 0; i < 2 * C::KC; ++i) {
+        for (int h = 0; h < NVH; ++h)
+            score_mfmas<D>(cx, kf[h], sc[h]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (values) {
+#pragma unroll
+            for (int h = 0; h < NVH; ++h)
+                value_mfmas<D, PRECISE>(cx, vf[h], pw[h]);
+        }
+        read_k(b0 + 1);
+#pragma unroll
+        for (int i = 0; i < NVH * 2 * C::KC; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, (PRECISE ? 2 : 1) * C::DT / C::KC, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
@@ -750,14 +785,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // K.  Stage s lives in buffer s % 6 from its copy (step s-5) to its last
     // read (V phase of step s).
     auto vphase = [&](auto b0, int t) __attribute__((always_inline)) {
-        read_vfrags<D>(vf, sbuf(b0).v, fa);
+#pragma unroll
+        for (int h = 0; h < NVH; ++h)
+            read_vfrags<D>(vf[h], sbuf(b0).v + h * D * BN, fa);
         __builtin_amdgcn_sched_barrier(0);
-        weights<D, PRECISE>(cx, sc, pw, c);
-        pin(pw.p);
-        pin(pw.w);
-        if constexpr (PRECISE) {
-            pin(pw.plo);
-            pin(pw.wlo);
+#pragma unroll
+        for (int h = 0; h < NVH; ++h) {
+            weights<D, PRECISE>(cx, sc[h], pw[h], c);
+            pin(pw[h].p);
+            pin(pw[h].w);
+            if constexpr (PRECISE) {
+                pin(pw[h].plo);
+                pin(pw[h].wlo);
+            }
         }
         copy(t + AHEAD, b0 + AHEAD);
         wait_copies<IN_FLIGHT * C::COPIES>();
@@ -799,9 +839,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         copy(2, kB2);
         copy(3, kB3);
         copy(4, kB4);
-        wait_copies<0>();
+        // The first M phase reads stages 0 and 1: wait for this wave's Q
+        // and R loads and its copies of those two (issued first), then
+        // publish them; stages 2 and 3 are waited for at the end of the
+        // first V phase, as in every step.
+        wait_copies<(AHEAD - 2) * C::COPIES>();
         __syncthreads();
-        read_kfrags<D>(kf, sb0.k, fa);
+        read_k(kB0);
         // The second group starts one phase later.
         if (grp == 1)
             phase_barrier();
@@ -812,7 +856,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         } else {
             mphase(kFull, kB0, 0, false);
             if (!offsets_set)
-                offsets_set = init_offsets<D>(cx, sc, c);
+                offsets_set = all_offsets();
         }
         phase_barrier<false>();
         vphase(kB0, 0);
@@ -869,7 +913,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
             step(kMasked, t, t);
         // Value MFMAs of the last stage; the first group catches up with the
         // second group's extra barrier.
-        value_mfmas<D, PRECISE>(cx, vf, pw);
+#pragma unroll
+        for (int h = 0; h < NVH; ++h)
+            value_mfmas<D, PRECISE>(cx, vf[h], pw[h]);
         if (grp == 0)
             phase_barrier();
 
