@@ -839,11 +839,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         copy(2, kB2);
         copy(3, kB3);
         copy(4, kB4);
-        // The first M phase reads stages 0 and 1: wait for this wave's Q
-        // and R loads and its copies of those two (issued first), then
-        // publish them; stages 2 and 3 are waited for at the end of the
-        // first V phase, as in every step.
-        wait_copies<(AHEAD - 2) * C::COPIES>();
+        // Wait for this wave's Q and R loads and its copies of stages 0-2
+        // (issued first), then publish them.  The first group's first two
+        // M phases read K of stages 0-2; each wave's copies of stage s+3
+        // are waited for at the end of its V phase of step s, but the
+        // second group runs a phase behind and has had no V phase when the
+        // first group reads stage 2, so stage 2 is waited for here.
+        wait_copies<(AHEAD - 3) * C::COPIES>();
         __syncthreads();
         read_k(kB0);
         // The second group starts one phase later.
