@@ -87,17 +87,20 @@ SMALL = [
 ]
 
 
-# Causal tiles end with 2 to 9 steps after the main loop (their remaining
+# Causal tiles end with a few steps after the main loop (their remaining
 # full stages and the diagonal), taken as whole groups of six plus a partial
-# group.  These lengths give tiles with each of those counts (2: L=257,
-# 3: 289, 4: 129, 5: 161, 6: 193, 7: 225, 8: 449, 9: 481), from the stage
-# schedule: 32-key stages, 128-row tiles, fully visible stages first.
-TAIL_LENGTHS = [129, 161, 193, 225, 257, 289, 449, 481]
+# group.  These lengths give tiles with each possible count, from the stage
+# schedule (128-row tiles, fully visible stages first): with 32-key stages
+# (d = 128) 2 to 9 steps (2: L=257, 3: 289, 4: 129, 5: 161, 6: 193, 7: 225,
+# 8: 449, 9: 481); with 64-key stages (d = 64) 2 to 7 steps (2: L=129,
+# 3: 193, 4: 257, 5: 321, 6: 385, 7: 449).
+TAIL_LENGTHS = {128: [129, 161, 193, 225, 257, 289, 449, 481],
+                64: [129, 193, 257, 321, 385, 449]}
 
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_causal_tail_step_counts(orc, d):
-    for i, L in enumerate(TAIL_LENGTHS):
+    for i, L in enumerate(TAIL_LENGTHS[d]):
         q, k, v, r = (rand((1, 1, L, d), 60 + 4 * i + j) for j in range(4))
         full_check(orc, q, k, v, r, what="causal tail L=%d d=%d" % (L, d))
 
@@ -231,6 +234,32 @@ def test_64bit_offsets(orc):
                                   scale, 0, 0)
         compare(f64(o[0, 1, i:i + 1]), f64(lse[0, 1, i:i + 1]), o_ref, lse_ref,
                 "64-bit offsets row %d" % i)
+
+
+def test_key_slice_past_31_bit_offsets(orc):
+    """K rows spaced 2^14 elements apart over 65616 rows (a slice of more than
+    2^31 bytes): the general kernel then builds buffer resources per stage
+    instead of one per tensor.  At d = 64 a stage is two 32-key V^T images,
+    the second of which does not exist for the last stage when the sequence
+    ends in its first half (65616 = 1025 * 64 + 16).  Rows across the
+    sequence against the oracle with their full causal context."""
+    B, H, L, d, ld = 1, 1, 65616, 64, 1 << 14
+    say("[case] 31-bit key slice B=%d H=%d L=%d d=%d row stride %d" % (B, H, L, d, ld))
+    q, v, r = (workloads.random_tensor((B, H, L, d), 1400 + t, device=DEV) for t in range(3))
+    kbuf = torch.zeros((L, ld), dtype=torch.bfloat16, device=DEV)
+    kbuf[:, :d] = workloads.random_tensor((L, d), 1403, device=DEV)
+    k = kbuf[:, :d].unsqueeze(0).unsqueeze(0)
+    assert k.stride() == (L * ld, L * ld, ld, 1)
+    o, lse = parallax_attn_fwd(q, k, v, r)
+    torch.cuda.synchronize()
+    scale = default_scale(d)
+    K, V = f64(k[0, 0]), f64(v[0, 0])
+    for i in (0, 31, 32, 63, 64, 127, 40000, L - 81, L - 17, L - 16, L - 1):
+        o_ref, lse_ref = orc.rows(f64(q[0, 0, i:i + 1]), f64(r[0, 0, i:i + 1]), [i],
+                                  K[:i + 1], V[:i + 1], scale, 0, 0)
+        compare(f64(o[0, 0, i:i + 1]), f64(lse[0, 0, i:i + 1]), o_ref, lse_ref,
+                "31-bit key slice row %d" % i)
+    del kbuf
 
 
 def test_many_slices(orc):
