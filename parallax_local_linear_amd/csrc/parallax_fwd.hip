@@ -936,7 +936,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         offsets_set = true;
     }
 
-    // Epilogue.
+    // Epilogue.  The outputs are stored non-temporally: no later work in the
+    // call reads them, and the 0.6B-like call measured 3% faster with it
+    // (the windowed kernel measured slower with it and keeps plain stores).
     const float ell_t = cx.accL[0];
     const float s_t = cx.accS[0];
     if (row < L) {
@@ -949,10 +951,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 out[u] = (cx.accA[dt][u] * keep + cx.accC[dt][u]) * inv;
-            *reinterpret_cast<f32x4 *>(ob + 16 * dt + 4 * G) = out;
+            __builtin_nontemporal_store(out, reinterpret_cast<f32x4 *>(ob + 16 * dt + 4 * G));
         }
         if (G == 0)
-            a.lse[(int64_t)bh * L + row] = (cx.m_ref + log2f(ell_t)) * kLn2;
+            __builtin_nontemporal_store((cx.m_ref + log2f(ell_t)) * kLn2, a.lse + (int64_t)bh * L + row);
         // Saved for the backward: sbar = S / ell and pv = A / ell.
         if constexpr (STATS) {
             float *pb = a.pv + ((int64_t)bh * L + row) * D;
