@@ -711,14 +711,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     Weights<PRECISE> pw[NVH];
     auto read_k = [&](auto b) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < NVH; ++h)
-            read_kfrags<D>(kf[h], sbuf(b).k + h * BN * D, fa);
+        for (int hv = 0; hv < NVH; ++hv)
+            read_kfrags<D>(kf[hv], sbuf(b).k + hv * BN * D, fa);
     };
     auto all_offsets = [&]() __attribute__((always_inline)) {
         bool set = false;
 #pragma unroll
-        for (int h = 0; h < NVH; ++h)
-            set = init_offsets<D>(cx, sc[h], c);
+        for (int hv = 0; hv < NVH; ++hv)
+            set = init_offsets<D>(cx, sc[hv], c);
         return set;
     };
 
@@ -733,25 +733,25 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         if constexpr (decltype(masked)::value == 2) {
             const int dlim = min(row, L - 1) - stage_j0(t) - 4 * G;
 #pragma unroll
-            for (int h = 0; h < NVH; ++h)
+            for (int hv = 0; hv < NVH; ++hv)
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        sc[h].q[kt][e] = (BN * h + 16 * kt + e <= dlim) ? sc[h].q[kt][e] : kNegInf;
+                        sc[hv].q[kt][e] = (BN * hv + 16 * kt + e <= dlim) ? sc[hv].q[kt][e] : kNegInf;
         } else if constexpr (decltype(masked)::value) {
 #pragma unroll
-            for (int h = 0; h < NVH; ++h)
-                mask_scores(sc[h], stage_j0(t) + BN * h, row, G, L, window, n_sink);
+            for (int hv = 0; hv < NVH; ++hv)
+                mask_scores(sc[hv], stage_j0(t) + BN * hv, row, G, L, window, n_sink);
             if (!offsets_set)
                 offsets_set = all_offsets();
         }
 #pragma unroll
-        for (int h = 0; h < NVH; ++h)
+        for (int hv = 0; hv < NVH; ++hv)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                pin(sc[h].q[kt]);
-                pin(sc[h].r[kt]);
+                pin(sc[hv].q[kt]);
+                pin(sc[hv].r[kt]);
             }
         pin(cx.msub);
     };
@@ -763,13 +763,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // LDS read that the busy LDS cannot take yet.
     auto mphase = [&](auto masked, auto b0, int t, bool values) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < NVH; ++h)
-            score_mfmas<D>(cx, kf[h], sc[h]);
+        for (int hv = 0; hv < NVH; ++hv)
+            score_mfmas<D>(cx, kf[hv], sc[hv]);
         __builtin_amdgcn_sched_barrier(0);
         if (values) {
 #pragma unroll
-            for (int h = 0; h < NVH; ++h)
-                value_mfmas<D, PRECISE>(cx, vf[h], pw[h]);
+            for (int hv = 0; hv < NVH; ++hv)
+                value_mfmas<D, PRECISE>(cx, vf[hv], pw[hv]);
         }
         read_k(b0 + 1);
 #pragma unroll
@@ -786,17 +786,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
     // read (V phase of step s).
     auto vphase = [&](auto b0, int t) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < NVH; ++h)
-            read_vfrags<D>(vf[h], sbuf(b0).v + h * D * BN, fa);
+        for (int hv = 0; hv < NVH; ++hv)
+            read_vfrags<D>(vf[hv], sbuf(b0).v + hv * D * BN, fa);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int h = 0; h < NVH; ++h) {
-            weights<D, PRECISE>(cx, sc[h], pw[h], c);
-            pin(pw[h].p);
-            pin(pw[h].w);
+        for (int hv = 0; hv < NVH; ++hv) {
+            weights<D, PRECISE>(cx, sc[hv], pw[hv], c);
+            pin(pw[hv].p);
+            pin(pw[hv].w);
             if constexpr (PRECISE) {
-                pin(pw[h].plo);
-                pin(pw[h].wlo);
+                pin(pw[hv].plo);
+                pin(pw[hv].wlo);
             }
         }
         copy(t + AHEAD, b0 + AHEAD);
@@ -916,8 +916,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         // Value MFMAs of the last stage; the first group catches up with the
         // second group's extra barrier.
 #pragma unroll
-        for (int h = 0; h < NVH; ++h)
-            value_mfmas<D, PRECISE>(cx, vf[h], pw[h]);
+        for (int hv = 0; hv < NVH; ++hv)
+            value_mfmas<D, PRECISE>(cx, vf[hv], pw[hv]);
         if (grp == 0)
             phase_barrier();
 
