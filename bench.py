@@ -64,6 +64,7 @@ KERNEL_SOURCES = {
     "decode": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
     "decode_paged": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
     "decode_gqa": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
+    "decode_mqa": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_decode.hip"),
     "based_decode": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_based.hip"),
     "backward": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_bwd.hip"),
     "projection": os.path.join(ROOT, "parallax_local_linear_amd", "csrc", "parallax_proj.hip"),
@@ -389,14 +390,14 @@ def time_backward(cfg, steps, warmup, stream):
 
 def time_decode_paged(dcfg, steps, warmup, stream):
     """General decode on the decode workload's size: 64-token pages in a shuffled
-    pool, 16 query heads over 16 or 4 kv heads.  GB/s counts the cache once."""
+    pool, 16 query heads over 16, 4 or 1 kv heads.  GB/s counts the cache once."""
     import torch
 
     from parallax_local_linear_amd import parallax_attn_decode_paged
     dev = torch.device("cuda:0")
     B, Hq, Lmax, d, page = dcfg.B, dcfg.H, dcfg.Lmax, dcfg.d, 64
     out = []
-    for Hkv in (16, 4):
+    for Hkv in (16, 4, 1):
         g = torch.Generator(device=dev).manual_seed(2024 + Hkv)
         q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
         r = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
@@ -426,11 +427,12 @@ def time_decode_paged(dcfg, steps, warmup, stream):
         gbs = nbytes / (ms * 1e-3) / 1e9
         # Four or more query heads per kv head take the matrix-core kernel.
         gqa = Hq // Hkv >= 4
+        key = "decode_paged" if not gqa else ("decode_gqa" if Hkv == 4 else "decode_mqa")
         out.append({"Hq": Hq, "Hkv": Hkv, "page": page, "ms": round(ms, 4),
                     "value": round(gbs, 1), "unit": "GB/s",
                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                  "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                 "traffic": measured_traffic("decode_gqa" if gqa else "decode_paged"),
+                                 "traffic": measured_traffic(key),
                                  "algorithmic_bytes_per_launch": nbytes,
                                  "kernel": "parallax_decode_gqa_kernel<128,...>" if gqa
                                            else "parallax_decode_paged_kernel<128,...>"}})

@@ -522,8 +522,15 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_gqa_kernel(PagedDecod
 
     const int g = a.Hq / a.Hkv;
     const int ngrp = (g + GQ - 1) / GQ;
-    const int pair = blockIdx.x / ngrp;
-    const int grp = blockIdx.x - pair * ngrp;
+    // Block v serves query group (v / 8) % ngrp of (sequence, kv head) pair
+    // 8 ((v / 8) / ngrp) + v % 8: the ngrp workgroups of a pair share an XCD
+    // (block v runs on XCD v % 8) and read its cache rows through one L2.
+    // Blocks past the last pair (the grid is rounded up to 8 pairs) exit.
+    const int vb = (int)(blockIdx.x >> 3);
+    const int pair = (vb / ngrp) * 8 + (int)(blockIdx.x & 7);
+    const int grp = vb % ngrp;
+    if (pair >= a.B * a.Hkv)
+        return;
     const int b = pair / a.Hkv;
     const int hk = pair - b * a.Hkv;
     const int q0 = hk * g + grp * GQ;            // first query head of the workgroup
@@ -763,7 +770,8 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_gqa_kernel(PagedDecod
 template <int D, int NS, int GQ>
 hipError_t launch_decode_gqa_t(const PagedDecodeArgs &a, hipStream_t stream) {
     const int g = a.Hq / a.Hkv;
-    const dim3 grid((unsigned)(a.B * a.Hkv * ((g + GQ - 1) / GQ)));
+    const int64_t pairs8 = ((int64_t)a.B * a.Hkv + 7) / 8 * 8;
+    const dim3 grid((unsigned)(pairs8 * ((g + GQ - 1) / GQ)));
     PagedDecodeArgs args = a;
     void *params[] = {&args};
     const void *fn = a.block_table
@@ -773,9 +781,11 @@ hipError_t launch_decode_gqa_t(const PagedDecodeArgs &a, hipStream_t stream) {
 }
 
 // Columns per workgroup: 4, 8 or 16 (the group, rounded up, at most 16).
+// (Smaller groups for calls with few (sequence, kv head) pairs, e.g. MQA
+// over 64 sequences as 256 workgroups of 4 query heads instead of 64 of 16,
+// measured the same: each wavefront still walks the same chain of stages.)
 // Wavefronts: the requested splits, at most 8 (up to 256 registers per lane;
-// with 16 columns also the LDS of the merge); two such workgroups share a
-// CU.
+// with 16 columns also the LDS of the merge).
 template <int D>
 hipError_t launch_decode_gqa(const PagedDecodeArgs &a, int num_splits, hipStream_t stream) {
     const int g = a.Hq / a.Hkv;

@@ -125,10 +125,12 @@ def test_bad_block_table_entries_are_clamped(orc):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
-@pytest.mark.parametrize("Hkv", [16, 4])
+@pytest.mark.parametrize("Hkv", [16, 4, 1])
 def test_full_size_paged_gqa(orc, Hkv):
     """The decode workload's size (B=64, 16 query heads, 4096 tokens, d=128) in
-    64-token pages, with 16 or 4 kv heads; sampled (b, h) rows against the oracle."""
+    64-token pages, with 16, 4 or 1 kv heads (with 1, 64 kv heads serve 16
+    query heads each, in four workgroups of 4 per kv head); sampled (b, h)
+    rows against the oracle."""
     cfg = workloads.DECODE
     B, Hq, Lmax, d, page = cfg.B, cfg.H, cfg.Lmax, cfg.d, 64
     say("[case] full-size paged decode Hkv=%d" % Hkv)
