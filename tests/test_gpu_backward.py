@@ -90,11 +90,12 @@ def full_check(orc, q, k, v, r, do, window=0, n_sink=0, scale=None, what=""):
     return compare_grads(list(zip(("dq", "dk", "dv", "dr"), (f64(g) for g in grads))), ref, what)
 
 
-def test_fwd_train_outputs(orc):
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_train_outputs(orc, d):
     """o and lse equal the inference forward bit for bit; pv and sbar match the
     oracle: pv is the oracle with rho = 0, and sbar = rho . kbar with kbar the
     oracle with rho = 0 and v = k."""
-    q, k, v, r = (rand((2, 2, 300, 128), 10 + t) for t in range(4))
+    q, k, v, r = (rand((2, 2, 300, d), 10 + t + d) for t in range(4))
     for window, n_sink in ((0, 0), (64, 3)):
         qd, kd, vd, rd = (x.to(DEV) for x in (q, k, v, r))
         o, lse, sbar, pv = parallax_attn_fwd_train(qd, kd, vd, rd, window=window, n_sink=n_sink)
@@ -106,7 +107,8 @@ def test_fwd_train_outputs(orc):
         sbar_ref = np.sum(f64(r) * kbar, axis=-1)
         e_pv = float(np.max(np.abs(f64(pv) - pv_ref)))
         e_s = float(np.max(np.abs(f64(sbar) - sbar_ref)))
-        say("[parity] fwd_train W=%d S=%d: max|dpv|=%.3e max|dsbar|=%.3e" % (window, n_sink, e_pv, e_s))
+        say("[parity] fwd_train d=%d W=%d S=%d: max|dpv|=%.3e max|dsbar|=%.3e"
+            % (d, window, n_sink, e_pv, e_s))
         assert e_pv <= 2e-2 and e_s <= 2e-2 * max(1.0, float(np.max(np.abs(sbar_ref))))
 
 
