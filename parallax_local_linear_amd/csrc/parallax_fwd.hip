@@ -191,6 +191,48 @@ __device__ __forceinline__ void pin(const T &x) {
     asm volatile("" ::"v"(x));
 }
 
+// Stores a wavefront's 16 output rows non-temporally (no later work in the
+// call reads them), each store instruction writing whole 128-byte lines.
+// Lane (l16, G) holds features 16 dt + 4G .. +3 of row l16 in out[dt]; lanes
+// l and l ^ 8 trade one 16-byte piece per pair of feature tiles, so that the
+// first instruction of a pair writes rows 0-7 and the second rows 8-15, each
+// row's 32 features by 8 lanes.  (Written from the accumulator layout, each
+// instruction would write half of every row's lines, and non-temporal
+// stores of half lines are not merged in L2.)  The outputs are
+// o = (A keep + C) inv from the accumulators, formed a pair of tiles at a
+// time.  Rows at or past `L` are not stored; o0 is row i0 of the wavefront,
+// ld the row stride in elements.
+template <int DT>
+__device__ __forceinline__ void store_rows_nt(float *o0, int64_t ld, int i0, int L, int l16,
+                                              int G, const f32x4 (&accA)[DT],
+                                              const f32x4 (&accC)[DT], float keep, float inv) {
+    static_assert(DT % 2 == 0, "pairs of feature tiles");
+    const bool lo = l16 < 8;
+    const int ra = lo ? l16 : l16 - 8;  // row of the first instruction of a pair
+    const int rb = ra + 8;              // row of the second
+    const int seg = (lo ? 0 : 4) + G;   // 16-byte piece of the row's 128-byte line
+#pragma unroll
+    for (int p = 0; p < DT / 2; ++p) {
+        f32x4 out[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                out[q][u] = (accA[2 * p + q][u] * keep + accC[2 * p + q][u]) * inv;
+        const f32x4 send = lo ? out[1] : out[0];
+        f32x4 recv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            recv[i] = __shfl_xor(send[i], 8, 64);
+        const f32x4 va = lo ? out[0] : recv;
+        const f32x4 vb = lo ? recv : out[1];
+        if (i0 + ra < L)
+            __builtin_nontemporal_store(va, reinterpret_cast<f32x4 *>(o0 + ra * ld + 32 * p + 4 * seg));
+        if (i0 + rb < L)
+            __builtin_nontemporal_store(vb, reinterpret_cast<f32x4 *>(o0 + rb * ld + 32 * p + 4 * seg));
+    }
+}
+
 // Workgroup barrier between ping-pong phases.  With WAIT_LDS, this wave's
 // LDS reads complete first (needed where another wave's next copy reuses
 // the buffer just read).  The scheduler may not move anything across it.
@@ -936,14 +978,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
         offsets_set = true;
     }
 
-    // Epilogue.  The outputs are stored non-temporally: no later work in the
-    // call reads them, and the 0.6B-like call measured 3% faster with it
-    // (the windowed kernel measured slower with it and keeps plain stores).
+    // Epilogue.  O is stored non-temporally, in whole lines (store_rows_nt;
+    // rows past L compute values nobody stores); the precise instantiation,
+    // one register short for the line exchange, stores each lane's pieces.
     const float ell_t = cx.accL[0];
     const float s_t = cx.accS[0];
-    if (row < L) {
-        const float inv = 1.f / ell_t;
-        const float keep = 1.f - s_t * inv;
+    const float inv = 1.f / ell_t;
+    const float keep = 1.f - s_t * inv;
+    if constexpr (!PRECISE) {
+        const int iw = i0 + ROWS * wave;  // the wavefront's first row
+        store_rows_nt<C::DT>(a.o + (int64_t)b * a.o_b + (int64_t)h * a.o_h + (int64_t)iw * a.o_l,
+                             a.o_l, iw, L, l16, G, cx.accA, cx.accC, keep, inv);
+    } else if (row < L) {
         float *ob = a.o + (int64_t)b * a.o_b + (int64_t)h * a.o_h + (int64_t)row * a.o_l;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
@@ -953,6 +999,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void parallax_fwd_kernel(FwdArgs a) {
                 out[u] = (cx.accA[dt][u] * keep + cx.accC[dt][u]) * inv;
             __builtin_nontemporal_store(out, reinterpret_cast<f32x4 *>(ob + 16 * dt + 4 * G));
         }
+    }
+    if (row < L) {
         if (G == 0)
             __builtin_nontemporal_store((cx.m_ref + log2f(ell_t)) * kLn2, a.lse + (int64_t)bh * L + row);
         // Saved for the backward: sbar = S / ell and pv = A / ell.
