@@ -393,9 +393,13 @@ def time_decode_paged(dcfg, steps, warmup, stream):
     pool, 16 query heads over 16, 4 or 1 kv heads.  GB/s counts the cache once."""
     import torch
 
-    from parallax_local_linear_amd import parallax_attn_decode_paged
+    from parallax_local_linear_amd import (parallax_attn_decode_paged,
+                                           parallax_attn_decode_paged_workspace_size)
     dev = torch.device("cuda:0")
     B, Hq, Lmax, d, page = dcfg.B, dcfg.H, dcfg.Lmax, dcfg.d, 64
+    # Key-split workspace of the grouped-head calls, allocated once.
+    ws = torch.empty(parallax_attn_decode_paged_workspace_size(B, Hq, d), dtype=torch.uint8,
+                     device=dev)
     out = []
     for Hkv in (16, 4, 1):
         g = torch.Generator(device=dev).manual_seed(2024 + Hkv)
@@ -411,7 +415,7 @@ def time_decode_paged(dcfg, steps, warmup, stream):
 
         def call():
             parallax_attn_decode_paged(q, r, kp, vp, table, None, num_splits=dcfg.num_splits,
-                                       out=o, lse=lse, stream=stream)
+                                       out=o, lse=lse, workspace=ws, stream=stream)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()

@@ -379,6 +379,33 @@ parallax_status parallax_attn_decode_paged(const void *q, const void *r,
                                            int num_splits, void *stream);
 
 /*
+ * parallax_attn_decode_paged with a caller workspace: the same operation,
+ * arguments, validation and results.  With four or more query heads per kv
+ * head, a call that has fewer (sequence, kv head) workgroups than the GPU
+ * has compute units (MQA over a small batch) splits each kv head's visible
+ * keys over up to 8 workgroups whose partial states (m, ell, S, A, C per
+ * query head, the same quantities the single-workgroup merge combines)
+ * meet in the workspace and are merged by a second launch; otherwise the
+ * workspace is not touched.  The workspace is device memory of at least
+ * parallax_attn_decode_paged_workspace_size(B, Hq, d) bytes, 16-byte
+ * aligned, owned by the caller; its contents need no initialisation and are
+ * scratch once the call's work on `stream` has finished.  A missing,
+ * misaligned or short workspace returns PARALLAX_ERR_INVALID_ARG before
+ * anything is launched.
+ */
+size_t parallax_attn_decode_paged_workspace_size(int B, int Hq, int d);
+parallax_status parallax_attn_decode_paged_ws(const void *q, const void *r,
+                                              const void *k_cache, const void *v_cache,
+                                              const int32_t *block_table, int num_pages,
+                                              int page_size, int max_pages,
+                                              const int32_t *seqlens, float *o, float *lse,
+                                              int B, int Hq, int Hkv, int d,
+                                              parallax_strides sk, parallax_strides sv,
+                                              float softmax_scale, int window, int n_sink,
+                                              int num_splits, void *workspace,
+                                              size_t workspace_bytes, void *stream);
+
+/*
  * Fused input projections: Y = X W^T with W the row-wise stack of W_Q, W_K,
  * W_V and the probe projection W_R (review page "Parallax: Parameterized
  * Local Linear Attention for Language Modeling", sec. 1 and sec. 3: the

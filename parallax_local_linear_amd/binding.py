@@ -31,7 +31,8 @@ EXPORTED = ("parallax_attn_fwd_workspace_size", "parallax_attn_fwd", "parallax_a
             "parallax_attn_fwd_noalloc", "parallax_attn_fwd_f32",
             "parallax_attn_fwd_train",
             "parallax_attn_bwd_workspace_size", "parallax_attn_bwd", "parallax_attn_decode",
-            "parallax_attn_decode_paged", "parallax_qkvr_project", "parallax_hadamard_out",
+            "parallax_attn_decode_paged", "parallax_attn_decode_paged_workspace_size",
+            "parallax_attn_decode_paged_ws", "parallax_qkvr_project", "parallax_hadamard_out",
             "parallax_based_state_floats", "parallax_based_workspace_size", "parallax_based_fwd",
             "parallax_based_decode", "parallax_status_string")
 
@@ -90,6 +91,12 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.parallax_attn_decode_paged.restype = ctypes.c_int
     lib.parallax_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, vp,
                                                i, i, i, i, S, S, f, i, i, i, vp]
+    lib.parallax_attn_decode_paged_workspace_size.restype = ctypes.c_size_t
+    lib.parallax_attn_decode_paged_workspace_size.argtypes = [i, i, i]
+    lib.parallax_attn_decode_paged_ws.restype = ctypes.c_int
+    lib.parallax_attn_decode_paged_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, vp,
+                                                  i, i, i, i, S, S, f, i, i, i, vp,
+                                                  ctypes.c_size_t, vp]
     lib.parallax_qkvr_project.restype = ctypes.c_int
     lib.parallax_qkvr_project.argtypes = [vp, vp, vp, i, i, i, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int64, vp]
@@ -392,16 +399,26 @@ def parallax_attn_decode(q, r, k_cache, v_cache, seqlens=None, *, softmax_scale=
     return out, lse
 
 
+def parallax_attn_decode_paged_workspace_size(B: int, Hq: int, d: int) -> int:
+    """Bytes of device workspace parallax_attn_decode_paged_ws needs."""
+    return int(load_library().parallax_attn_decode_paged_workspace_size(B, Hq, d))
+
+
 @_stream_ordered
 def parallax_attn_decode_paged(q, r, k_cache, v_cache, block_table=None, seqlens=None, *,
                                softmax_scale=None, window=0, n_sink=0, num_splits=16,
-                               out=None, lse=None, stream=None):
+                               out=None, lse=None, workspace=None, stream=None):
     """General decode step.  q, r: bf16 [B,Hq,d].
 
     Paged (block_table: int32 [B, max_pages]): k_cache, v_cache are page pools
     [num_pages, page_size, Hkv, d] (any strides, d contiguous).  Contiguous
     (block_table None): caches [B, Lmax, Hkv, d]; pass cache.permute(0, 2, 1, 3)
     for a [B, Hkv, Lmax, d] tensor.  seqlens: int32 [B] or None.
+    ``workspace``: with four or more query heads per kv head the call goes
+    through parallax_attn_decode_paged_ws, which may split each kv head's
+    keys over several workgroups; None allocates its workspace here, a
+    uint8 device tensor of at least parallax_attn_decode_paged_workspace_size
+    bytes is used as given, and False calls parallax_attn_decode_paged.
     Returns (o fp32 [B,Hq,d], lse fp32 [B,Hq]).
     """
     _need(q, "q", torch.bfloat16, 3)
@@ -443,12 +460,22 @@ def parallax_attn_decode_paged(q, r, k_cache, v_cache, block_table=None, seqlens
         raise ValueError("out / lse have the wrong shape")
     ks = parallax_strides(k_cache.stride(0), k_cache.stride(2), k_cache.stride(1))
     vs = parallax_strides(v_cache.stride(0), v_cache.stride(2), v_cache.stride(1))
-    st = load_library().parallax_attn_decode_paged(
-        q.data_ptr(), r.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_table.data_ptr() if block_table is not None else None, P, page_size, max_pages,
-        seqlens.data_ptr() if seqlens is not None else None, out.data_ptr(), lse.data_ptr(),
-        B, Hq, Hkv, d, ks, vs, float(softmax_scale), int(window), int(n_sink),
-        int(num_splits), _stream_handle(q.device, stream))
+    args = (q.data_ptr(), r.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_table.data_ptr() if block_table is not None else None, P, page_size, max_pages,
+            seqlens.data_ptr() if seqlens is not None else None, out.data_ptr(), lse.data_ptr(),
+            B, Hq, Hkv, d, ks, vs, float(softmax_scale), int(window), int(n_sink),
+            int(num_splits))
+    lib = load_library()
+    grouped = Hkv > 0 and Hq % Hkv == 0 and Hq // Hkv >= 4
+    if workspace is False or not grouped:
+        st = lib.parallax_attn_decode_paged(*args, _stream_handle(q.device, stream))
+    else:
+        if workspace is None:
+            workspace = torch.empty(max(1, parallax_attn_decode_paged_workspace_size(B, Hq, d)),
+                                    dtype=torch.uint8, device=q.device)
+        _need(workspace, "workspace", torch.uint8, 1)
+        st = lib.parallax_attn_decode_paged_ws(*args, workspace.data_ptr(), workspace.numel(),
+                                               _stream_handle(q.device, stream))
     _check(st)
     return out, lse
 

@@ -129,7 +129,19 @@ struct PagedDecodeArgs {
     int max_len;                    // longest sequence the cache holds
     float scale_log2;
     int window, n_sink;
+    // Grouped-head kernel only: the visible keys of each (sequence, kv head)
+    // are split over `ksplit` workgroups (1: no split), whose partial states
+    // go to `part` ([B*Hq][ksplit][2d+3] floats) for a merge launch.
+    int ksplit;
+    float *part;
 };
+
+// Most key splits of the grouped-head decode, and the workspace its partial
+// states need: [B*Hq][splits][m, ell, S, A[d], C[d]] floats.
+constexpr int kDecodeMaxKeySplits = 8;
+inline size_t decode_paged_workspace_bytes(int64_t B, int64_t Hq, int d) {
+    return (size_t)(B * Hq * kDecodeMaxKeySplits * (2 * d + 3)) * sizeof(float);
+}
 
 struct BwdArgs {
     const uint16_t *q, *k, *v, *r, *dout;  // bf16 bits, [B,H,L,d] with the strides below

@@ -351,13 +351,16 @@ parallax_status parallax_attn_decode(const void *q, const void *r, const void *k
     return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
 }
 
-parallax_status parallax_attn_decode_paged(const void *q, const void *r, const void *k_cache,
-                                           const void *v_cache, const int32_t *block_table,
-                                           int num_pages, int page_size, int max_pages,
-                                           const int32_t *seqlens, float *o, float *lse, int B,
-                                           int Hq, int Hkv, int d, parallax_strides sk,
-                                           parallax_strides sv, float softmax_scale, int window,
-                                           int n_sink, int num_splits, void *stream) {
+namespace {
+
+// The general decode; `part` is the key-split workspace of
+// parallax_attn_decode_paged_ws (nullptr: no key splits).
+parallax_status decode_paged(const void *q, const void *r, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table, int num_pages,
+                             int page_size, int max_pages, const int32_t *seqlens, float *o,
+                             float *lse, int B, int Hq, int Hkv, int d, parallax_strides sk,
+                             parallax_strides sv, float softmax_scale, int window, int n_sink,
+                             int num_splits, float *part, void *stream) {
     if (B < 0 || Hq < 0 || Hkv < 0)
         return PARALLAX_ERR_INVALID_ARG;
     if (d != 64 && d != 128)
@@ -410,9 +413,49 @@ parallax_status parallax_attn_decode_paged(const void *q, const void *r, const v
     a.scale_log2 = softmax_scale * kLog2e;
     a.window = window;
     a.n_sink = n_sink;
+    a.ksplit = 1;
+    a.part = part;
     hipError_t e =
         plx::launch_decode_paged(a, d, num_splits, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_LAUNCH;
+}
+
+}  // namespace
+
+parallax_status parallax_attn_decode_paged(const void *q, const void *r, const void *k_cache,
+                                           const void *v_cache, const int32_t *block_table,
+                                           int num_pages, int page_size, int max_pages,
+                                           const int32_t *seqlens, float *o, float *lse, int B,
+                                           int Hq, int Hkv, int d, parallax_strides sk,
+                                           parallax_strides sv, float softmax_scale, int window,
+                                           int n_sink, int num_splits, void *stream) {
+    return decode_paged(q, r, k_cache, v_cache, block_table, num_pages, page_size, max_pages,
+                        seqlens, o, lse, B, Hq, Hkv, d, sk, sv, softmax_scale, window, n_sink,
+                        num_splits, nullptr, stream);
+}
+
+size_t parallax_attn_decode_paged_workspace_size(int B, int Hq, int d) {
+    if (B <= 0 || Hq <= 0 || (d != 64 && d != 128))
+        return 0;
+    return plx::decode_paged_workspace_bytes(B, Hq, d);
+}
+
+parallax_status parallax_attn_decode_paged_ws(const void *q, const void *r, const void *k_cache,
+                                              const void *v_cache, const int32_t *block_table,
+                                              int num_pages, int page_size, int max_pages,
+                                              const int32_t *seqlens, float *o, float *lse,
+                                              int B, int Hq, int Hkv, int d, parallax_strides sk,
+                                              parallax_strides sv, float softmax_scale,
+                                              int window, int n_sink, int num_splits,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *stream) {
+    if (B > 0 && Hq > 0 && (d == 64 || d == 128) &&
+        (!workspace || !aligned(workspace, 16) ||
+         workspace_bytes < plx::decode_paged_workspace_bytes(B, Hq, d)))
+        return PARALLAX_ERR_INVALID_ARG;
+    return decode_paged(q, r, k_cache, v_cache, block_table, num_pages, page_size, max_pages,
+                        seqlens, o, lse, B, Hq, Hkv, d, sk, sv, softmax_scale, window, n_sink,
+                        num_splits, static_cast<float *>(workspace), stream);
 }
 
 parallax_status parallax_qkvr_project(const void *x, const void *w, void *y, int M, int N,

@@ -29,6 +29,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace plx {
@@ -526,8 +527,13 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_gqa_kernel(PagedDecod
     // 8 ((v / 8) / ngrp) + v % 8: the ngrp workgroups of a pair share an XCD
     // (block v runs on XCD v % 8) and read its cache rows through one L2.
     // Blocks past the last pair (the grid is rounded up to 8 pairs) exit.
-    const int vb = (int)(blockIdx.x >> 3);
-    const int pair = (vb / ngrp) * 8 + (int)(blockIdx.x & 7);
+    // With key splits, block ks * nbase + v takes split ks of block v's keys
+    // (nbase is a multiple of 8, so the mapping above is unchanged).
+    const int nbase = ((a.B * a.Hkv + 7) / 8) * 8 * ngrp;
+    const int ks = (int)blockIdx.x / nbase;
+    const int vblk = (int)blockIdx.x - ks * nbase;
+    const int vb = vblk >> 3;
+    const int pair = (vb / ngrp) * 8 + (vblk & 7);
     const int grp = vb % ngrp;
     if (pair >= a.B * a.Hkv)
         return;
@@ -545,9 +551,13 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_gqa_kernel(PagedDecod
         ns = min(a.n_sink, lo);
     }
     const int total = ns + (n - lo);
-    const int chunk = (total + NS - 1) / NS;
-    const int ts = min(wave * chunk, total);
-    const int te = min(ts + chunk, total);
+    // This workgroup's split of the visible keys, then each wavefront's chunk.
+    const int kchunk = (total + a.ksplit - 1) / a.ksplit;
+    const int sub_lo = min(ks * kchunk, total);
+    const int sub_hi = min(sub_lo + kchunk, total);
+    const int chunk = (sub_hi - sub_lo + NS - 1) / NS;
+    const int ts = min(sub_lo + wave * chunk, sub_hi);
+    const int te = min(ts + chunk, sub_hi);
 
     // Q^T and R^T B fragments: column l16 = query head q0 + l16, features
     // 32 kc + 8G .. +7 (zeros past the group's heads).
@@ -758,26 +768,79 @@ __global__ __launch_bounds__(64 * NS) void parallax_decode_gqa_kernel(PagedDecod
             at += fw * r0[3 + f];
             ct += fw * r0[3 + D + f];
         }
+        const int64_t row = (int64_t)b * a.Hq + q0 + col;
+        if (a.ksplit > 1) {
+            // This split's partial state; the merge launch finishes the row.
+            float *pr = a.part + (row * a.ksplit + ks) * (2 * D + 3);
+            pr[3 + f] = at;
+            pr[3 + D + f] = ct;
+            if (f == 0) {
+                pr[0] = M;
+                pr[1] = lt;
+                pr[2] = st;
+            }
+            continue;
+        }
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const float keep = 1.f - st * inv;
-        const int64_t row = (int64_t)b * a.Hq + q0 + col;
         a.o[row * D + f] = (at * keep + ct) * inv;
         if (f == 0)
             a.lse[row] = lt > 0.f ? (M + log2f(lt)) * kLn2 : kNegInf;
     }
 }
 
+// Merge of the key splits' partial states of each (sequence, query head):
+// the same rescaled sums as the merge across wavefronts, then the epilogue.
+// One workgroup of D threads per row, thread f owning feature f.
+template <int D>
+__global__ __launch_bounds__(D) void parallax_decode_split_merge_kernel(PagedDecodeArgs a) {
+    const int64_t row = blockIdx.x;
+    const int f = threadIdx.x;
+    const int S = a.ksplit;
+    const float *pr = a.part + row * S * (2 * D + 3);
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s)
+        M = fmaxf(M, pr[s * (2 * D + 3)]);
+    float lt = 0.f, st = 0.f, at = 0.f, ct = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const float *r0 = pr + s * (2 * D + 3);
+        const float fw = (M == kNegInf) ? 0.f : exp2_fast(r0[0] - M);
+        lt += fw * r0[1];
+        st += fw * r0[2];
+        at += fw * r0[3 + f];
+        ct += fw * r0[3 + D + f];
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float keep = 1.f - st * inv;
+    a.o[row * D + f] = (at * keep + ct) * inv;
+    if (f == 0)
+        a.lse[row] = lt > 0.f ? (M + log2f(lt)) * kLn2 : kNegInf;
+}
+
+// With a workspace, calls with fewer workgroups than the chip has CUs split
+// each kv head's keys over up to kDecodeMaxKeySplits workgroups (MQA over 64
+// sequences: 4 splits, 256 workgroups); each workgroup's wavefronts walk a
+// shorter chain of stages, and a merge launch combines the splits.
+constexpr int kDecodeCUs = 256;  // compute units of the MI355X
 template <int D, int NS, int GQ>
 hipError_t launch_decode_gqa_t(const PagedDecodeArgs &a, hipStream_t stream) {
     const int g = a.Hq / a.Hkv;
     const int64_t pairs8 = ((int64_t)a.B * a.Hkv + 7) / 8 * 8;
-    const dim3 grid((unsigned)(pairs8 * ((g + GQ - 1) / GQ)));
+    const int64_t nbase = pairs8 * ((g + GQ - 1) / GQ);
     PagedDecodeArgs args = a;
+    args.ksplit = 1;
+    if (a.part && nbase < kDecodeCUs)
+        args.ksplit = (int)std::min<int64_t>(kDecodeMaxKeySplits, (kDecodeCUs + nbase - 1) / nbase);
     void *params[] = {&args};
     const void *fn = a.block_table
                          ? reinterpret_cast<const void *>(&parallax_decode_gqa_kernel<D, NS, GQ, true>)
                          : reinterpret_cast<const void *>(&parallax_decode_gqa_kernel<D, NS, GQ, false>);
-    return hipLaunchKernel(fn, grid, dim3(64 * NS), params, 0, stream);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(nbase * args.ksplit)), dim3(64 * NS), params,
+                                   0, stream);
+    if (e != hipSuccess || args.ksplit == 1)
+        return e;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&parallax_decode_split_merge_kernel<D>),
+                           dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(D), params, 0, stream);
 }
 
 // Columns per workgroup: 4, 8 or 16 (the group, rounded up, at most 16).

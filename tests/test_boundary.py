@@ -261,6 +261,46 @@ def test_decode_paged_empty_is_a_no_op(lib):
     assert decp(lib, Hq=0, bt=None, page=300) == OK
 
 
+def decp_ws(lib, ws=A16, ws_bytes=None, B=2, Hq=4, d=128, **kw):
+    """parallax_attn_decode_paged_ws with decp's defaults and a workspace."""
+    if ws_bytes is None:
+        ws_bytes = lib.parallax_attn_decode_paged_workspace_size(B, Hq, d)
+    args = dict(q=A16, r=A16, k=A16, v=A16, bt=A16, num_pages=64, page=16, max_pages=8,
+                seqlens=None, o=A16, lse=A16, Hkv=2, sk=CONTIG, sv=CONTIG, scale=0.1, window=0,
+                n_sink=0, splits=16)
+    args.update(kw)
+    a = args
+    return lib.parallax_attn_decode_paged_ws(a["q"], a["r"], a["k"], a["v"], a["bt"],
+                                             a["num_pages"], a["page"], a["max_pages"],
+                                             a["seqlens"], a["o"], a["lse"], B, Hq, a["Hkv"], d,
+                                             a["sk"], a["sv"], a["scale"], a["window"],
+                                             a["n_sink"], a["splits"], ws, ws_bytes, None)
+
+
+def test_decode_paged_workspace_size(lib):
+    """[B*Hq][8 splits][m, ell, S, A[d], C[d]] fp32; 0 for an empty or unsupported problem."""
+    assert lib.parallax_attn_decode_paged_workspace_size(64, 16, 128) == 64 * 16 * 8 * 259 * 4
+    assert lib.parallax_attn_decode_paged_workspace_size(3, 5, 64) == 3 * 5 * 8 * 131 * 4
+    assert lib.parallax_attn_decode_paged_workspace_size(0, 16, 128) == 0
+    assert lib.parallax_attn_decode_paged_workspace_size(4, 0, 128) == 0
+    assert lib.parallax_attn_decode_paged_workspace_size(4, 16, 96) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), INVALID), (dict(ws=A16 + 8), INVALID),
+    (dict(ws_bytes=2 * 4 * 8 * 259 * 4 - 1), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(splits=3), UNSUPPORTED), (dict(Hkv=3), INVALID),
+    (dict(q=None), INVALID), (dict(page=24), INVALID), (dict(scale=0.0), INVALID),
+])
+def test_decode_paged_ws_rejects(lib, kw, status):
+    assert decp_ws(lib, **kw) == status
+
+
+def test_decode_paged_ws_empty_is_a_no_op(lib):
+    assert decp_ws(lib, B=0, ws=None, ws_bytes=0, q=None, r=None, k=None, v=None, o=None,
+                   lse=None) == OK
+
+
 def proj(lib, x=A16, w=A16, y=A16, M=64, N=64, K=64, ldx=64, ldw=64, ldy=64):
     return lib.parallax_qkvr_project(x, w, y, M, N, K, ldx, ldw, ldy, None)
 

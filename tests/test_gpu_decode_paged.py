@@ -13,7 +13,7 @@ import torch
 
 from gpu_util import compare, f64, say
 from parallax_local_linear_amd import (parallax_attn_decode, parallax_attn_decode_paged,
-                                       workloads)
+                                       parallax_attn_decode_paged_workspace_size, workloads)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,8 @@ def to_pages(cache, page_size, seed, spare=3):
     return pool, table
 
 
-def run_case(orc, B, Hq, Hkv, Lmax, d, seqlens, window, n_sink, page_size, splits, seed):
+def run_case(orc, B, Hq, Hkv, Lmax, d, seqlens, window, n_sink, page_size, splits, seed,
+             workspace=None):
     say("[case] paged decode B=%d Hq=%d Hkv=%d Lmax=%d d=%d page=%s W=%d S=%d splits=%d"
         % (B, Hq, Hkv, Lmax, d, page_size, window, n_sink, splits))
     q, r = (rand((B, Hq, d), seed + t) for t in range(2))
@@ -60,7 +61,7 @@ def run_case(orc, B, Hq, Hkv, Lmax, d, seqlens, window, n_sink, page_size, split
         vp, _ = to_pages(v, page_size, seed)
         kc, vc, table = kp.to(DEV), vp.to(DEV), table.to(DEV)
     o, lse = parallax_attn_decode_paged(q.to(DEV), r.to(DEV), kc, vc, table, sl, window=window,
-                                        n_sink=n_sink, num_splits=splits)
+                                        n_sink=n_sink, num_splits=splits, workspace=workspace)
     torch.cuda.synchronize()
     o_ref, lse_ref = orc.decode_ext(f64(q), f64(r), f64(k), f64(v), seqlens=seqlens,
                                     window=window, n_sink=n_sink)
@@ -94,6 +95,29 @@ CASES = [
 def test_paged_decode(orc, B, Hq, Hkv, Lmax, d, seqlens, window, n_sink, page_size, splits):
     seed = B * 7919 + Hq * 104729 + Lmax + d + window * 13 + n_sink + (page_size or 0)
     run_case(orc, B, Hq, Hkv, Lmax, d, seqlens, window, n_sink, page_size, splits, seed)
+
+
+GROUPED = [c for c in CASES if c[1] // c[2] >= 4]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lmax,d,seqlens,window,n_sink,page_size,splits", GROUPED)
+def test_grouped_without_key_splits(orc, B, Hq, Hkv, Lmax, d, seqlens, window, n_sink,
+                                    page_size, splits):
+    """The grouped cases through parallax_attn_decode_paged (no workspace, so
+    one workgroup per kv head and column group); the cases above take the
+    workspace entry, which splits these small calls' keys over 8 workgroups."""
+    seed = B * 7919 + Hq * 104729 + Lmax + d + window * 13 + n_sink + (page_size or 0) + 1
+    run_case(orc, B, Hq, Hkv, Lmax, d, seqlens, window, n_sink, page_size, splits, seed,
+             workspace=False)
+
+
+def test_workspace_reused_by_a_smaller_call(orc):
+    """One caller workspace, two calls in a row (the second smaller, over
+    stale partial states of the first): both match the oracle."""
+    ws = torch.empty(parallax_attn_decode_paged_workspace_size(3, 16, 128), dtype=torch.uint8,
+                     device=DEV)
+    run_case(orc, 3, 16, 1, 900, 128, [900, 450, 2], 0, 0, 64, 16, 4242, workspace=ws)
+    run_case(orc, 2, 8, 2, 333, 128, [1, 333], 0, 0, None, 16, 4343, workspace=ws)
 
 
 def test_plain_case_matches_contiguous_decode(orc):
