@@ -200,3 +200,48 @@ def test_paged_rejects_bad_outputs(bad):
         out = torch.empty((B, Hq, 2 * d), dtype=torch.float32, device=DEV)[..., :d]
     with pytest.raises((TypeError, ValueError)):
         parallax_attn_decode_paged(q, r, k, v, out=out, lse=lse)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (16, 1)])
+def test_workspace_entry_through_the_c_abi(Hq, Hkv):
+    """parallax_attn_decode_paged_ws called directly: with fewer than four
+    query heads per kv head it leaves the workspace alone and gives the plain
+    entry's bits; with sixteen it splits the keys, within the decode's
+    tolerance of the plain entry."""
+    from parallax_local_linear_amd import binding
+    lib = binding.load_library()
+    B, L, d, page = 3, 640, 128, 64
+    say("[case] C-ABI workspace decode Hq=%d Hkv=%d" % (Hq, Hkv))
+    q, r = (rand((B, Hq, d), 900 + t).to(DEV) for t in range(2))
+    n_pages = B * L // page
+    kp, vp = (rand((n_pages, page, Hkv, d), 910 + t).to(DEV) for t in range(2))
+    table = torch.arange(n_pages, dtype=torch.int32).flip(0).view(B, L // page).contiguous().to(DEV)
+    sl = torch.tensor([640, 333, 1], dtype=torch.int32, device=DEV)
+    ks = binding.parallax_strides(kp.stride(0), kp.stride(2), kp.stride(1))
+    vs = binding.parallax_strides(vp.stride(0), vp.stride(2), vp.stride(1))
+    nbytes = lib.parallax_attn_decode_paged_workspace_size(B, Hq, d)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device=DEV)  # NaN-like fill
+    outs = []
+    for use_ws in (False, True):
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+        args = (q.data_ptr(), r.data_ptr(), kp.data_ptr(), vp.data_ptr(), table.data_ptr(),
+                n_pages, page, L // page, sl.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq,
+                Hkv, d, ks, vs, 1.0 / d ** 0.5, 0, 0, 16)
+        if use_ws:
+            st = lib.parallax_attn_decode_paged_ws(*args, ws.data_ptr(), nbytes, None)
+        else:
+            st = lib.parallax_attn_decode_paged(*args, None)
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    (o1, l1), (o2, l2) = outs
+    assert torch.isfinite(o2).all() and torch.isfinite(l2).all()
+    if Hq // Hkv < 4:
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert bool((ws == 0x7f).all()), "the workspace was touched"
+    else:
+        err = float((o1 - o2).abs().max())
+        say("[parity] key splits vs one workgroup: max|dO|=%.3e" % err)
+        assert err <= 2e-2
+        assert float((l1 - l2).abs().max()) <= 1e-3
