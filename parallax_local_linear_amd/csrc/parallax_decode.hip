@@ -492,7 +492,11 @@ __global__ __launch_bounds__(64 * NS * GW) void parallax_decode_paged_kernel(Pag
 //     the sums of p~ and p~ s from an all-ones operand (f16 MFMAs, fp32
 //     sums), as in the prefill's precise mode;
 //   * the NS partial states of each head merge in LDS (the stage memory,
-//     reused after one barrier).
+//     reused after one barrier);
+//   * with a caller workspace and fewer workgroups than CUs, several
+//     workgroups take consecutive slices of the visible keys, write their
+//     merged (m, ell, S, A, C) per query head to the workspace, and
+//     parallax_decode_split_merge_kernel combines them the same way.
 // Each wavefront's stage count differs, so the loop synchronises within the
 // wavefront only.
 // 16-byte slot of chunk q (reduction positions 8q .. 8q+7) of V^T row r in a
