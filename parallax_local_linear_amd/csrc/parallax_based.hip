@@ -575,8 +575,15 @@ __global__ __launch_bounds__(64 * OW) void parallax_based_out_kernel(BasedArgs a
 template <int DV>
 __global__ __launch_bounds__(4 * BCfg<DV>::NC) void parallax_based_decode_kernel(BasedArgs a) {
     using C = BCfg<DV>;
+    // Thread (fg, cq) owns state columns 4 cq .. 4 cq + 3 of features
+    // fg, fg + FGN, ...: 16-byte accesses, all of a thread's loads issued
+    // before its stores.
+    constexpr int NQ = C::NC / 4;             // column quads
+    constexpr int FGN = 4 * C::NC / NQ;       // feature groups (16)
+    constexpr int NI = NF / FGN;              // features per thread
+    static_assert(C::NC % 4 == 0 && FGN * NQ == 4 * C::NC && NI * FGN == NF, "decode split");
     __shared__ float phq[NF], phk[NF], qv[BK + 1], kv[BK + 1], vv[DV];
-    __shared__ float part[4][C::NC];
+    __shared__ float part[FGN][C::NC];
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
     const uint16_t *qr = a.q + (int64_t)bh * BK;
@@ -599,20 +606,42 @@ __global__ __launch_bounds__(4 * BCfg<DV>::NC) void parallax_based_decode_kernel
         phk[tid] = fa.coef * kv[fa.a] * kv[fa.b];
     }
     __syncthreads();
-    const int fg = tid / C::NC, c = tid - fg * C::NC;
-    const float vc = c < DV ? vv[c] : 1.f;
-    float *st = a.state + (int64_t)bh * (NF * C::NC) + c;
-    float sum = 0.f;
-    for (int f = fg; f < NF; f += 4) {
-        const float sv = st[f * C::NC] + phk[f] * vc;
-        st[f * C::NC] = sv;
-        sum += phq[f] * sv;
+    const int fg = tid / NQ, cq = tid - fg * NQ;
+    float vc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        vc[j] = 4 * cq + j < DV ? vv[4 * cq + j] : 1.f;
+    float4 *st = reinterpret_cast<float4 *>(a.state + (int64_t)bh * (NF * C::NC)) + cq;
+    float4 sv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        sv[i] = st[(fg + FGN * i) * NQ];
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int f = fg + FGN * i;
+        const float pk = phk[f], pq = phq[f];
+        sv[i].x += pk * vc[0];
+        sv[i].y += pk * vc[1];
+        sv[i].z += pk * vc[2];
+        sv[i].w += pk * vc[3];
+        st[f * NQ] = sv[i];
+        sum[0] += pq * sv[i].x;
+        sum[1] += pq * sv[i].y;
+        sum[2] += pq * sv[i].z;
+        sum[3] += pq * sv[i].w;
     }
-    part[fg][c] = sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        part[fg][4 * cq + j] = sum[j];
     __syncthreads();
     if (tid < DV) {
-        const float num = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
-        const float den = part[0][DV] + part[1][DV] + part[2][DV] + part[3][DV];
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int g = 0; g < FGN; ++g) {
+            num += part[g][tid];
+            den += part[g][DV];
+        }
         a.o[(int64_t)bh * DV + tid] = num / den;
     }
 }
